@@ -1,0 +1,319 @@
+"""Plain fp64 CPU oracle for the MoBA prefill forward.
+
+TEST INFRASTRUCTURE ONLY.  This file is the checker that the HIP kernels are
+compared against.  Only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may import it; the product path never does, and it shares
+no code, table or helper with the HIP sources.
+
+Sources (cited by page title and section):
+  report  -- the deep-dive report page on "MoBA: Mixture of Block Attention
+             for Long-Context LLMs" (arXiv 2502.13189).
+  course  -- the course page "Paper: MoBA (Moonshot)" (module F26).
+  blog    -- the blog page on getting the MoonshotAI/MoBA code to run.
+
+What MoBA computes, per query row (b, t, h), written out step by step in the
+order the report gives it:
+  1. report §2.1: cut the length-S context into n = S/B blocks of B keys;
+     block i (0-indexed here) holds positions [iB, (i+1)B).  A block is the
+     unit of choice: a chosen block is attended in full, an unchosen one not
+     at all.  S not divisible by B is an error (blog §1.1: the original code
+     asserts), so no padding is defined.
+  2. report §2.2 and the course summary: summarise each block by the mean of
+     its keys, mu_i = mean(K[block i]); the gate score is s_i = <q, mu_i>.
+     No router parameters and no scaling are involved.
+  3. report §2.3: causality.  Blocks that lie in the query's future get score
+     -inf (never routed to); the query's own block j = floor(t/B) is always
+     chosen; inside the own block a causal mask applies.
+  4. report §2.2: hard top-k gating (g_i in {0, 1}) over the admissible
+     blocks; the output is softmax attention over the union of the chosen
+     blocks' positions.
+Readings where the pages leave a step open (each listed in the design notes):
+  * top-k counts the forced own block: own block + (k-1) best past blocks.
+    Pinned by the report's sparsity figures (3 of 16 blocks -> 81.25 %,
+    3 of 64 and 12 of 256 -> 95.31 %; report summary and §3.3).
+  * when fewer than k-1 past blocks exist, all of them are chosen; topk >= n
+    is allowed and gives dense causal attention (course summary: with every
+    block chosen MoBA is exactly dense attention).
+  * ties in the gate go to the lower block index.
+  * the attention logits carry the usual 1/sqrt(D) factor (the report prints
+    the softmax without it; MoBA has to reduce to standard attention).
+  * grouped-query attention: query head h reads KV head floor(h / (Hq/Hkv)),
+    and routes with its own q (course exercise: per-head routing).
+  * non-causal mode (causal = False): no future mask, no forced block, plain
+    top-k over all n blocks, no mask inside blocks.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# Step 1 and 2: blocks and their mean keys (report §2.1, §2.2)
+# ----------------------------------------------------------------------------
+def num_blocks(seqlen: int, block_size: int) -> int:
+    """n = S / B (report §2.1).  Non-divisible lengths are rejected, as the
+    original code does (blog §1.1)."""
+    if block_size <= 0 or seqlen % block_size != 0:
+        raise ValueError(f"seqlen {seqlen} is not a multiple of block_size {block_size}")
+    return seqlen // block_size
+
+
+def block_means(k: np.ndarray, block_size: int) -> np.ndarray:
+    """mu[b, hk, i, :] = mean of K[b, iB:(i+1)B, hk, :]  (report §2.2).
+
+    k: [batch, S, Hkv, D] (any float dtype; values are taken exactly).
+    Returns fp64 [batch, Hkv, n, D].  Computed block by block so the 1M
+    workload does not need an fp64 copy of all of K at once."""
+    b, S, Hkv, D = k.shape
+    n = num_blocks(S, block_size)
+    mu = np.empty((b, Hkv, n, D), dtype=np.float64)
+    for bb in range(b):
+        for i in range(n):
+            blk = np.asarray(k[bb, i * block_size:(i + 1) * block_size], dtype=np.float64)  # [B, Hkv, D]
+            mu[bb, :, i, :] = blk.mean(axis=0)
+    return mu
+
+
+# ----------------------------------------------------------------------------
+# Step 3 and 4: gate scores, causal rules, top-k (report §2.2, §2.3)
+# ----------------------------------------------------------------------------
+def gate_scores(q_row: np.ndarray, mu_head: np.ndarray) -> np.ndarray:
+    """s_i = <q, mu_i> for every block i  (report §2.2).  mu_head: [n, D]."""
+    return mu_head @ np.asarray(q_row, dtype=np.float64)
+
+
+def select_blocks(scores: np.ndarray, j: int, topk: int, causal: bool) -> List[int]:
+    """The chosen block indices, ascending.
+
+    causal (report §2.3): blocks after the own block j are excluded (score
+    -inf), block j is always kept and fills one of the k slots; the other
+    min(k-1, j) slots go to the highest-scoring past blocks 0..j-1, ties to
+    the lower index.
+    non-causal: the top min(k, n) of all n blocks, ties to the lower index.
+    """
+    n = len(scores)
+    if topk < 1:
+        raise ValueError("topk must be >= 1")
+    if causal:
+        past = list(range(j))
+        m = min(topk - 1, j)
+        # sort by (-score, index): a stable descending order
+        ranked = sorted(past, key=lambda i: (-float(scores[i]), i))
+        chosen = ranked[:m] + [j]
+    else:
+        ranked = sorted(range(n), key=lambda i: (-float(scores[i]), i))
+        chosen = ranked[:min(topk, n)]
+    return sorted(chosen)
+
+
+def key_positions(sel: Sequence[int], t: int, block_size: int, causal: bool) -> np.ndarray:
+    """Union of the chosen blocks' positions, ascending (report §2.2); the own
+    block is cut at the query itself (report §2.3, causal mask in-block)."""
+    B = block_size
+    j = t // B
+    parts = []
+    for i in sorted(sel):
+        if causal and i == j:
+            parts.append(np.arange(j * B, t + 1))
+        else:
+            parts.append(np.arange(i * B, (i + 1) * B))
+    return np.concatenate(parts) if parts else np.zeros((0,), dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------
+# Step 4: softmax attention over the union (report §2.2)
+# ----------------------------------------------------------------------------
+def attend(q_row: np.ndarray, k_head: np.ndarray, v_head: np.ndarray,
+           keys: np.ndarray, scale: float) -> np.ndarray:
+    """o = softmax(scale * q.K[keys]^T) V[keys], fp64, max-subtracted.
+
+    k_head, v_head: [S, D] for the row's KV head."""
+    q64 = np.asarray(q_row, dtype=np.float64)
+    logits = (np.asarray(k_head[keys], dtype=np.float64) @ q64) * scale
+    m = logits.max()
+    p = np.exp(logits - m)
+    return (p @ np.asarray(v_head[keys], dtype=np.float64)) / p.sum()
+
+
+def _attend_blocks(q64: np.ndarray, k_head: np.ndarray, v_head: np.ndarray,
+                   sel: Sequence[int], t: int, B: int, causal: bool, scale: float) -> np.ndarray:
+    """Same value as `attend` over key_positions(sel, ...), but reading the
+    chosen blocks as contiguous slices (no gathered copy of K), which keeps
+    the 1M rows affordable.  Logits are laid out in the same ascending key
+    order, so the result is the same softmax."""
+    j = t // B
+    logit_parts, v_parts = [], []
+    for i in sorted(sel):
+        hi = (t + 1) if (causal and i == j) else (i + 1) * B
+        kb = k_head[i * B:hi]
+        logit_parts.append((kb @ q64) * scale)
+        v_parts.append(v_head[i * B:hi])
+    logits = np.concatenate(logit_parts)
+    m = logits.max()
+    p = np.exp(logits - m)
+    acc = np.zeros(q64.shape[0], dtype=np.float64)
+    off = 0
+    for vp in v_parts:
+        acc += p[off:off + vp.shape[0]] @ vp
+        off += vp.shape[0]
+    return acc / p.sum()
+
+
+# ----------------------------------------------------------------------------
+# Whole forward
+# ----------------------------------------------------------------------------
+def _check_shapes(q, k, v, block_size, topk):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [batch, seqlen, heads, head_dim]")
+    b, S, Hq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != b or k.shape[1] != S or k.shape[3] != D:
+        raise ValueError("k and v must be [batch, seqlen, kv_heads, head_dim] matching q")
+    Hkv = k.shape[2]
+    if Hq % Hkv != 0:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    if topk < 1:
+        raise ValueError("topk must be >= 1")
+    num_blocks(S, block_size)
+    return b, S, Hq, Hkv, D
+
+
+def moba_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_size: int,
+                 topk: int, causal: bool = True) -> Tuple[np.ndarray, np.ndarray]:
+    """Full MoBA forward on small inputs.
+
+    Returns out [batch, S, Hq, D] fp64 and sel_idx [batch, Hq, S, topk] int32
+    (chosen blocks ascending, padded with -1)."""
+    b, S, Hq, Hkv, D = _check_shapes(q, k, v, block_size, topk)
+    rows = [(bb, t, h) for bb in range(b) for h in range(Hq) for t in range(S)]
+    res = moba_rows(q, k, v, block_size, topk, causal, rows)
+    out = np.zeros((b, S, Hq, D), dtype=np.float64)
+    sel_idx = np.full((b, Hq, S, topk), -1, dtype=np.int32)
+    for r, (bb, t, h) in enumerate(rows):
+        out[bb, t, h] = res.out[r]
+        sel_idx[bb, h, t] = res.sel[r]
+    return out, sel_idx
+
+
+class RowResult:
+    """Per-row oracle results: out [R, D], sel [R, topk] (-1 padded) and, for
+    the gate check, the fp64 gap between the last chosen and the first
+    unchosen past score and an upper bound on the fp32 error of one score."""
+
+    def __init__(self, R: int, D: int, topk: int):
+        self.out = np.zeros((R, D), dtype=np.float64)
+        self.sel = np.full((R, topk), -1, dtype=np.int32)
+        self.gap = np.full((R,), np.inf)
+        self.boundary = np.zeros((R, 2))
+        self.score_eps = np.zeros((R,))
+        self.scores: List[Optional[np.ndarray]] = [None] * R
+
+
+def moba_rows(q, k, v, block_size: int, topk: int, causal: bool,
+              rows: Sequence[Tuple[int, int, int]], mu: Optional[np.ndarray] = None,
+              given_sel: Optional[Sequence[Sequence[int]]] = None,
+              keep_scores: bool = False) -> RowResult:
+    """MoBA forward for the listed rows (b, t, h) only.
+
+    `mu` may be passed in (block_means of k) to avoid recomputing it.
+    `given_sel`, if set, replaces the gate's choice for each row (used to check
+    a row's output under another valid top-k set after a near tie).
+    q, k, v can be any array type with numpy indexing (torch CPU tensors are
+    converted per head)."""
+    b, S, Hq, Hkv, D = _check_shapes(q, k, v, block_size, topk)
+    B = block_size
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(D)
+    if mu is None:
+        mu = block_means(k, B)
+    absk = None
+    res = RowResult(len(rows), D, topk)
+    # group rows by (batch, kv head) so each head's K/V is converted once
+    order = sorted(range(len(rows)), key=lambda r: (rows[r][0], rows[r][2] // g, r))
+    cur = None
+    for r in order:
+        bb, t, h = rows[r]
+        hk = h // g
+        if cur != (bb, hk):
+            cur = (bb, hk)
+            k_head = np.asarray(k[bb, :, hk, :], dtype=np.float64)
+            v_head = np.asarray(v[bb, :, hk, :], dtype=np.float64)
+            absk = np.abs(k_head).reshape(S // B, B, D).mean(axis=1)  # [n, D] mean |K| per block
+        q64 = np.asarray(q[bb, t, h], dtype=np.float64)
+        j = t // B
+        scores = gate_scores(q64, mu[bb, hk])
+        if given_sel is None:
+            sel = select_blocks(scores, j, topk, causal)
+        else:
+            sel = sorted(int(i) for i in given_sel[r] if i >= 0)
+        res.out[r] = _attend_blocks(q64, k_head, v_head, sel, t, B, causal, scale)
+        res.sel[r, :len(sel)] = sel
+        if keep_scores:
+            res.scores[r] = scores
+        # gate margin and fp32 error bound (used by the near-tie protocol)
+        cand = list(range(j)) if causal else list(range(len(scores)))
+        m = min(topk - 1, j) if causal else min(topk, len(scores))
+        if 0 < m < len(cand):
+            ranked = sorted(cand, key=lambda i: (-float(scores[i]), i))
+            res.gap[r] = float(scores[ranked[m - 1]] - scores[ranked[m]])
+            res.boundary[r] = (scores[ranked[m - 1]], scores[ranked[m]])
+        res.score_eps[r] = score_error_bound(q64, mu[bb, hk], absk, B)
+    return res
+
+
+def near_tie_rows(res: "RowResult", rel: float = 1e-4) -> np.ndarray:
+    """Rows whose gate decision is a near tie: the fp64 gap between the last
+    chosen and the first unchosen past score is at most `rel` times their
+    magnitude, or at most twice the fp32 error bound of a score."""
+    mag = np.max(np.abs(res.boundary), axis=1)
+    return (res.gap <= rel * mag) | (res.gap <= 2.0 * res.score_eps)
+
+
+# ----------------------------------------------------------------------------
+# Near-tie protocol (test infrastructure for comparing an fp32 gate)
+# ----------------------------------------------------------------------------
+def _gamma(n: int, u: float = 2.0 ** -24) -> float:
+    """Higham's gamma_n = n u / (1 - n u) for fp32 unit roundoff u."""
+    return n * u / (1.0 - n * u)
+
+
+def score_error_bound(q64: np.ndarray, mu_head: np.ndarray, absk_mean: np.ndarray, B: int) -> float:
+    """An upper bound, over all blocks of this row, on |fp32 score - exact
+    score| when the block mean is summed and the dot product is formed in fp32
+    in any order: gamma_{3D+1} * sum|q_d mu_d| (the dot product, allowing the
+    mean to be split into three exact bf16 parts) plus
+    gamma_{B+2} * sum |q_d| mean|K_d| (the mean's sum and its division)."""
+    D = q64.shape[0]
+    dot = _gamma(3 * D + 1) * (np.abs(mu_head) @ np.abs(q64))
+    mean = _gamma(B + 2) * (absk_mean @ np.abs(q64))
+    return float(np.max(dot + mean))
+
+
+def valid_topk_set(scores: np.ndarray, chosen_past: Iterable[int], j: int, m: int, eps: float) -> bool:
+    """Whether `chosen_past` is a top-m set of the past scores up to 2*eps:
+    it has m distinct past blocks and no unchosen past block beats any chosen
+    one by more than 2*eps."""
+    chosen = sorted(set(int(i) for i in chosen_past))
+    if len(chosen) != m or any(i < 0 or i >= j for i in chosen):
+        return False
+    rest = [i for i in range(j) if i not in set(chosen)]
+    if not rest or not chosen:
+        return True
+    return max(scores[i] for i in rest) <= min(scores[i] for i in chosen) + 2.0 * eps
+
+
+def count_selected_keys(seqlen: int, block_size: int, topk: int, causal: bool) -> int:
+    """Keys attended by one query head summed over all positions, from the
+    selection rule alone (the gate picks exactly min(k-1, j) past blocks)."""
+    B = block_size
+    n = num_blocks(seqlen, B)
+    total = 0
+    for t in range(seqlen):
+        j = t // B
+        if causal:
+            total += min(topk - 1, j) * B + (t - j * B + 1)
+        else:
+            total += min(topk, n) * B
+    return total

@@ -1,0 +1,441 @@
+"""Pins for the fp64 oracle: checks against things other than the oracle itself.
+
+- printed figures (sparsity, block counts) from the pages, under tests/golden;
+- dense causal / non-causal attention from torch's scaled_dot_product_attention
+  in fp64 when every block is selected (course summary: all blocks selected is
+  exactly dense attention);
+- textbook masked attention for the special cases the report names
+  (own block only; sliding window = previous block + own, report §2.4);
+- brute force over all block subsets and an explicit S x S mask on tiny inputs;
+- invariants that hold exactly in exact arithmetic (future keys never matter,
+  report §2.3; key shifts, value affine maps, in-block permutations);
+- planted mistakes in a copy of the oracle, which the pins must catch.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle.moba_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_qkv(rng, b, S, Hq, Hkv, D, scale=1.0):
+    q = rng.standard_normal((b, S, Hq, D)) * scale
+    k = rng.standard_normal((b, S, Hkv, D)) * scale
+    v = rng.standard_normal((b, S, Hkv, D))
+    return q, k, v
+
+
+def sdpa_fp64(q, k, v, mask=None, causal=False):
+    """torch SDPA in fp64 on [b, S, H, D] numpy arrays; KV heads are expanded
+    with repeat_interleave (query head h reads KV head h // g)."""
+    Hq, Hkv = q.shape[2], k.shape[2]
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    m = None if mask is None else torch.from_numpy(mask)
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, is_causal=causal)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+# ----------------------------------------------------------------------------
+# printed figures
+# ----------------------------------------------------------------------------
+def test_printed_sparsity_pins_topk_counts_own_block():
+    cases = json.load(open(os.path.join(GOLDEN, "sparsity_figures.json")))["cases"]
+    rng = np.random.default_rng(0)
+    for c in cases:
+        n = O.num_blocks(c["seqlen"], c["block_size"])
+        assert n == c["num_blocks"]
+        # a late query (own block n-1): how many blocks does the gate keep?
+        scores = rng.standard_normal(n)
+        sel = O.select_blocks(scores, n - 1, c["topk"], True)
+        sparsity = 100.0 * (1.0 - len(sel) / n)
+        assert round(sparsity, 2) == c["sparsity_percent_printed"]
+
+
+def test_count_selected_keys_matches_rule():
+    # keys per head = sum over rows of min(k-1, j) B + (r+1)
+    S, B, k = 1024, 128, 3
+    n = S // B
+    want = sum(min(k - 1, j) * B * B + B * (B + 1) // 2 for j in range(n))
+    assert O.count_selected_keys(S, B, k, True) == want
+    # dense: topk >= n gives S(S+1)/2 keys
+    assert O.count_selected_keys(S, B, n, True) == S * (S + 1) // 2
+    assert O.count_selected_keys(S, B, 2 * n, True) == S * (S + 1) // 2
+
+
+# ----------------------------------------------------------------------------
+# dense equality and textbook special cases
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 64, 2, 2, 16, 8), (2, 96, 4, 2, 8, 16), (1, 128, 3, 1, 32, 32)])
+@pytest.mark.parametrize("extra", [0, 3])
+def test_dense_equality_causal(shape, extra):
+    b, S, Hq, Hkv, D, B = shape
+    rng = np.random.default_rng(1)
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    n = S // B
+    out, sel = O.moba_forward(q, k, v, B, n + extra, causal=True)
+    ref = sdpa_fp64(q, k, v, causal=True)
+    assert np.max(np.abs(out - ref)) < 1e-12
+    # every causal block is chosen
+    for t in range(S):
+        assert list(sel[0, 0, t][sel[0, 0, t] >= 0]) == list(range(t // B + 1))
+
+
+def test_dense_equality_noncausal():
+    b, S, Hq, Hkv, D, B = 1, 64, 2, 1, 16, 16
+    rng = np.random.default_rng(2)
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    out, sel = O.moba_forward(q, k, v, B, S // B, causal=False)
+    ref = sdpa_fp64(q, k, v, causal=False)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_topk1_is_block_local_causal_attention():
+    b, S, Hq, Hkv, D, B = 1, 96, 2, 2, 16, 16
+    rng = np.random.default_rng(3)
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    out, _ = O.moba_forward(q, k, v, B, 1, causal=True)
+    t = np.arange(S)
+    mask = (t[None, :] <= t[:, None]) & (t[None, :] // B == t[:, None] // B)
+    ref = sdpa_fp64(q, k, v, mask=mask)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_sliding_window_construction():
+    """report §2.4: SWA = always routing to the most recent block.  Plant a
+    strong alignment between each query and its previous block's keys; with
+    topk = 2 the gate must pick exactly {j-1, j}, and the output must equal
+    attention over the window [(j-1)B, t]."""
+    b, S, Hq, Hkv, D, B = 1, 128, 1, 1, 16, 16
+    rng = np.random.default_rng(4)
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D, scale=0.1)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    q[0, :, 0, :] += 3.0 * u
+    # every block's keys carry a rising multiple of u, so the newest past
+    # block always has the largest mean-key score
+    for i in range(S // B):
+        k[0, i * B:(i + 1) * B, 0, :] += (0.5 * i) * u
+    out, sel = O.moba_forward(q, k, v, B, 2, causal=True)
+    t = np.arange(S)
+    j = t // B
+    lo = np.maximum(j - 1, 0) * B
+    mask = (t[None, :] <= t[:, None]) & (t[None, :] >= lo[:, None])
+    ref = sdpa_fp64(q, k, v, mask=mask)
+    for tt in range(S):
+        jj = tt // B
+        want = [jj - 1, jj] if jj >= 1 else [0, -1]
+        assert list(sel[0, 0, tt]) == want
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_gqa_head_mapping_dense():
+    b, S, Hq, Hkv, D, B = 1, 64, 6, 2, 8, 16
+    rng = np.random.default_rng(5)
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    out, _ = O.moba_forward(q, k, v, B, 100, causal=True)
+    ref = sdpa_fp64(q, k, v, causal=True)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_gqa_routing_equals_expanded_mha():
+    """Sparse case: a GQA call equals the MHA call on explicitly expanded K/V
+    (query head h reads KV head h // g, per-head routing)."""
+    b, S, Hq, Hkv, D, B = 1, 128, 4, 2, 8, 16
+    rng = np.random.default_rng(6)
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    out, sel = O.moba_forward(q, k, v, B, 3, causal=True)
+    ke = np.repeat(k, Hq // Hkv, axis=2)
+    ve = np.repeat(v, Hq // Hkv, axis=2)
+    out2, sel2 = O.moba_forward(q, ke, ve, B, 3, causal=True)
+    assert np.array_equal(sel, sel2)
+    assert np.max(np.abs(out - out2)) == 0.0
+
+
+# ----------------------------------------------------------------------------
+# brute force on tiny inputs
+# ----------------------------------------------------------------------------
+def brute_force(q, k, v, B, topk, causal):
+    """Enumerate every admissible block subset of the right size, take the one
+    with the largest score sum (ties: lexicographically smallest index tuple),
+    build the S x S mask element by element and run a per-query masked
+    softmax with explicit loops."""
+    b, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    n = S // B
+    out = np.zeros_like(q)
+    sels = np.full((b, Hq, S, topk), -1, dtype=np.int32)
+    for bb in range(b):
+        for h in range(Hq):
+            hk = h // g
+            mu = [[sum(k[bb, s, hk, d] for s in range(i * B, (i + 1) * B)) / B for d in range(D)]
+                  for i in range(n)]
+            for t in range(S):
+                j = t // B
+                score = [sum(q[bb, t, h, d] * mu[i][d] for d in range(D)) for i in range(n)]
+                if causal:
+                    m = min(topk - 1, j)
+                    best = None
+                    for sub in itertools.combinations(range(j), m):
+                        key = (sum(score[i] for i in sub), tuple(-i for i in sub))
+                        if best is None or key > best[0]:
+                            best = (key, sub)
+                    chosen = sorted(best[1] + (j,))
+                else:
+                    m = min(topk, n)
+                    best = None
+                    for sub in itertools.combinations(range(n), m):
+                        key = (sum(score[i] for i in sub), tuple(-i for i in sub))
+                        if best is None or key > best[0]:
+                            best = (key, sub)
+                    chosen = sorted(best[1])
+                sels[bb, h, t, :len(chosen)] = chosen
+                mask = [False] * S
+                for s in range(S):
+                    i = s // B
+                    if i in chosen and (not causal or s <= t):
+                        mask[s] = True
+                logits = [sum(q[bb, t, h, d] * k[bb, s, hk, d] for d in range(D)) / math.sqrt(D)
+                          if mask[s] else -math.inf for s in range(S)]
+                mx = max(logits)
+                w = [math.exp(x - mx) if x != -math.inf else 0.0 for x in logits]
+                z = sum(w)
+                for d in range(D):
+                    out[bb, t, h, d] = sum(w[s] * v[bb, s, hk, d] for s in range(S)) / z
+    return out, sels
+
+
+@pytest.mark.parametrize("S,B,topk,causal,Hq,Hkv", [
+    (32, 8, 2, True, 1, 1), (32, 4, 3, True, 2, 1), (24, 4, 4, True, 2, 2),
+    (32, 8, 1, True, 1, 1), (16, 4, 2, False, 1, 1), (24, 8, 9, True, 2, 1),
+])
+def test_bruteforce_tiny(S, B, topk, causal, Hq, Hkv):
+    rng = np.random.default_rng(7 + S + B + topk)
+    q, k, v = rand_qkv(rng, 1, S, Hq, Hkv, 4)
+    out, sel = O.moba_forward(q, k, v, B, topk, causal)
+    bout, bsel = brute_force(q, k, v, B, topk, causal)
+    assert np.array_equal(sel, bsel)
+    assert np.max(np.abs(out - bout)) < 1e-12
+
+
+def test_bruteforce_exact_ties_go_to_lower_index():
+    """Integer-valued keys make several block means (and scores) exactly
+    equal; the chosen set must be the lowest-indexed among the tied ones."""
+    S, B, D = 32, 4, 2
+    rng = np.random.default_rng(8)
+    q = rng.integers(-2, 3, size=(1, S, 1, D)).astype(np.float64)
+    base = rng.integers(-2, 3, size=(B, D)).astype(np.float64)
+    k = np.zeros((1, S, 1, D))
+    for i in range(S // B):
+        k[0, i * B:(i + 1) * B, 0] = base if i % 2 == 0 else base[::-1]  # equal means
+    v = rng.standard_normal((1, S, 1, D))
+    for topk in (2, 3):
+        out, sel = O.moba_forward(q, k, v, B, topk, True)
+        bout, bsel = brute_force(q, k, v, B, topk, True)
+        assert np.array_equal(sel, bsel)
+        assert np.max(np.abs(out - bout)) < 1e-12
+        # all past means are equal: the gate must take the lowest past blocks
+        for t in range(S):
+            j = t // B
+            m = min(topk - 1, j)
+            assert list(sel[0, 0, t][:m]) == list(range(m))
+
+
+# ----------------------------------------------------------------------------
+# invariants
+# ----------------------------------------------------------------------------
+def test_future_keys_never_matter():
+    b, S, Hq, Hkv, D, B = 1, 96, 2, 1, 8, 16
+    rng = np.random.default_rng(9)
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    out, sel = O.moba_forward(q, k, v, B, 3, True)
+    for t in [0, 5, 15, 16, 40, 63, 64, 80, 94]:
+        k2, v2 = k.copy(), v.copy()
+        k2[:, t + 1:] = rng.standard_normal(k2[:, t + 1:].shape) * 7.0
+        v2[:, t + 1:] = rng.standard_normal(v2[:, t + 1:].shape) * 7.0
+        res = O.moba_rows(q, k2, v2, B, 3, True, [(0, t, h) for h in range(Hq)])
+        for h in range(Hq):
+            assert np.array_equal(res.out[h], out[0, t, h])  # bit-exact
+            assert np.array_equal(res.sel[h], sel[0, h, t])
+
+
+def test_own_block_always_selected_and_padding():
+    b, S, Hq, Hkv, D, B = 1, 128, 2, 2, 8, 16
+    rng = np.random.default_rng(10)
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    for topk in (1, 2, 3, 5, 8, 12):
+        _, sel = O.moba_forward(q, k, v, B, topk, True)
+        for h in range(Hq):
+            for t in range(S):
+                j = t // B
+                row = sel[0, h, t]
+                valid = row[row >= 0]
+                assert j in valid
+                assert len(valid) == min(topk, j + 1)
+                assert np.all(valid <= j)
+                assert list(valid) == sorted(valid)
+                assert np.all(row[len(valid):] == -1)
+
+
+def test_key_shift_and_value_affine_invariance():
+    b, S, Hq, Hkv, D, B = 1, 128, 2, 1, 8, 16
+    rng = np.random.default_rng(11)
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    out, sel = O.moba_forward(q, k, v, B, 3, True)
+    c = rng.standard_normal(D)
+    out_k, sel_k = O.moba_forward(q, k + c, v, B, 3, True)
+    assert np.array_equal(sel, sel_k)
+    assert np.max(np.abs(out - out_k)) < 1e-12
+    a, cv = 1.7, rng.standard_normal(D)
+    out_v, sel_v = O.moba_forward(q, k, a * v + cv, B, 3, True)
+    assert np.array_equal(sel, sel_v)
+    assert np.max(np.abs(a * out + cv - out_v)) < 1e-12
+
+
+def test_permuting_keys_inside_a_past_block():
+    b, S, Hq, Hkv, D, B = 1, 128, 1, 1, 8, 16
+    rng = np.random.default_rng(12)
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    out, sel = O.moba_forward(q, k, v, B, 3, True)
+    perm = rng.permutation(B)
+    k2, v2 = k.copy(), v.copy()
+    blk = 2
+    k2[0, blk * B:(blk + 1) * B] = k[0, blk * B + perm]
+    v2[0, blk * B:(blk + 1) * B] = v[0, blk * B + perm]
+    out2, sel2 = O.moba_forward(q, k2, v2, B, 3, True)
+    assert np.array_equal(sel, sel2)
+    # rows past block 2 see a permuted but equal key set
+    assert np.max(np.abs(out[0, (blk + 1) * B:] - out2[0, (blk + 1) * B:])) < 1e-12
+
+
+def test_block_means_definition():
+    rng = np.random.default_rng(13)
+    k = rng.standard_normal((2, 32, 3, 4))
+    mu = O.block_means(k, 8)
+    assert mu.shape == (2, 3, 4, 4)
+    for bb in range(2):
+        for hk in range(3):
+            for i in range(4):
+                want = [math.fsum(k[bb, s, hk, d] for s in range(8 * i, 8 * i + 8)) / 8 for d in range(4)]
+                assert np.max(np.abs(mu[bb, hk, i] - want)) < 1e-15
+    with pytest.raises(ValueError):
+        O.block_means(k, 5)
+
+
+# ----------------------------------------------------------------------------
+# near-tie protocol
+# ----------------------------------------------------------------------------
+def test_near_tie_detection_and_valid_set():
+    b, S, Hq, Hkv, D, B = 1, 64, 1, 1, 4, 16
+    rng = np.random.default_rng(14)
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    # make blocks 0 and 1 means nearly equal: differ by 1e-9 relative
+    k[0, 16:32] = k[0, 0:16] * (1 + 1e-9)
+    t = 63
+    res = O.moba_rows(q, k, v, B, 2, True, [(0, t, 0)], keep_scores=True)
+    s = res.scores[0]
+    if abs(s[0] - s[1]) < abs(s[2] - max(s[0], s[1])) and max(s[0], s[1]) > s[2]:
+        assert O.near_tie_rows(res)[0]
+    # a clear separation is not a near tie
+    k2 = k.copy()
+    k2[0, 16:32] += 3.0 * np.sign(q[0, t, 0])
+    res2 = O.moba_rows(q, k2, v, B, 2, True, [(0, t, 0)], keep_scores=True)
+    assert not O.near_tie_rows(res2)[0]
+    s2 = res2.scores[0]
+    best = int(np.argmax(s2[:3]))
+    assert O.valid_topk_set(s2, [best], 3, 1, res2.score_eps[0])
+    worst = int(np.argmin(s2[:3]))
+    assert not O.valid_topk_set(s2, [worst], 3, 1, res2.score_eps[0])
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: each variant must fail at least one pin above
+# ----------------------------------------------------------------------------
+def _mutant_select(kind):
+    orig = O.select_blocks
+
+    def sel(scores, j, topk, causal):
+        if kind == "no_forced_own":
+            past = list(range(j + 1))
+            ranked = sorted(past, key=lambda i: (-float(scores[i]), i))
+            return sorted(ranked[:min(topk, j + 1)])
+        if kind == "k_excludes_own":
+            ranked = sorted(range(j), key=lambda i: (-float(scores[i]), i))
+            return sorted(ranked[:min(topk, j)] + [j])
+        if kind == "ties_to_higher":
+            ranked = sorted(range(j), key=lambda i: (-float(scores[i]), -i))
+            return sorted(ranked[:min(topk - 1, j)] + [j])
+        if kind == "future_leak":
+            cand = list(range(min(j + 2, len(scores))))
+            cand.remove(j)
+            ranked = sorted(cand, key=lambda i: (-float(scores[i]), i))
+            return sorted(ranked[:min(topk - 1, len(cand))] + [j])
+        return orig(scores, j, topk, causal)
+    return sel
+
+
+@pytest.mark.parametrize("kind", ["no_forced_own", "k_excludes_own", "ties_to_higher", "future_leak"])
+def test_planted_selection_mistakes_are_caught(kind, monkeypatch):
+    rng = np.random.default_rng(15)
+    S, B = 32, 4
+    q, k, v = rand_qkv(rng, 1, S, 1, 1, 3)
+    # exact ties as in the tie test so the tie rule is exercised
+    base = rng.integers(-2, 3, size=(B, 3)).astype(np.float64)
+    kt = np.zeros((1, S, 1, 3))
+    for i in range(S // B):
+        kt[0, i * B:(i + 1) * B, 0] = base if i % 2 == 0 else base[::-1]
+    qt = rng.integers(-2, 3, size=(1, S, 1, 3)).astype(np.float64)
+    monkeypatch.setattr(O, "select_blocks", _mutant_select(kind))
+    caught = False
+    for (qq, kk) in ((q, k), (qt, kt)):
+        bout, bsel = brute_force(qq, kk, v, B, 2, True)
+        try:
+            out, sel = O.moba_forward(qq, kk, v, B, 2, True)
+        except ValueError:  # more blocks than slots: the mutant cannot even fill sel_idx
+            caught = True
+            continue
+        if not np.array_equal(sel, bsel) or np.max(np.abs(out - bout)) > 1e-12:
+            caught = True
+    # the printed sparsity figures catch a wrong slot count on their own
+    try:
+        test_printed_sparsity_pins_topk_counts_own_block()
+    except AssertionError:
+        caught = True
+    assert caught
+
+
+def test_planted_missing_scale_is_caught(monkeypatch):
+    rng = np.random.default_rng(16)
+    q, k, v = rand_qkv(rng, 1, 64, 1, 1, 16)
+    orig = O._attend_blocks
+
+    def no_scale(q64, kh, vh, sel, t, B, causal, scale):
+        return orig(q64, kh, vh, sel, t, B, causal, 1.0)
+    monkeypatch.setattr(O, "_attend_blocks", no_scale)
+    out, _ = O.moba_forward(q, k, v, 16, 4, True)
+    assert np.max(np.abs(out - sdpa_fp64(q, k, v, causal=True))) > 1e-6
+
+
+def test_planted_own_block_off_by_one_is_caught(monkeypatch):
+    """Letting the own block see one key past the query breaks future
+    invariance and dense equality."""
+    rng = np.random.default_rng(17)
+    q, k, v = rand_qkv(rng, 1, 64, 1, 1, 8)
+    orig = O._attend_blocks
+
+    def leak(q64, kh, vh, sel, t, B, causal, scale):
+        return orig(q64, kh, vh, sel, min(t + 1, kh.shape[0] - 1), B, causal, scale) if (t + 1) % B else \
+            orig(q64, kh, vh, sel, t, B, causal, scale)
+    monkeypatch.setattr(O, "_attend_blocks", leak)
+    out, _ = O.moba_forward(q, k, v, 16, 4, True)
+    assert np.max(np.abs(out - sdpa_fp64(q, k, v, causal=True))) > 1e-6
