@@ -1,0 +1,18 @@
+"""MoBA (Mixture of Block Attention) prefill forward for AMD MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind the C ABI of
+include/moba.h (libmoba.so, built in-tree); this package is a thin binding.
+"""
+from ._lib import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_F32,
+    LIB_PATH,
+    MAX_SELECTIVE_TOPK,
+    MobaError,
+    moba_attn_fwd,
+    moba_gate,
+    moba_meanpool,
+    status_string,
+    version,
+    workspace_bytes,
+)

@@ -1,0 +1,156 @@
+"""ctypes binding of the MoBA C ABI (include/moba.h).
+
+Argument marshalling only: every step of the forward runs in the HIP kernels
+of libmoba.so.  PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoba.so")
+
+MOBA_OK = 0
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+MAX_SELECTIVE_TOPK = 32
+
+_c_i64, _c_i32, _c_p, _c_sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+
+# name -> (restype, argtypes), one entry per function declared in include/moba.h
+SIGNATURES = {
+    "moba_version": (ctypes.c_int, []),
+    "moba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moba_workspace_bytes": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                            _c_i32, ctypes.POINTER(_c_sz)]),
+    "moba_attn_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                     _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "moba_meanpool": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p]),
+    "moba_gate": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                 _c_i32, _c_p, _c_p]),
+}
+
+
+class MobaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run block_sparse_attention_40_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.moba_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib.moba_version())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_dev(*ts: torch.Tensor):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def workspace_bytes(batch: int, seqlen: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                    dtype: int, block_size: int, topk: int, causal: bool = True) -> int:
+    out = _c_sz(0)
+    st = lib.moba_workspace_bytes(batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
+                                  int(bool(causal)), ctypes.byref(out))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_workspace_bytes")
+    return int(out.value)
+
+
+def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int, topk: int,
+                  causal: bool = True, out: Optional[torch.Tensor] = None,
+                  sel_idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  return_sel: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """MoBA prefill forward.  q [b, S, Hq, D], k/v [b, S, Hkv, D] (bf16 with
+    D = 128, or fp32 with D in {64, 128}).  Returns (out, sel_idx) where
+    sel_idx is [b, Hq, S, topk] int32 (None if return_sel is False and no
+    sel_idx tensor was passed)."""
+    _check_dev(q, k, v)
+    b, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype or k.shape != v.shape:
+        raise ValueError("q, k, v must share dtype; k and v must share shape")
+    if out is None:
+        out = torch.empty_like(q)
+    if sel_idx is None and return_sel:
+        sel_idx = torch.empty((b, Hq, S, topk), dtype=torch.int32, device=q.device)
+    nbytes = workspace_bytes(b, S, Hq, Hkv, D, dt, block_size, topk, causal)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check_dev(out, workspace)
+    if sel_idx is not None:
+        _check_dev(sel_idx)
+    st = lib.moba_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, S, Hq, Hkv, D, dt, block_size, topk,
+                           int(bool(causal)), out.data_ptr(), sel_idx.data_ptr() if sel_idx is not None else None,
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           _stream_ptr(q.device))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_attn_fwd")
+    return out, sel_idx
+
+
+def moba_meanpool(k: torch.Tensor, block_size: int, mu: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block means of the keys: mu [b, Hkv, S / block_size, D] fp32."""
+    _check_dev(k)
+    b, S, Hkv, D = k.shape
+    if mu is None:
+        mu = torch.empty((b, Hkv, S // max(block_size, 1), D), dtype=torch.float32, device=k.device)
+    st = lib.moba_meanpool(k.data_ptr(), b, S, Hkv, D, _dtype_code(k), block_size, mu.data_ptr(),
+                           _stream_ptr(k.device))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_meanpool")
+    return mu
+
+
+def moba_gate(q: torch.Tensor, mu: torch.Tensor, block_size: int, topk: int, causal: bool = True,
+              sel_idx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gate and top-k: sel_idx [b, Hq, S, topk] int32 from q and block means."""
+    _check_dev(q, mu)
+    b, S, Hq, D = q.shape
+    Hkv = mu.shape[1]
+    if sel_idx is None:
+        sel_idx = torch.empty((b, Hq, S, topk), dtype=torch.int32, device=q.device)
+    st = lib.moba_gate(q.data_ptr(), mu.data_ptr(), b, S, Hq, Hkv, D, _dtype_code(q), block_size, topk,
+                       int(bool(causal)), sel_idx.data_ptr(), _stream_ptr(q.device))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_gate")
+    return sel_idx

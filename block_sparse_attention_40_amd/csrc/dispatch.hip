@@ -1,0 +1,131 @@
+// MoE-style dispatch of query rows to key blocks (deep-dive report on MoBA,
+// section 3.2: the implementation groups work per selected block the way an
+// MoE layer dispatches tokens to experts).
+//
+// For one query chunk, list (hk, i) collects every (row, slot) whose row is
+// served by KV head hk and chose block i as a non-own block.  Three steps,
+// all on the device (no host round trip):
+//   1. list_scan:  per list, exclusive prefix over the gate work-groups of
+//                  their per-block counts (gate writes the counts);
+//   2. tile_plan:  one work-group scans the list sizes into list offsets and
+//                  cuts every list into tiles of kTileRows rows;
+//   3. scatter:    every row writes its (row, slot) entries into its lists at
+//                  (list offset + work-group start + local rank).
+// The order inside a work-group's stretch of a list may vary between runs;
+// each entry is computed independently, so results do not.
+#include "moba_device.h"
+#include "moba_kernels.h"
+#include "moba_plan.h"
+
+namespace moba {
+
+__global__ __launch_bounds__(256) void list_scan_kernel(int32_t* __restrict__ hist, int32_t* __restrict__ count,
+                                                        int64_t n, int64_t gate_wg, int64_t lists) {
+  const int64_t L = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (L >= lists) return;
+  const int64_t hk = L / n, i = L % n;
+  int32_t* col = hist + hk * gate_wg * n + i;
+  int32_t run = 0;
+  int64_t w = 0;
+  for (; w + 4 <= gate_wg; w += 4) {
+    const int32_t c0 = col[(w + 0) * n], c1 = col[(w + 1) * n], c2 = col[(w + 2) * n], c3 = col[(w + 3) * n];
+    col[(w + 0) * n] = run; run += c0;
+    col[(w + 1) * n] = run; run += c1;
+    col[(w + 2) * n] = run; run += c2;
+    col[(w + 3) * n] = run; run += c3;
+  }
+  for (; w < gate_wg; ++w) {
+    const int32_t c = col[w * n];
+    col[w * n] = run;
+    run += c;
+  }
+  count[L] = run;
+}
+
+// Exclusive block scan of 1024 values in LDS (Hillis-Steele).
+__device__ __forceinline__ int32_t block_excl_scan_1024(int32_t x, int32_t* buf, int32_t* total) {
+  const int tid = threadIdx.x;
+  buf[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t y = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += y;
+    __syncthreads();
+  }
+  const int32_t incl = buf[tid];
+  *total = buf[1023];
+  __syncthreads();
+  return incl - x;
+}
+
+__global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restrict__ count,
+                                                         int32_t* __restrict__ listoff,
+                                                         int32_t* __restrict__ tiles, int64_t lists) {
+  __shared__ int32_t buf[1024];
+  int32_t carry_e = 0, carry_t = 0;
+  for (int64_t base = 0; base < lists; base += 1024) {
+    const int64_t L = base + threadIdx.x;
+    const int32_t c = L < lists ? count[L] : 0;
+    const int32_t nt = (c + kTileRows - 1) / kTileRows;
+    int32_t tot_e, tot_t;
+    const int32_t ex_e = block_excl_scan_1024(c, buf, &tot_e);
+    const int32_t ex_t = block_excl_scan_1024(nt, buf, &tot_t);
+    if (L < lists) {
+      const int32_t off = carry_e + ex_e;
+      listoff[L] = off;
+      for (int32_t t = 0; t < nt; ++t) {
+        tiles[8 + 2 * (carry_t + ex_t + t)] = (int32_t)L;
+        tiles[9 + 2 * (carry_t + ex_t + t)] = off + t * kTileRows;
+      }
+    }
+    carry_e += tot_e;
+    carry_t += tot_t;
+  }
+  if (threadIdx.x == 0) {
+    listoff[lists] = carry_e;
+    tiles[0] = carry_t;
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(DispatchArgs a) {
+  extern __shared__ int32_t lcnt[];  // [n]
+  const int tid = threadIdx.x;
+  const int64_t w = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int64_t n = a.n;
+  for (int64_t i = tid; i < n; i += 256) lcnt[i] = 0;
+  __syncthreads();
+  const int g = a.g;
+  const int64_t pic = w * a.gate_t + tid / g;
+  const int h = hk * g + tid % g;
+  const bool valid = tid < a.gate_t * g && pic < a.cnt;
+  if (!valid) return;
+  const int64_t t = a.t0 + pic;
+  const int64_t j = t / a.block;
+  const int32_t* row = a.sel + (int64_t)h * a.sel_stride_h + (t - a.sel_pos_base) * a.topk;
+  const int32_t* wstart = a.hist + ((int64_t)hk * a.gate_wg + w) * n;
+  const int64_t local_row = pic * a.hq + h;
+  int slot = 0;
+  for (int c = 0; c < a.topk && slot < a.kp; ++c) {
+    const int32_t i = row[c];
+    if (i < 0) break;
+    if (a.causal && i == j) continue;  // own block: handled by the own-block kernel
+    const int32_t r = atomicAdd(&lcnt[i], 1);
+    const int64_t L = (int64_t)hk * n + i;
+    a.entries[a.listoff[L] + wstart[i] + r] = (int32_t)(local_row * a.kp + slot);
+    ++slot;
+  }
+}
+
+int launch_dispatch(const DispatchArgs& a, hipStream_t st) {
+  const int64_t lists = (int64_t)a.hkv * a.n;
+  hipLaunchKernelGGL(list_scan_kernel, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, st, a.hist, a.count,
+                     a.n, a.gate_wg, lists);
+  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, st, a.count, a.listoff, a.tiles, lists);
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)a.gate_wg, (unsigned)a.hkv), dim3(256),
+                     (size_t)a.n * sizeof(int32_t), st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace moba

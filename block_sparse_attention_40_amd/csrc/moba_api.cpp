@@ -1,0 +1,193 @@
+// C ABI of the MoBA forward: validation, workspace carving and launch
+// sequencing on the caller's stream.  No device allocation, no host sync.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/moba.h"
+#include "moba_kernels.h"
+#include "moba_plan.h"
+
+using namespace moba;
+
+namespace {
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+float scale_log2_for(int d) {
+  // log2(e) / sqrt(D): the softmax scale 1/sqrt(D) folded into base-2 exponentials
+  return (float)(1.4426950408889634 / std::sqrt((double)d));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moba_version(void) { return 100; }
+
+const char* moba_status_string(int status) {
+  switch (status) {
+    case MOBA_OK: return "ok";
+    case MOBA_ERR_NULL: return "a required pointer is NULL";
+    case MOBA_ERR_DTYPE: return "unknown dtype";
+    case MOBA_ERR_HEAD_DIM: return "head_dim not supported for this dtype (bf16: 128; fp32: 64 or 128)";
+    case MOBA_ERR_SEQ_NOT_DIVISIBLE: return "seqlen is not a multiple of block_size";
+    case MOBA_ERR_TOPK: return "topk < 1, or a selective topk above MOBA_MAX_SELECTIVE_TOPK";
+    case MOBA_ERR_GQA: return "num_q_heads is not a multiple of num_kv_heads, or the group exceeds 128";
+    case MOBA_ERR_WORKSPACE: return "workspace is NULL or smaller than moba_workspace_bytes()";
+    case MOBA_ERR_HIP: return "a HIP call or kernel launch failed";
+    case MOBA_ERR_SHAPE: return "non-positive or too large sizes";
+    case MOBA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int moba_workspace_bytes(int64_t batch, int64_t seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t dtype, int32_t block_size, int32_t topk, int32_t causal,
+                         size_t* bytes) {
+  if (!bytes) return MOBA_ERR_NULL;
+  Plan p;
+  const int st = make_plan(Shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
+                                 causal ? 1 : 0},
+                           &p);
+  if (st != MOBA_OK) return st;
+  *bytes = p.total;
+  return MOBA_OK;
+}
+
+int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, int64_t seqlen,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                  int32_t block_size, int32_t topk, int32_t causal, void* out, int32_t* sel_idx,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  const int st = make_plan(Shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
+                                 causal ? 1 : 0},
+                           &p);
+  if (st != MOBA_OK) return st;
+  if (!q || !k || !v || !out) return MOBA_ERR_NULL;
+  if (!workspace || workspace_bytes < p.total) return MOBA_ERR_WORKSPACE;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(workspace) ||
+      (sel_idx && (reinterpret_cast<uintptr_t>(sel_idx) & 3u)))
+    return MOBA_ERR_ALIGN;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* mu = reinterpret_cast<float*>(ws + p.off_mu);
+  int32_t* ws_sel = reinterpret_cast<int32_t*>(ws + p.off_sel);
+  int32_t* hist = reinterpret_cast<int32_t*>(ws + p.off_hist);
+  int32_t* count = reinterpret_cast<int32_t*>(ws + p.off_count);
+  int32_t* listoff = reinterpret_cast<int32_t*>(ws + p.off_listoff);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + p.off_tiles);
+  int32_t* entries = reinterpret_cast<int32_t*>(ws + p.off_entries);
+  float* part_o = reinterpret_cast<float*>(ws + p.off_part_o);
+  float* part_lse = reinterpret_cast<float*>(ws + p.off_part_lse);
+  const bool bf16 = dtype == MOBA_DTYPE_BF16;
+  const float sl2 = scale_log2_for(head_dim);
+
+  // 1. block means of the keys, all blocks of all batch entries
+  if (launch_meanpool(k, dtype, batch, seqlen, num_kv_heads, head_dim, block_size, mu, s)) return MOBA_ERR_HIP;
+
+  // 2.. per query chunk: gate, dispatch, past blocks, own block + merge
+  for (int64_t bb = 0; bb < batch; ++bb) {
+    for (int64_t jc = 0; jc < p.n; jc += p.chunk_blocks) {
+      const int64_t nb = (jc + p.chunk_blocks <= p.n) ? p.chunk_blocks : p.n - jc;
+      const int64_t t0 = jc * block_size, cnt = nb * block_size;
+      const int64_t gate_wg = (cnt + p.gate_t - 1) / p.gate_t;
+      int32_t* sel_base;
+      int64_t sel_stride_h, sel_pos_base;
+      if (sel_idx) {
+        sel_base = sel_idx + bb * (int64_t)num_q_heads * seqlen * topk;
+        sel_stride_h = seqlen * (int64_t)topk;
+        sel_pos_base = 0;
+      } else {
+        sel_base = ws_sel;
+        sel_stride_h = cnt * (int64_t)topk;
+        sel_pos_base = t0;
+      }
+      const bool need_lists = bf16 && p.kp > 0;
+
+      GateArgs ga{};
+      ga.q = q; ga.mu = mu; ga.sel = sel_base; ga.sel_stride_h = sel_stride_h; ga.sel_pos_base = sel_pos_base;
+      ga.hist = need_lists ? hist : nullptr;
+      ga.seqlen = seqlen; ga.n = p.n; ga.t0 = t0; ga.cnt = cnt; ga.gate_wg = gate_wg;
+      ga.hq = num_q_heads; ga.hkv = num_kv_heads; ga.block = block_size; ga.topk = topk; ga.kp = p.kp;
+      ga.causal = causal ? 1 : 0; ga.g = p.g; ga.gate_t = p.gate_t; ga.bb = (int32_t)bb;
+      if (launch_gate(ga, dtype, head_dim, s)) return MOBA_ERR_HIP;
+
+      if (!bf16) {
+        F32Args fa{};
+        fa.q = static_cast<const float*>(q); fa.k = static_cast<const float*>(k);
+        fa.v = static_cast<const float*>(v); fa.out = static_cast<float*>(out);
+        fa.sel = sel_base; fa.sel_stride_h = sel_stride_h; fa.sel_pos_base = sel_pos_base;
+        fa.seqlen = seqlen; fa.t0 = t0; fa.cnt = cnt; fa.hq = num_q_heads; fa.hkv = num_kv_heads;
+        fa.d = head_dim; fa.block = block_size; fa.topk = topk; fa.causal = causal ? 1 : 0; fa.g = p.g;
+        fa.bb = (int32_t)bb; fa.scale_log2 = sl2;
+        if (launch_attn_f32(fa, s)) return MOBA_ERR_HIP;
+        continue;
+      }
+
+      if (need_lists) {
+        DispatchArgs da{};
+        da.sel = sel_base; da.sel_stride_h = sel_stride_h; da.sel_pos_base = sel_pos_base;
+        da.hist = hist; da.count = count; da.listoff = listoff; da.tiles = tiles; da.entries = entries;
+        da.n = p.n; da.t0 = t0; da.cnt = cnt; da.gate_wg = gate_wg; da.hq = num_q_heads;
+        da.hkv = num_kv_heads; da.block = block_size; da.topk = topk; da.kp = p.kp;
+        da.causal = causal ? 1 : 0; da.g = p.g; da.gate_t = p.gate_t;
+        if (launch_dispatch(da, s)) return MOBA_ERR_HIP;
+
+        PastArgs pa{};
+        pa.q = q; pa.k = k; pa.v = v; pa.tiles = tiles; pa.count = count; pa.listoff = listoff;
+        pa.entries = entries; pa.part_o = part_o; pa.part_lse = part_lse; pa.seqlen = seqlen; pa.n = p.n;
+        pa.t0 = t0; pa.hq = num_q_heads; pa.hkv = num_kv_heads; pa.block = block_size; pa.kp = p.kp;
+        pa.g = p.g; pa.bb = (int32_t)bb; pa.max_tiles = (int32_t)p.max_tiles; pa.scale_log2 = sl2;
+        if (launch_attn_past(pa, s)) return MOBA_ERR_HIP;
+      }
+
+      OwnArgs oa{};
+      oa.q = q; oa.k = k; oa.v = v; oa.out = out; oa.part_o = part_o; oa.part_lse = part_lse;
+      oa.seqlen = seqlen; oa.n = p.n; oa.t0 = t0; oa.cnt = cnt; oa.hq = num_q_heads; oa.hkv = num_kv_heads;
+      oa.block = block_size; oa.kp = p.kp; oa.g = p.g; oa.own_t = p.own_t; oa.bb = (int32_t)bb;
+      oa.causal = causal ? 1 : 0; oa.scale_log2 = sl2;
+      if (launch_attn_own(oa, s)) return MOBA_ERR_HIP;
+    }
+  }
+  return MOBA_OK;
+}
+
+int moba_meanpool(const void* k, int64_t batch, int64_t seqlen, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t dtype, int32_t block_size, float* mu, void* stream) {
+  Plan p;
+  const int st = make_plan(Shape{batch, seqlen, num_kv_heads, num_kv_heads, head_dim, dtype, block_size, 1, 1}, &p);
+  if (st != MOBA_OK) return st;
+  if (!k || !mu) return MOBA_ERR_NULL;
+  if (misaligned(k) || misaligned(mu)) return MOBA_ERR_ALIGN;
+  if (launch_meanpool(k, dtype, batch, seqlen, num_kv_heads, head_dim, block_size, mu,
+                      reinterpret_cast<hipStream_t>(stream)))
+    return MOBA_ERR_HIP;
+  return MOBA_OK;
+}
+
+int moba_gate(const void* q, const float* mu, int64_t batch, int64_t seqlen, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t dtype, int32_t block_size, int32_t topk,
+              int32_t causal, int32_t* sel_idx, void* stream) {
+  Plan p;
+  const int st = make_plan(Shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
+                                 causal ? 1 : 0},
+                           &p);
+  if (st != MOBA_OK) return st;
+  if (!q || !mu || !sel_idx) return MOBA_ERR_NULL;
+  if (misaligned(q) || misaligned(mu) || (reinterpret_cast<uintptr_t>(sel_idx) & 3u)) return MOBA_ERR_ALIGN;
+  for (int64_t bb = 0; bb < batch; ++bb) {
+    GateArgs ga{};
+    ga.q = q; ga.mu = mu; ga.sel = sel_idx + bb * (int64_t)num_q_heads * seqlen * topk;
+    ga.sel_stride_h = seqlen * (int64_t)topk; ga.sel_pos_base = 0; ga.hist = nullptr;
+    ga.seqlen = seqlen; ga.n = p.n; ga.t0 = 0; ga.cnt = seqlen; ga.gate_wg = (seqlen + p.gate_t - 1) / p.gate_t;
+    ga.hq = num_q_heads; ga.hkv = num_kv_heads; ga.block = block_size; ga.topk = topk; ga.kp = p.kp;
+    ga.causal = causal ? 1 : 0; ga.g = p.g; ga.gate_t = p.gate_t; ga.bb = (int32_t)bb;
+    if (launch_gate(ga, dtype, head_dim, reinterpret_cast<hipStream_t>(stream))) return MOBA_ERR_HIP;
+  }
+  return MOBA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Launch interface between the host sequencing code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moba {
+
+// Gate over one query chunk: positions [t0, t0 + cnt) of batch entry bb.
+struct GateArgs {
+  const void* q;
+  const float* mu;       // [batch, hkv, n, D]
+  int32_t* sel;          // row (h, t) at sel + h * sel_stride_h + (t - sel_pos_base) * topk
+  int64_t sel_stride_h;
+  int64_t sel_pos_base;
+  int32_t* hist;         // [hkv, gate_wg, n] rows per block per work-group, or null
+  int64_t seqlen, n, t0, cnt, gate_wg;
+  int32_t hq, hkv, block, topk, kp, causal, g, gate_t, bb;
+};
+
+// Row lists of one chunk: list (hk, i) holds the (row, slot) pairs whose row
+// chose block i as a non-own block.
+struct DispatchArgs {
+  const int32_t* sel;    // as GateArgs
+  int64_t sel_stride_h;
+  int64_t sel_pos_base;
+  int32_t* hist;         // in: per-WG counts; out: per-WG start inside the list
+  int32_t* count;        // [hkv * n]
+  int32_t* listoff;      // [hkv * n + 1]
+  int32_t* tiles;        // [0] = number of tiles, [8 + 2 t] = list id, [9 + 2 t] = first entry
+  int32_t* entries;      // local_row * kp + slot
+  int64_t n, t0, cnt, gate_wg;
+  int32_t hq, hkv, block, topk, kp, causal, g, gate_t;
+};
+
+// Attention over one list tile (non-own blocks, no mask).
+struct PastArgs {
+  const void* q;         // whole q, [batch, seqlen, hq, D]
+  const void* k;
+  const void* v;
+  const int32_t* tiles;
+  const int32_t* count;
+  const int32_t* listoff;
+  const int32_t* entries;
+  float* part_o;         // [pairs, D] normalised partial output
+  float* part_lse;       // [pairs] log2-domain log-sum-exp of the scaled logits
+  int64_t seqlen, n, t0;
+  int32_t hq, hkv, block, kp, g, bb, max_tiles;
+  float scale_log2;      // log2(e) / sqrt(D)
+};
+
+// Own block (causal) + merge of the partials, writes out.
+struct OwnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const float* part_o;
+  const float* part_lse;
+  int64_t seqlen, n, t0, cnt;
+  int32_t hq, hkv, block, kp, g, own_t, bb, causal;
+  float scale_log2;
+};
+
+// fp32 path: one wave per query row, reading the row's selection directly.
+struct F32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* out;
+  const int32_t* sel;
+  int64_t sel_stride_h;
+  int64_t sel_pos_base;
+  int64_t seqlen, t0, cnt;
+  int32_t hq, hkv, d, block, topk, causal, g, bb;
+  float scale_log2;
+};
+
+int launch_meanpool(const void* k, int dtype, int64_t batch, int64_t seqlen, int hkv, int d, int block,
+                    float* mu, hipStream_t stream);
+int launch_gate(const GateArgs& a, int dtype, int d, hipStream_t stream);
+int launch_dispatch(const DispatchArgs& a, hipStream_t stream);
+int launch_attn_past(const PastArgs& a, hipStream_t stream);
+int launch_attn_own(const OwnArgs& a, hipStream_t stream);
+int launch_attn_f32(const F32Args& a, hipStream_t stream);
+
+}  // namespace moba

@@ -1,0 +1,77 @@
+// Host-side validation and workspace planning (no HIP calls).
+#include "moba_plan.h"
+
+#include <algorithm>
+
+#include "../../include/moba.h"
+
+namespace moba {
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int make_plan(const Shape& s, Plan* p) {
+  if (!p) return MOBA_ERR_NULL;
+  if (s.dtype != MOBA_DTYPE_F32 && s.dtype != MOBA_DTYPE_BF16) return MOBA_ERR_DTYPE;
+  if (s.batch < 1 || s.seqlen < 1 || s.hq < 1 || s.hkv < 1 || s.block < 1 || s.d < 1)
+    return MOBA_ERR_SHAPE;
+  if (s.dtype == MOBA_DTYPE_BF16 && s.d != 128) return MOBA_ERR_HEAD_DIM;
+  if (s.dtype == MOBA_DTYPE_F32 && s.d != 64 && s.d != 128) return MOBA_ERR_HEAD_DIM;
+  // no padding is defined for a ragged last block: reject it
+  if (s.seqlen % s.block != 0) return MOBA_ERR_SEQ_NOT_DIVISIBLE;
+  if (s.hq % s.hkv != 0) return MOBA_ERR_GQA;
+  if (s.hq / s.hkv > kMaxGroup) return MOBA_ERR_GQA;
+  if (s.topk < 1) return MOBA_ERR_TOPK;
+
+  Plan q{};
+  q.s = s;
+  q.n = s.seqlen / s.block;
+  // per-block counters live in LDS (32 KiB at most); grid z carries the batch
+  if (q.n > 8192 || s.batch > 65535) return MOBA_ERR_SHAPE;
+  q.keff = (int32_t)std::min<int64_t>(s.topk, q.n);
+  q.kp = s.causal ? q.keff - 1 : q.keff;
+  q.g = s.hq / s.hkv;
+  // candidates the gate ranks: past blocks (at most n-1) or all n blocks
+  const int64_t cand = s.causal ? q.n - 1 : q.n;
+  q.selective = q.kp < cand;
+  if (q.selective && q.kp > MOBA_MAX_SELECTIVE_TOPK) return MOBA_ERR_TOPK;
+
+  // index arithmetic bounds: rows and row*slot products stay in int32 range
+  const int64_t rows_total = s.batch * s.seqlen * (int64_t)s.hq;
+  if (s.seqlen > (int64_t(1) << 31) / s.hq || rows_total <= 0) return MOBA_ERR_SHAPE;
+
+  q.gate_t = std::max(1, kGateRows / q.g);
+  q.own_t = std::max(1, kTileRows / q.g);
+
+  const uint64_t per_block_partial =
+      (uint64_t)s.block * s.hq * (uint64_t)std::max(q.kp, 0) * (uint64_t)(s.d + 1) * 4u;
+  if (q.kp == 0) {
+    q.chunk_blocks = q.n;
+  } else {
+    q.chunk_blocks = (int64_t)std::max<uint64_t>(1, kPartialCapBytes / per_block_partial);
+    q.chunk_blocks = std::min<int64_t>(q.chunk_blocks, q.n);
+  }
+  const int64_t chunk_pos = q.chunk_blocks * s.block;
+  q.gate_wg = (chunk_pos + q.gate_t - 1) / q.gate_t;
+  q.max_pairs = chunk_pos * s.hq * (int64_t)q.kp;
+  if (q.max_pairs >= (int64_t(1) << 31)) return MOBA_ERR_SHAPE;
+  const int64_t lists = (int64_t)s.hkv * q.n;
+  q.max_tiles = (q.max_pairs + kTileRows - 1) / kTileRows + lists;
+  q.max_tiles = (q.max_tiles + 7) / 8 * 8;
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  q.off_mu = take((size_t)s.batch * s.hkv * q.n * s.d * sizeof(float));
+  q.off_sel = take((size_t)s.hq * chunk_pos * s.topk * sizeof(int32_t));
+  q.off_hist = take((size_t)s.hkv * q.gate_wg * q.n * sizeof(int32_t));
+  q.off_count = take((size_t)lists * sizeof(int32_t));
+  q.off_listoff = take((size_t)(lists + 1) * sizeof(int32_t));
+  q.off_tiles = take((size_t)(2 * q.max_tiles + 8) * sizeof(int32_t));
+  q.off_entries = take((size_t)std::max<int64_t>(q.max_pairs, 1) * sizeof(int32_t));
+  q.off_part_o = take((size_t)std::max<int64_t>(q.max_pairs, 1) * s.d * sizeof(float));
+  q.off_part_lse = take((size_t)std::max<int64_t>(q.max_pairs, 1) * sizeof(float));
+  q.total = off;
+  *p = q;
+  return MOBA_OK;
+}
+
+}  // namespace moba

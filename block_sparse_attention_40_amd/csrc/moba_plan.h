@@ -1,0 +1,45 @@
+// Host-side argument validation and workspace planning for the MoBA forward.
+// Pure C++ (no HIP calls), so it is exercised by the CPU tests as well.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace moba {
+
+// Rows of one gate work-group (threads; one query row per thread).
+constexpr int kGateRows = 256;
+// Query rows of one attention tile (4 waves x 32 rows).
+constexpr int kTileRows = 128;
+// Largest query-head group (num_q_heads / num_kv_heads) the tiles support.
+constexpr int kMaxGroup = 128;
+// Upper bound on the fp32 partial-result buffer of one query chunk.
+constexpr uint64_t kPartialCapBytes = 8ull << 30;
+
+struct Shape {
+  int64_t batch, seqlen;
+  int32_t hq, hkv, d, dtype, block, topk, causal;
+};
+
+struct Plan {
+  Shape s;
+  int64_t n;            // number of blocks
+  int32_t keff;         // min(topk, n)
+  int32_t kp;           // past slots per row: keff - 1 (causal) or keff (non-causal)
+  int32_t g;            // query heads per KV head
+  int32_t gate_t;       // query positions per gate work-group
+  int32_t own_t;        // query positions per own-block tile
+  int64_t chunk_blocks; // query blocks processed per chunk
+  int64_t gate_wg;      // gate work-groups per KV head per chunk
+  int64_t max_pairs;    // (row, past block) pairs in one chunk, upper bound
+  int64_t max_tiles;    // attention tiles in one chunk, upper bound (multiple of 8)
+  bool selective;       // whether the gate has to score and rank blocks
+  // workspace layout (byte offsets, 256-aligned)
+  size_t off_mu, off_sel, off_hist, off_count, off_listoff, off_tiles, off_entries;
+  size_t off_part_o, off_part_lse, total;
+};
+
+// Validate `s` and fill `p`.  Returns a moba_status code.
+int make_plan(const Shape& s, Plan* p);
+
+}  // namespace moba

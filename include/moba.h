@@ -1,0 +1,131 @@
+/*
+ * moba.h -- C ABI of the MoBA (Mixture of Block Attention) prefill forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (deep-dive report on "MoBA: Mixture of Block Attention for
+ * Long-Context LLMs", sections 2.1-2.3, and the course page "Paper: MoBA
+ * (Moonshot)", summary):
+ *   - the length-S context is cut into n = S / B blocks of B keys (report 2.1);
+ *   - block i is summarised by the mean of its keys mu_i (report 2.2);
+ *   - each query row scores every block by s_i = <q, mu_i> (report 2.2);
+ *   - causal mode: blocks after the query's own block j = t / B are excluded,
+ *     block j is always chosen, and min(topk - 1, j) further past blocks with
+ *     the highest scores are chosen, ties going to the lower block index
+ *     (report 2.3; topk counts the own block, as the report's sparsity figures
+ *     81.25 % for 3 of 16 blocks and 95.31 % for 3 of 64 and 12 of 256 fix);
+ *   - the output is softmax(q K^T / sqrt(D)) V over the union of the chosen
+ *     blocks, with a causal mask inside the own block (report 2.2, 2.3).
+ *   With topk >= n every causal block is chosen and the result is dense causal
+ *   attention (course page summary).
+ *   Non-causal mode (causal = 0): no exclusion, no forced block, the top
+ *   min(topk, n) of all n blocks are chosen and attended in full.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  Layouts are dense row-major:
+ *       q, out : [batch, seqlen, num_q_heads,  head_dim]
+ *       k, v   : [batch, seqlen, num_kv_heads, head_dim]
+ *       mu     : [batch, num_kv_heads, seqlen / block_size, head_dim] fp32
+ *       sel_idx: [batch, num_q_heads, seqlen, topk] int32; the chosen block
+ *                indices of each row in ascending order, padded with -1.
+ *   - Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *   - dtype is MOBA_DTYPE_BF16 (q, k, v, out bf16; head_dim 128) or
+ *     MOBA_DTYPE_F32 (all fp32; head_dim 64 or 128).  Gate scores and all
+ *     accumulations are fp32 in both cases.
+ *   - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
+ *     stream).  Work is enqueued asynchronously on it; nothing synchronises.
+ *     A kernel fault surfaces at the caller's next synchronisation.
+ *   - Every argument is validated on the host before anything is enqueued;
+ *     on an error status nothing has been launched and nothing written.
+ *   - The functions are stateless and may be called from several threads;
+ *     concurrent calls need distinct workspaces.
+ */
+#ifndef MOBA_H_
+#define MOBA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moba_status {
+  MOBA_OK = 0,
+  MOBA_ERR_NULL = -1,               /* a required pointer is NULL */
+  MOBA_ERR_DTYPE = -2,              /* unknown dtype */
+  MOBA_ERR_HEAD_DIM = -3,           /* head_dim not supported for this dtype */
+  MOBA_ERR_SEQ_NOT_DIVISIBLE = -4,  /* seqlen % block_size != 0 (no padding is defined) */
+  MOBA_ERR_TOPK = -5,               /* topk < 1, or a selective topk above the supported maximum */
+  MOBA_ERR_GQA = -6,                /* num_q_heads % num_kv_heads != 0 or group too large */
+  MOBA_ERR_WORKSPACE = -7,          /* workspace NULL or smaller than moba_workspace_bytes() */
+  MOBA_ERR_HIP = -8,                /* a HIP runtime call or kernel launch failed */
+  MOBA_ERR_SHAPE = -9,              /* non-positive or overflowing sizes */
+  MOBA_ERR_ALIGN = -10              /* a pointer is not 16-byte aligned */
+};
+
+enum moba_dtype { MOBA_DTYPE_F32 = 0, MOBA_DTYPE_BF16 = 1 };
+
+/* Largest topk - 1 (causal) or topk (non-causal) for which the gate really has
+ * to choose, i.e. when it is smaller than the number of candidate blocks.  A
+ * topk that already covers every candidate block is always accepted. */
+#define MOBA_MAX_SELECTIVE_TOPK 32
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int moba_version(void);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* moba_status_string(int status);
+
+/*
+ * moba_workspace_bytes: the size of the device workspace moba_attn_fwd needs
+ * for these shapes (block means, per-block row lists, tile list and the
+ * per-(row, past block) partial results, sized for the query chunk the
+ * library processes at a time).  Pure host arithmetic; touches no device.
+ * Returns a status; on MOBA_OK *bytes holds the size.
+ */
+int moba_workspace_bytes(int64_t batch, int64_t seqlen, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                         int32_t block_size, int32_t topk, int32_t causal,
+                         size_t* bytes);
+
+/*
+ * moba_attn_fwd: the whole MoBA prefill forward (block means, gate, top-k,
+ * block-sparse attention with the own-block causal mask).
+ *   q, k, v   : inputs, layouts above, same dtype.
+ *   out       : output, same shape and dtype as q.
+ *   sel_idx   : optional output of the chosen blocks (may be NULL).
+ *   workspace : device scratch of at least moba_workspace_bytes() bytes,
+ *               owned by the caller; its contents on entry do not matter.
+ * topk >= n is clamped to n (dense causal attention).  Returns a status.
+ */
+int moba_attn_fwd(const void* q, const void* k, const void* v,
+                  int64_t batch, int64_t seqlen, int32_t num_q_heads,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                  int32_t block_size, int32_t topk, int32_t causal,
+                  void* out, int32_t* sel_idx,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moba_meanpool: stage 1 alone (report 2.2): mu[b, hk, i, :] = mean of the B
+ * keys of block i, summed in fp32.  k as above; mu is written in full.
+ */
+int moba_meanpool(const void* k, int64_t batch, int64_t seqlen,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                  int32_t block_size, float* mu, void* stream);
+
+/*
+ * moba_gate: stage 2 alone (report 2.2, 2.3): fp32 scores <q, mu_i>, the
+ * causal exclusion and forced own block, and the top-k with ties to the
+ * lower index.  mu as written by moba_meanpool; sel_idx is written in full.
+ */
+int moba_gate(const void* q, const float* mu, int64_t batch, int64_t seqlen,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+              int32_t dtype, int32_t block_size, int32_t topk, int32_t causal,
+              int32_t* sel_idx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOBA_H_ */

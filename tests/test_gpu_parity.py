@@ -1,0 +1,183 @@
+"""GPU parity of the HIP MoBA forward (through the C ABI) against the fp64 oracle.
+
+Tolerances: out within max-abs 2e-2 for bf16 and 1e-4 for fp32; block
+selection exact except counted near ties (see parity_utils).  Block means are
+compared with a bound derived from fp32 summation (Higham's gamma_{B+2} times
+the mean absolute key)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_40_amd as M
+import moba_workloads as W
+import oracle.moba_oracle as O
+from parity_utils import compare, to_np32
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small(name, dtype, b, S, Hq, Hkv, D, B, topk, causal=True, seed=7):
+    return W.Workload(name, dtype, b, Hq, Hkv, S, D, B, topk, causal=causal, seed=seed)
+
+
+def run(w: W.Workload, rows=None, device_inputs=False):
+    say(f"[case] {w}")
+    q, k, v, _ = W.make_inputs(w, device=DEV if device_inputs else "cpu")
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, sel = M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal)
+    torch.cuda.synchronize()
+    rep = compare(q, k, v, out, sel, w.block_size, w.topk, w.causal, rows=rows, tol=TOL[w.dtype])
+    say(f"[parity] {w.name}: {rep.as_dict()}")
+    return rep, (q, k, v, out, sel)
+
+
+# ----------------------------------------------------------------------------
+# stage parity
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,b,S,Hkv,D,B", [
+    ("bf16", 1, 2048, 2, 128, 256), ("bf16", 2, 1536, 3, 128, 96), ("f32", 1, 1024, 1, 64, 128),
+    ("f32", 1, 512, 2, 128, 16), ("bf16", 1, 8192, 16, 128, 512),
+])
+def test_meanpool_matches_oracle(dtype, b, S, Hkv, D, B):
+    w = small("mp", dtype, b, S, Hkv, Hkv, D, B, 1, seed=3)
+    say(f"[case] meanpool {w}")
+    _, k, _, _ = W.make_inputs(w, device="cpu")
+    mu = M.moba_meanpool(k.to(DEV), B)
+    torch.cuda.synchronize()
+    k32 = to_np32(k)
+    ref = O.block_means(k32, B)
+    absmean = np.abs(k32.astype(np.float64)).reshape(b, S // B, B, Hkv, D).mean(axis=2).transpose(0, 2, 1, 3)
+    u = 2.0 ** -24
+    gam = (B + 2) * u / (1 - (B + 2) * u)
+    err = np.abs(mu.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= gam * absmean + 1e-30), float((err - gam * absmean).max())
+
+
+@pytest.mark.parametrize("dtype,S,Hq,Hkv,D,B,topk,causal", [
+    ("bf16", 2048, 4, 2, 128, 128, 3, True), ("bf16", 4096, 8, 1, 128, 64, 9, True),
+    ("bf16", 2048, 2, 2, 128, 128, 20, True), ("bf16", 1024, 2, 1, 128, 64, 5, False),
+    ("f32", 1024, 1, 1, 64, 128, 3, True), ("bf16", 4096, 2, 2, 128, 32, 33, True),
+])
+def test_gate_matches_oracle(dtype, S, Hq, Hkv, D, B, topk, causal):
+    w = small("gate", dtype, 1, S, Hq, Hkv, D, B, topk, causal, seed=11)
+    say(f"[case] gate {w}")
+    q, k, v, _ = W.make_inputs(w, device="cpu")
+    mu = M.moba_meanpool(k.to(DEV), B)
+    sel = M.moba_gate(q.to(DEV), mu, B, topk, causal)
+    torch.cuda.synchronize()
+    k32 = to_np32(k)
+    ref_mu = O.block_means(k32, B)
+    from parity_utils import RowSource
+    rows = [(0, t, h) for h in range(Hq) for t in range(S)]
+    res = O.moba_rows(RowSource(q), k32, to_np32(v), B, topk, causal, rows, mu=ref_mu, keep_scores=True)
+    ties = O.near_tie_rows(res)
+    selh = sel.cpu()
+    bad = 0
+    for r, (bb, t, h) in enumerate(rows):
+        g = selh[bb, h, t].numpy()
+        if not np.array_equal(g, res.sel[r]):
+            assert ties[r], f"row {(bb, t, h)}: gpu {g.tolist()} oracle {res.sel[r].tolist()} gap {res.gap[r]}"
+            bad += 1
+    say(f"[gate] near ties {int(ties.sum())}, differing near-tie rows {bad}")
+
+
+# ----------------------------------------------------------------------------
+# whole forward, small shapes spanning several tiles and ragged tails
+# ----------------------------------------------------------------------------
+SMALL = [
+    small("gqa_s2k", "bf16", 1, 2048, 4, 2, 128, 256, 3),
+    small("mha_b128", "bf16", 1, 1536, 2, 2, 128, 128, 4),
+    small("ragged_b96", "bf16", 1, 960, 2, 1, 128, 96, 3),
+    small("b64_g8", "bf16", 1, 4096, 8, 1, 128, 64, 5),
+    small("batch2", "bf16", 2, 1024, 2, 2, 128, 128, 3),
+    small("topk1", "bf16", 1, 1024, 2, 2, 128, 128, 1),
+    small("dense_eq", "bf16", 1, 1024, 2, 1, 128, 128, 8),
+    small("dense_clamp", "bf16", 1, 1024, 2, 1, 128, 128, 20),
+    small("noncausal", "bf16", 1, 1024, 2, 2, 128, 128, 3, causal=False),
+    small("b16_tiny_blocks", "bf16", 1, 512, 2, 2, 128, 16, 4),
+    small("b2048_long", "bf16", 1, 8192, 4, 1, 128, 2048, 2),
+    small("single_block", "bf16", 1, 256, 2, 2, 128, 256, 3),
+    small("f32_d128_gqa", "f32", 1, 1024, 4, 2, 128, 128, 3),
+    small("f32_noncausal", "f32", 1, 512, 2, 1, 64, 64, 3, causal=False),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_forward_small(w):
+    run(w)
+
+
+def test_forward_dense_equals_sdpa():
+    """topk = n: equal to dense causal attention (course page: with every block
+    chosen MoBA is dense attention); checked against torch's fp32 CPU SDPA."""
+    w = small("dense_sdpa", "bf16", 1, 1024, 4, 2, 128, 128, 8)
+    q, k, v, _ = W.make_inputs(w, device="cpu")
+    out, _ = M.moba_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), 128, 8, True)
+    torch.cuda.synchronize()
+    g = 2
+    qt = q.float().permute(0, 2, 1, 3)
+    kt = k.float().permute(0, 2, 1, 3).repeat_interleave(g, 1)
+    vt = v.float().permute(0, 2, 1, 3).repeat_interleave(g, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True).permute(0, 2, 1, 3)
+    assert (out.cpu().float() - ref).abs().max().item() < 2e-2
+
+
+def test_forward_deterministic_and_future_invariant():
+    w = small("determinism", "bf16", 1, 4096, 4, 2, 128, 256, 3)
+    q, k, v, _ = W.make_inputs(w, device=DEV)
+    o1, s1 = M.moba_attn_fwd(q, k, v, 256, 3, True)
+    o2, s2 = M.moba_attn_fwd(q, k, v, 256, 3, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    # perturb every key and value after position t: rows <= t must not move by one bit
+    for t in (700, 1023, 2100):
+        k2, v2 = k.clone(), v.clone()
+        k2[:, t + 1:] = (torch.randn_like(k2[:, t + 1:], dtype=torch.float32) * 5).to(k2.dtype)
+        v2[:, t + 1:] = (torch.randn_like(v2[:, t + 1:], dtype=torch.float32) * 5).to(v2.dtype)
+        o3, s3 = M.moba_attn_fwd(q, k2, v2, 256, 3, True)
+        torch.cuda.synchronize()
+        assert torch.equal(o3[:, :t + 1], o1[:, :t + 1])
+        assert torch.equal(s3[:, :, :t + 1], s1[:, :, :t + 1])
+
+
+# ----------------------------------------------------------------------------
+# the five workloads
+# ----------------------------------------------------------------------------
+def test_workload_tiny_f32_1k_both_topk():
+    w = W.WORKLOADS["tiny_f32_1k"]
+    run(w)
+    run(w.with_(topk=8))
+
+
+def test_workload_mha16_8k_sampled():
+    w = W.WORKLOADS["mha16_8k"]
+    run(w, rows=W.sample_rows(w, 256, seed=21), device_inputs=True)
+
+
+def test_workload_mha32_32k_needle_sampled():
+    w = W.WORKLOADS["mha32_32k_needle"]
+    rep, _ = run(w, rows=W.sample_rows(w, 256, seed=22), device_inputs=True)
+    assert rep.rows >= 32 * 200
+
+
+@pytest.mark.slow
+def test_workload_gqa32x8_128k_sampled():
+    w = W.WORKLOADS["gqa32x8_128k"]
+    run(w, rows=W.sample_rows(w, 24, seed=23), device_inputs=True)
+
+
+@pytest.mark.slow
+def test_workload_gqa32x8_1m_sampled():
+    w = W.WORKLOADS["gqa32x8_1m"]
+    run(w, rows=W.sample_rows(w, 8, seed=24), device_inputs=True)
