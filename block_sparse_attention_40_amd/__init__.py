@@ -12,6 +12,9 @@ from ._lib import (  # noqa: F401
     moba_attn_fwd,
     moba_gate,
     moba_meanpool,
+    profile_enable,
+    profile_read,
+    STAGES,
     status_string,
     version,
     workspace_bytes,

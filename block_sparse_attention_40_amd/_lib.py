@@ -33,7 +33,12 @@ SIGNATURES = {
     "moba_meanpool": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p]),
     "moba_gate": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                  _c_i32, _c_p, _c_p]),
+    "moba_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "moba_profile_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_i64),
+                                         ctypes.POINTER(ctypes.c_double), _c_i32]),
 }
+
+STAGES = ("meanpool", "gate", "dispatch", "attn_past", "attn_own", "attn_f32")
 
 
 class MobaError(RuntimeError):
@@ -126,6 +131,23 @@ def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size:
     if st != MOBA_OK:
         raise MobaError(st, "moba_attn_fwd")
     return out, sel_idx
+
+
+def profile_enable(on: bool = True) -> None:
+    lib.moba_profile_enable(int(bool(on)))
+
+
+def profile_read() -> dict:
+    """Per stage: summed kernel ms (HIP events on the launch stream), number
+    of launches and summed algorithmic work (FLOPs or bytes); clears them."""
+    n = len(STAGES)
+    ms = (ctypes.c_double * n)()
+    launches = (_c_i64 * n)()
+    work = (ctypes.c_double * n)()
+    st = lib.moba_profile_read(ms, launches, work, n)
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_profile_read")
+    return {name: {"ms": ms[i], "launches": int(launches[i]), "work": work[i]} for i, name in enumerate(STAGES)}
 
 
 def moba_meanpool(k: torch.Tensor, block_size: int, mu: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -4,6 +4,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
+#include <vector>
 
 #include "../../include/moba.h"
 #include "moba_kernels.h"
@@ -15,6 +17,62 @@ namespace {
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// ---- measurement support: events around each launch, work per stage ----
+struct ProfRec {
+  int stage;
+  hipEvent_t a, b;
+  double work;
+};
+struct Profiler {
+  bool on = false;
+  std::mutex mu;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Profiler g_prof;
+
+// Brackets one launch (or a short sequence of launches of one stage).
+struct StageScope {
+  int stage;
+  hipStream_t s;
+  double work;
+  hipEvent_t a = nullptr;
+  StageScope(int stage_, hipStream_t s_, double work_) : stage(stage_), s(s_), work(work_) {
+    if (g_prof.on) {
+      std::lock_guard<std::mutex> lk(g_prof.mu);
+      a = g_prof.get();
+      if (a) hipEventRecord(a, s);
+    }
+  }
+  ~StageScope() {
+    if (!a) return;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    hipEvent_t b = g_prof.get();
+    if (!b) return;
+    hipEventRecord(b, s);
+    g_prof.recs.push_back(ProfRec{stage, a, b, work});
+  }
+};
+
+// Sum over query positions [t0, t0 + cnt) of the past blocks a row attends.
+double past_blocks_sum(const Plan& p, int64_t t0, int64_t cnt) {
+  const int64_t B = p.s.block;
+  double tot = 0;
+  for (int64_t jb = t0 / B; jb < (t0 + cnt) / B; ++jb)
+    tot += (double)B * (double)(p.s.causal ? (jb < p.kp ? jb : p.kp) : p.kp);
+  return tot;
+}
+
 float scale_log2_for(int d) {
   // log2(e) / sqrt(D): the softmax scale 1/sqrt(D) folded into base-2 exponentials
   return (float)(1.4426950408889634 / std::sqrt((double)d));
@@ -25,6 +83,34 @@ float scale_log2_for(int d) {
 extern "C" {
 
 int moba_version(void) { return 100; }
+
+int moba_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = on != 0;
+  return MOBA_OK;
+}
+
+int moba_profile_read(double* ms, int64_t* launches, double* work, int32_t n) {
+  if (!ms || !launches || !work) return MOBA_ERR_NULL;
+  if (n < 0 || n > MOBA_NUM_STAGES) return MOBA_ERR_SHAPE;
+  for (int i = 0; i < n; ++i) { ms[i] = 0; launches[i] = 0; work[i] = 0; }
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  int status = MOBA_OK;
+  for (const ProfRec& r : g_prof.recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+      status = MOBA_ERR_HIP;
+    if (r.stage < n) {
+      ms[r.stage] += t;
+      launches[r.stage] += 1;
+      work[r.stage] += r.work;
+    }
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  return status;
+}
 
 const char* moba_status_string(int status) {
   switch (status) {
@@ -85,8 +171,14 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
   const bool bf16 = dtype == MOBA_DTYPE_BF16;
   const float sl2 = scale_log2_for(head_dim);
 
+  const double elt = bf16 ? 2.0 : 4.0;
+  const double D = head_dim;
   // 1. block means of the keys, all blocks of all batch entries
-  if (launch_meanpool(k, dtype, batch, seqlen, num_kv_heads, head_dim, block_size, mu, s)) return MOBA_ERR_HIP;
+  {
+    StageScope sc(MOBA_STAGE_MEANPOOL, s,
+                  (double)batch * seqlen * num_kv_heads * D * elt + (double)batch * num_kv_heads * p.n * D * 4.0);
+    if (launch_meanpool(k, dtype, batch, seqlen, num_kv_heads, head_dim, block_size, mu, s)) return MOBA_ERR_HIP;
+  }
 
   // 2.. per query chunk: gate, dispatch, past blocks, own block + merge
   for (int64_t bb = 0; bb < batch; ++bb) {
@@ -113,7 +205,14 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
       ga.seqlen = seqlen; ga.n = p.n; ga.t0 = t0; ga.cnt = cnt; ga.gate_wg = gate_wg;
       ga.hq = num_q_heads; ga.hkv = num_kv_heads; ga.block = block_size; ga.topk = topk; ga.kp = p.kp;
       ga.causal = causal ? 1 : 0; ga.g = p.g; ga.gate_t = p.gate_t; ga.bb = (int32_t)bb;
-      if (launch_gate(ga, dtype, head_dim, s)) return MOBA_ERR_HIP;
+      {
+        StageScope sc(MOBA_STAGE_GATE, s,
+                      (double)cnt * num_q_heads * D * elt + (double)num_kv_heads * p.n * D * 4.0 +
+                          (double)cnt * num_q_heads * topk * 4.0);
+        if (launch_gate(ga, dtype, head_dim, s)) return MOBA_ERR_HIP;
+      }
+      const double past_rows = past_blocks_sum(p, t0, cnt) * num_q_heads;  // (row, past block) pairs
+      const double own_keys = causal ? (double)nb * num_q_heads * (double)block_size * (block_size + 1) / 2.0 : 0.0;
 
       if (!bf16) {
         F32Args fa{};
@@ -123,6 +222,7 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
         fa.seqlen = seqlen; fa.t0 = t0; fa.cnt = cnt; fa.hq = num_q_heads; fa.hkv = num_kv_heads;
         fa.d = head_dim; fa.block = block_size; fa.topk = topk; fa.causal = causal ? 1 : 0; fa.g = p.g;
         fa.bb = (int32_t)bb; fa.scale_log2 = sl2;
+        StageScope sc(MOBA_STAGE_F32, s, 4.0 * D * (past_rows * block_size + own_keys));
         if (launch_attn_f32(fa, s)) return MOBA_ERR_HIP;
         continue;
       }
@@ -134,14 +234,20 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
         da.n = p.n; da.t0 = t0; da.cnt = cnt; da.gate_wg = gate_wg; da.hq = num_q_heads;
         da.hkv = num_kv_heads; da.block = block_size; da.topk = topk; da.kp = p.kp;
         da.causal = causal ? 1 : 0; da.g = p.g; da.gate_t = p.gate_t;
-        if (launch_dispatch(da, s)) return MOBA_ERR_HIP;
+        {
+          StageScope sc(MOBA_STAGE_DISPATCH, s, (double)cnt * num_q_heads * topk * 4.0 + past_rows * 4.0);
+          if (launch_dispatch(da, s)) return MOBA_ERR_HIP;
+        }
 
         PastArgs pa{};
         pa.q = q; pa.k = k; pa.v = v; pa.tiles = tiles; pa.count = count; pa.listoff = listoff;
         pa.entries = entries; pa.part_o = part_o; pa.part_lse = part_lse; pa.seqlen = seqlen; pa.n = p.n;
         pa.t0 = t0; pa.hq = num_q_heads; pa.hkv = num_kv_heads; pa.block = block_size; pa.kp = p.kp;
         pa.g = p.g; pa.bb = (int32_t)bb; pa.max_tiles = (int32_t)p.max_tiles; pa.scale_log2 = sl2;
-        if (launch_attn_past(pa, s)) return MOBA_ERR_HIP;
+        {
+          StageScope sc(MOBA_STAGE_PAST, s, 4.0 * D * past_rows * block_size);
+          if (launch_attn_past(pa, s)) return MOBA_ERR_HIP;
+        }
       }
 
       OwnArgs oa{};
@@ -149,7 +255,10 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
       oa.seqlen = seqlen; oa.n = p.n; oa.t0 = t0; oa.cnt = cnt; oa.hq = num_q_heads; oa.hkv = num_kv_heads;
       oa.block = block_size; oa.kp = p.kp; oa.g = p.g; oa.own_t = p.own_t; oa.bb = (int32_t)bb;
       oa.causal = causal ? 1 : 0; oa.scale_log2 = sl2;
-      if (launch_attn_own(oa, s)) return MOBA_ERR_HIP;
+      {
+        StageScope sc(MOBA_STAGE_OWN, s, 4.0 * D * own_keys);
+        if (launch_attn_own(oa, s)) return MOBA_ERR_HIP;
+      }
     }
   }
   return MOBA_OK;

@@ -124,6 +124,30 @@ int moba_gate(const void* q, const float* mu, int64_t batch, int64_t seqlen,
               int32_t dtype, int32_t block_size, int32_t topk, int32_t causal,
               int32_t* sel_idx, void* stream);
 
+/*
+ * Measurement support (for benchmarks; not thread-safe).  While enabled, every
+ * kernel launch made by the calls above is bracketed by two HIP events
+ * recorded on the caller's stream, and the host adds the launch's
+ * algorithmic work to its stage: useful FLOPs (4 * head_dim per attended key)
+ * for the attention stages, compulsory HBM bytes for the others.
+ * moba_profile_read waits for the recorded events, writes per stage the
+ * summed kernel milliseconds, the number of launches and the summed work into
+ * the caller's host arrays (n entries each, n <= MOBA_NUM_STAGES), and clears
+ * the records.  The events are created by the library on first use and kept
+ * for reuse.
+ */
+enum moba_stage {
+  MOBA_STAGE_MEANPOOL = 0,  /* block means: bytes */
+  MOBA_STAGE_GATE = 1,      /* gate + top-k: bytes */
+  MOBA_STAGE_DISPATCH = 2,  /* per-block row lists: bytes */
+  MOBA_STAGE_PAST = 3,      /* attention over non-own blocks: FLOPs */
+  MOBA_STAGE_OWN = 4,       /* own block + merge: FLOPs */
+  MOBA_STAGE_F32 = 5,       /* fp32 attention path: FLOPs */
+  MOBA_NUM_STAGES = 6
+};
+int moba_profile_enable(int on);
+int moba_profile_read(double* ms, int64_t* launches, double* work, int32_t n);
+
 #ifdef __cplusplus
 }
 #endif
