@@ -8,7 +8,7 @@
 //   1. list_scan:  per list, exclusive prefix over the gate work-groups of
 //                  their per-block counts (gate writes the counts);
 //   2. tile_plan:  one work-group scans the list sizes into list offsets and
-//                  cuts every list into tiles of kTileRows rows;
+//                  cuts every list into tiles of tile_rows rows;
 //   3. scatter:    every row writes its (row, slot) entries into its lists at
 //                  (list offset + work-group start + local rank).
 // The order inside a work-group's stretch of a list may vary between runs;
@@ -61,13 +61,14 @@ __device__ __forceinline__ int32_t block_excl_scan_1024(int32_t x, int32_t* buf,
 
 __global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restrict__ count,
                                                          int32_t* __restrict__ listoff,
-                                                         int32_t* __restrict__ tiles, int64_t lists) {
+                                                         int32_t* __restrict__ tiles, int64_t lists,
+                                                         int32_t tile_rows) {
   __shared__ int32_t buf[1024];
   int32_t carry_e = 0, carry_t = 0;
   for (int64_t base = 0; base < lists; base += 1024) {
     const int64_t L = base + threadIdx.x;
     const int32_t c = L < lists ? count[L] : 0;
-    const int32_t nt = (c + kTileRows - 1) / kTileRows;
+    const int32_t nt = (c + tile_rows - 1) / tile_rows;
     int32_t tot_e, tot_t;
     const int32_t ex_e = block_excl_scan_1024(c, buf, &tot_e);
     const int32_t ex_t = block_excl_scan_1024(nt, buf, &tot_t);
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restri
       listoff[L] = off;
       for (int32_t t = 0; t < nt; ++t) {
         tiles[8 + 2 * (carry_t + ex_t + t)] = (int32_t)L;
-        tiles[9 + 2 * (carry_t + ex_t + t)] = off + t * kTileRows;
+        tiles[9 + 2 * (carry_t + ex_t + t)] = off + t * tile_rows;
       }
     }
     carry_e += tot_e;
@@ -122,7 +123,8 @@ int launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   const int64_t lists = (int64_t)a.hkv * a.n;
   hipLaunchKernelGGL(list_scan_kernel, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, st, a.hist, a.count,
                      a.n, a.gate_wg, lists);
-  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, st, a.count, a.listoff, a.tiles, lists);
+  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, st, a.count, a.listoff, a.tiles, lists,
+                     a.tile_rows);
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)a.gate_wg, (unsigned)a.hkv), dim3(256),
                      (size_t)a.n * sizeof(int32_t), st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -233,7 +233,7 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
         da.hist = hist; da.count = count; da.listoff = listoff; da.tiles = tiles; da.entries = entries;
         da.n = p.n; da.t0 = t0; da.cnt = cnt; da.gate_wg = gate_wg; da.hq = num_q_heads;
         da.hkv = num_kv_heads; da.block = block_size; da.topk = topk; da.kp = p.kp;
-        da.causal = causal ? 1 : 0; da.g = p.g; da.gate_t = p.gate_t;
+        da.causal = causal ? 1 : 0; da.g = p.g; da.gate_t = p.gate_t; da.tile_rows = p.tile_rows;
         {
           StageScope sc(MOBA_STAGE_DISPATCH, s, (double)cnt * num_q_heads * topk * 4.0 + past_rows * 4.0);
           if (launch_dispatch(da, s)) return MOBA_ERR_HIP;
@@ -243,7 +243,8 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
         pa.q = q; pa.k = k; pa.v = v; pa.tiles = tiles; pa.count = count; pa.listoff = listoff;
         pa.entries = entries; pa.part_o = part_o; pa.part_lse = part_lse; pa.seqlen = seqlen; pa.n = p.n;
         pa.t0 = t0; pa.hq = num_q_heads; pa.hkv = num_kv_heads; pa.block = block_size; pa.kp = p.kp;
-        pa.g = p.g; pa.bb = (int32_t)bb; pa.max_tiles = (int32_t)p.max_tiles; pa.scale_log2 = sl2;
+        pa.g = p.g; pa.bb = (int32_t)bb; pa.max_tiles = (int32_t)p.max_tiles; pa.tile_rows = p.tile_rows;
+        pa.scale_log2 = sl2;
         {
           StageScope sc(MOBA_STAGE_PAST, s, 4.0 * D * past_rows * block_size);
           if (launch_attn_past(pa, s)) return MOBA_ERR_HIP;

@@ -30,7 +30,7 @@ struct DispatchArgs {
   int32_t* tiles;        // [0] = number of tiles, [8 + 2 t] = list id, [9 + 2 t] = first entry
   int32_t* entries;      // local_row * kp + slot
   int64_t n, t0, cnt, gate_wg;
-  int32_t hq, hkv, block, topk, kp, causal, g, gate_t;
+  int32_t hq, hkv, block, topk, kp, causal, g, gate_t, tile_rows;
 };
 
 // Attention over one list tile (non-own blocks, no mask).
@@ -45,7 +45,7 @@ struct PastArgs {
   float* part_o;         // [pairs, D] normalised partial output
   float* part_lse;       // [pairs] log2-domain log-sum-exp of the scaled logits
   int64_t seqlen, n, t0;
-  int32_t hq, hkv, block, kp, g, bb, max_tiles;
+  int32_t hq, hkv, block, kp, g, bb, max_tiles, tile_rows;
   float scale_log2;      // log2(e) / sqrt(D)
 };
 

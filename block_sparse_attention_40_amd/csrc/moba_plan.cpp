@@ -40,7 +40,7 @@ int make_plan(const Shape& s, Plan* p) {
   if (s.seqlen > (int64_t(1) << 31) / s.hq || rows_total <= 0) return MOBA_ERR_SHAPE;
 
   q.gate_t = std::max(1, kGateRows / q.g);
-  q.own_t = std::max(1, kTileRows / q.g);
+  q.own_t = std::max(1, kOwnRows / q.g);
 
   const uint64_t per_block_partial =
       (uint64_t)s.block * s.hq * (uint64_t)std::max(q.kp, 0) * (uint64_t)(s.d + 1) * 4u;
@@ -55,7 +55,8 @@ int make_plan(const Shape& s, Plan* p) {
   q.max_pairs = chunk_pos * s.hq * (int64_t)q.kp;
   if (q.max_pairs >= (int64_t(1) << 31)) return MOBA_ERR_SHAPE;
   const int64_t lists = (int64_t)s.hkv * q.n;
-  q.max_tiles = (q.max_pairs + kTileRows - 1) / kTileRows + lists;
+  q.tile_rows = (q.max_pairs / lists >= kLargeTileMinRows) ? kTileRowsLarge : kTileRowsSmall;
+  q.max_tiles = (q.max_pairs + q.tile_rows - 1) / q.tile_rows + lists;
   q.max_tiles = (q.max_tiles + 7) / 8 * 8;
 
   size_t off = 0;

@@ -9,8 +9,14 @@ namespace moba {
 
 // Rows of one gate work-group (threads; one query row per thread).
 constexpr int kGateRows = 256;
-// Query rows of one attention tile (4 waves x 32 rows).
-constexpr int kTileRows = 128;
+// Query rows of one past-block attention tile: 4 or 8 waves x 32 rows,
+// the larger when the per-block row lists are long.
+constexpr int kTileRowsSmall = 128;
+constexpr int kTileRowsLarge = 256;
+// Mean list length from which the large tile is used.
+constexpr int64_t kLargeTileMinRows = 2048;
+// Query rows of one own-block attention tile (8 waves x 32 rows).
+constexpr int kOwnRows = 256;
 // Largest query-head group (num_q_heads / num_kv_heads) the tiles support.
 constexpr int kMaxGroup = 128;
 // Upper bound on the fp32 partial-result buffer of one query chunk.
@@ -29,6 +35,7 @@ struct Plan {
   int32_t g;            // query heads per KV head
   int32_t gate_t;       // query positions per gate work-group
   int32_t own_t;        // query positions per own-block tile
+  int32_t tile_rows;    // rows per past-block attention tile
   int64_t chunk_blocks; // query blocks processed per chunk
   int64_t gate_wg;      // gate work-groups per KV head per chunk
   int64_t max_pairs;    // (row, past block) pairs in one chunk, upper bound
