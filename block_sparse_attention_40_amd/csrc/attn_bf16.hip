@@ -164,11 +164,14 @@ __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, fl
     }
   mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
   const float mxs = mx * c;
-  // decided per row (lanes l and l^32 agree), so a row's rounding never
-  // depends on the other rows sharing its wave
-  if (mxs > R.m + kLazyRescale) {
-    const float mn = __builtin_fmaxf(R.m, mxs);
-    const float alpha = fast_exp2(R.m - mn);
+  // The need to rescale is decided per row (lanes l and l^32 agree); rows
+  // that do not need it multiply by exactly 1, so a row's rounding never
+  // depends on the other rows sharing its wave.  The branch itself is
+  // wave-uniform.
+  const bool need = mxs > R.m + kLazyRescale;
+  if (__any(need)) {
+    const float mn = need ? __builtin_fmaxf(R.m, mxs) : R.m;
+    const float alpha = need ? fast_exp2(R.m - mn) : 1.0f;
     R.m = mn;
     R.l *= alpha;
 #pragma unroll
@@ -257,20 +260,23 @@ __global__ __launch_bounds__(NW * 64) void attn_past_kernel(PastArgs a) {
   const int64_t key_begin = blk * a.block, key_end = key_begin + a.block;
   const int nsl = (a.block + KT - 1) / KT;
 
+  const int nfull = a.block / KT;  // slices with 64 real keys; a ragged tail slice follows
   KVStager<NW> st;
   st.load(kbase, vbase, rs, key_begin, key_end);
   st.store(smem);
   __syncthreads();
-  for (int sl = 0; sl < nsl; ++sl) {
+  // unmasked and masked slices run in separate loops, so the accumulators
+  // keep one register assignment through each loop
+  for (int sl = 0; sl < nfull; ++sl) {
     const int64_t k0 = key_begin + (int64_t)sl * KT;
     if (sl + 1 < nsl) st.load(kbase, vbase, rs, k0 + KT, key_end);
-    const bf16raw* buf = smem + (sl & 1) * BUF_ELEMS;
-    if (key_end - k0 >= KT)
-      attend_slice<false>(buf, R, a.scale_log2, lane, NoMask{});
-    else
-      attend_slice<true>(buf, R, a.scale_log2, lane, TailMask{(int)(key_end - k0)});
+    attend_slice<false>(smem + (sl & 1) * BUF_ELEMS, R, a.scale_log2, lane, NoMask{});
     if (sl + 1 < nsl) st.store(smem + ((sl + 1) & 1) * BUF_ELEMS);
     __syncthreads();
+  }
+  if (nfull < nsl) {
+    const int64_t k0 = key_begin + (int64_t)nfull * KT;
+    attend_slice<true>(smem + (nfull & 1) * BUF_ELEMS, R, a.scale_log2, lane, TailMask{(int)(key_end - k0)});
   }
 
   const int lg = lane >> 5;
@@ -325,18 +331,24 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
     // last position any row of this wave holds: later slices are invisible to it
     int64_t wmax = p0 + (wave * 32 + 31) / G;
     if (wmax > a.block - 1) wmax = a.block - 1;
+    // slices wholly before the tile's first query need no mask
+    const int nfree = (int)(p0 / KT);
     KVStager<OWN_NW> st;
     st.load(kbase, vbase, rs, kb0, kb0 + last);
     st.store(smem);
     __syncthreads();
-    for (int sl = 0; sl < nsl; ++sl) {
+    for (int sl = 0; sl < nfree; ++sl) {
       const int64_t k0 = (int64_t)sl * KT;
       if (sl + 1 < nsl) st.load(kbase, vbase, rs, kb0 + k0 + KT, kb0 + last);
-      const bf16raw* buf = smem + (sl & 1) * BUF_ELEMS;
-      if (k0 + KT <= p0)
-        attend_slice<false>(buf, R, a.scale_log2, lane, NoMask{});
-      else if (k0 <= wmax)
-        attend_slice<true>(buf, R, a.scale_log2, lane, CausalMask{(int)(pos - k0)});
+      attend_slice<false>(smem + (sl & 1) * BUF_ELEMS, R, a.scale_log2, lane, NoMask{});
+      if (sl + 1 < nsl) st.store(smem + ((sl + 1) & 1) * BUF_ELEMS);
+      __syncthreads();
+    }
+    for (int sl = nfree; sl < nsl; ++sl) {
+      const int64_t k0 = (int64_t)sl * KT;
+      if (sl + 1 < nsl) st.load(kbase, vbase, rs, kb0 + k0 + KT, kb0 + last);
+      if (k0 <= wmax)
+        attend_slice<true>(smem + (sl & 1) * BUF_ELEMS, R, a.scale_log2, lane, CausalMask{(int)(pos - k0)});
       if (sl + 1 < nsl) st.store(smem + ((sl + 1) & 1) * BUF_ELEMS);
       __syncthreads();
     }
