@@ -30,7 +30,7 @@
 //   O^T += V^T P^T on the same instruction: P^T is fed straight from the
 //   score registers (inside each 16-key step the key order is permuted to the
 //   accumulator layout, and V^T is read from LDS in the same permuted order),
-//   V being stored transposed in LDS so those reads are 8-byte vectors.
+//   V being stored transposed in LDS so those reads are 16-byte vectors.
 //   The max is taken on raw scores; p = exp2(s * c - m) with
 //   c = log2(e)/sqrt(D), one FMA and one exp2 per score.  The running max m
 //   is only raised when a slice exceeds it by more than 2^8 (then the
@@ -45,12 +45,21 @@ namespace moba {
 constexpr int HD = 128;                    // head dim of the bf16 path
 constexpr int KT = 64;                     // keys per LDS slice
 constexpr int KS_STRIDE = HD + 8;          // bf16 per K row in LDS (272 B: conflict-free 16 B reads)
-constexpr int VT_STRIDE = KT + 4;          // bf16 per V^T row in LDS (136 B: conflict-free 8 B reads)
+constexpr int VT_STRIDE = KT + 8;          // bf16 per V^T row in LDS (144 B, see vt_index)
 constexpr int KS_ELEMS = KT * KS_STRIDE;
 constexpr int VT_ELEMS = HD * VT_STRIDE;
-constexpr int BUF_ELEMS = KS_ELEMS + VT_ELEMS;   // one slice buffer, 34816 B
+constexpr int BUF_ELEMS = KS_ELEMS + VT_ELEMS;   // one slice buffer, 35840 B
 constexpr float kLazyRescale = 8.0f;       // log2 units
 constexpr float kMInit = -1e30f;           // finite "minus infinity" for the running max
+
+// V^T layout in LDS.  Inside every 16-key step the key bits 2 and 3 are
+// swapped, so the 8 keys one MFMA lane needs (two groups of 4, 8 apart) form
+// one 16-byte unit; the unit index is XOR-swizzled with (d >> 4) & 7.  With
+// 144-byte rows the 16-byte operand reads are free of bank conflicts.
+__device__ __forceinline__ int vt_index(int d, int key) {
+  const int pk = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+  return d * VT_STRIDE + ((((pk >> 3) ^ (d >> 4)) & 7) << 3) + (pk & 7);
+}
 
 // Per-thread registers that carry one slice from HBM to LDS.  K: 64 keys x
 // 16 chunks of 16 bytes.  V: units of KPU consecutive keys x 8 consecutive d,
@@ -92,9 +101,10 @@ struct KVStager {
     const int dc = tid & 15, kg = tid >> 4;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      // V^T rows d = dc*8 + 2w (low bf16 of each word) and dc*8 + 2w + 1 (high bf16)
-      bf16raw* lo = vts + (dc * 8 + 2 * w) * VT_STRIDE + kg * KPU;
-      bf16raw* hi = lo + VT_STRIDE;
+      // V^T rows d = dc*8 + 2w (low bf16 of each word) and dc*8 + 2w + 1 (high bf16);
+      // the KPU keys of a unit stay adjacent under the key-bit swap
+      bf16raw* lo = vts + vt_index(dc * 8 + 2 * w, kg * KPU);
+      bf16raw* hi = vts + vt_index(dc * 8 + 2 * w + 1, kg * KPU);
       if constexpr (KPU == 4) {
         const uint32_t lo01 = __builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x05040100u);
         const uint32_t lo23 = __builtin_amdgcn_perm(vr[3][w], vr[2][w], 0x05040100u);
@@ -201,10 +211,8 @@ __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, fl
       const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const bf16raw* vrow = vts + (b * 32 + lr) * VT_STRIDE + kb * 32 + 16 * hs + lg * 4;
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 8);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+        // keys kb*32 + 16 hs + 8 (e/4) + 4 lg + e%4, e = 0..7: one 16-byte unit
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vts + vt_index(b * 32 + lr, kb * 32 + 16 * hs + 4 * lg));
         R.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, R.o[b], 0, 0, 0);
       }
     }
