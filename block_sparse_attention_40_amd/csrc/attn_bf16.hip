@@ -75,17 +75,20 @@ struct KVStager {
   __device__ __forceinline__ void load(const bf16raw* __restrict__ k, const bf16raw* __restrict__ v,
                                        int64_t rs, int64_t key0, int64_t key_end) {
     const int tid = threadIdx.x;
+    // Rows past key_end (a ragged last slice) repeat the last real row: their
+    // scores are masked to -inf, so they carry weight exactly 0.
 #pragma unroll
     for (int x = 0; x < KCH; ++x) {
       const int c = tid + NT * x, key = c >> 4, dc = c & 15;
-      kr[x] = (key0 + key < key_end) ? *reinterpret_cast<const u32x4*>(k + (key0 + key) * rs + dc * 8)
-                                     : u32x4{0u, 0u, 0u, 0u};
+      const int64_t kk = (key0 + key < key_end) ? key0 + key : key_end - 1;
+      kr[x] = *reinterpret_cast<const u32x4*>(k + kk * rs + dc * 8);
     }
     const int dc = tid & 15, kg = tid >> 4;
 #pragma unroll
     for (int y = 0; y < KPU; ++y) {
       const int64_t key = key0 + kg * KPU + y;
-      vr[y] = (key < key_end) ? *reinterpret_cast<const u32x4*>(v + key * rs + dc * 8) : u32x4{0u, 0u, 0u, 0u};
+      const int64_t kk = key < key_end ? key : key_end - 1;
+      vr[y] = *reinterpret_cast<const u32x4*>(v + kk * rs + dc * 8);
     }
   }
 
@@ -142,6 +145,45 @@ __device__ __forceinline__ void load_q(const bf16raw* qrow, int lane, bf16x8* qb
   for (int s = 0; s < 8; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + (lane >> 5) * 8 + 16 * s);
 }
 
+// Combine a value with the one held by lane l ^ 32 (the other half of the same
+// query's keys) without going through LDS.  v_permlane32_swap(a, b) returns,
+// for lane l < 32, (a[l], a[l + 32]) and for lane l >= 32, (b[l - 32], b[l]);
+// with a = b = x every lane gets its own value and its partner's.  (The two
+// results are copied to scalars before the bit cast: a bit cast applied to a
+// vector element directly reads element 0.)
+__device__ __forceinline__ void pair_values(float x, float& u, float& w) {
+  const uint32_t xb = __builtin_bit_cast(uint32_t, x);
+  const auto pr = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+  const uint32_t r0 = pr[0], r1 = pr[1];
+  u = __builtin_bit_cast(float, r0);
+  w = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float u, w;
+  pair_values(x, u, w);
+  return __builtin_fmaxf(u, w);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float u, w;
+  pair_values(x, u, w);
+  return u + w;
+}
+
+// Sum of the two bf16 halves of a packed word, accumulated into acc in fp32.
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
+// Byte offset of this lane's V^T operand unit for (b, kb, hs) = vt_lane_base +
+// vt_const(b, kb, hs): with d = 32 b + lr and unit (4 kb + 2 hs + lg) ^ ((d >> 4) & 7),
+// only bit 0 of the unit (lg ^ (lr >> 4)) depends on the lane.
+__device__ __forceinline__ int vt_lane_base(int lr, int lg) { return lr * VT_STRIDE * 2 + ((lg ^ (lr >> 4)) << 4); }
+__host__ __device__ constexpr int vt_const(int b, int kb, int hs) {
+  return b * 32 * VT_STRIDE * 2 + (((hs ^ (b & 1)) << 1) | ((kb ^ (b >> 1)) << 2)) * 16;
+}
+
 // Slice-relative key index held in accumulator element e of 32-key block kb.
 __device__ __forceinline__ int key_of(int kb, int e, int lg) { return kb * 32 + 8 * (e >> 2) + lg * 4 + (e & 3); }
 
@@ -150,7 +192,7 @@ __device__ __forceinline__ int key_of(int kb, int e, int lg) { return kb * 32 + 
 template <bool kMasked, typename Mask>
 __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, float c, int lane, Mask masked) {
   const bf16raw* ks = buf;
-  const bf16raw* vts = buf + KS_ELEMS;
+  const char* vtb = reinterpret_cast<const char*>(buf + KS_ELEMS) + vt_lane_base(lane & 31, lane >> 5);
   const int lr = lane & 31, lg = lane >> 5;
   f32x16 s[2];
 #pragma unroll
@@ -172,7 +214,7 @@ __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, fl
       if (kMasked && masked(key_of(kb, e, lg))) s[kb][e] = -__builtin_inff();
       mx = __builtin_fmaxf(mx, s[kb][e]);
     }
-  mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+  mx = pair_max(mx);
   const float mxs = mx * c;
   // The need to rescale is decided per row (lanes l and l^32 agree); rows
   // that do not need it multiply by exactly 1, so a row's rounding never
@@ -190,7 +232,6 @@ __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, fl
       for (int e = 0; e < 16; ++e) R.o[b][e] *= alpha;
   }
   const float negm = -R.m;
-  float ps = 0.f;
   uint32_t pk[2][8];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -198,10 +239,17 @@ __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, fl
     for (int e = 0; e < 16; e += 2) {
       const float p0 = fast_exp2(__builtin_fmaf(s[kb][e], c, negm));
       const float p1 = fast_exp2(__builtin_fmaf(s[kb][e + 1], c, negm));
-      ps += p0 + p1;
       pk[kb][e >> 1] = pack_bf16x2(p0, p1);
     }
-  R.l += ps;
+  // the row sum adds the bf16 weights that P V actually uses; two partial
+  // sums keep the dependency chains short
+  float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    ps0 = add_bf16_pair(pk[0][x], ps0);
+    ps1 = add_bf16_pair(pk[1][x], ps1);
+  }
+  R.l += ps0 + ps1;
   // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -212,7 +260,7 @@ __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, fl
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         // keys kb*32 + 16 hs + 8 (e/4) + 4 lg + e%4, e = 0..7: one 16-byte unit
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vts + vt_index(b * 32 + lr, kb * 32 + 16 * hs + 4 * lg));
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vtb + vt_const(b, kb, hs));
         R.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, R.o[b], 0, 0, 0);
       }
     }
@@ -288,7 +336,7 @@ __global__ __launch_bounds__(NW * 64) void attn_past_kernel(PastArgs a) {
   }
 
   const int lg = lane >> 5;
-  const float ltot = R.l + __shfl_xor(R.l, 32);
+  const float ltot = pair_sum(R.l);
   if (valid) {
     const float inv = 1.f / ltot;
     float* dst = a.part_o + (int64_t)entry * HD;
@@ -365,7 +413,7 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
   // merge this row's partials (log-sum-exp rule), normalise, store bf16
   const int lg = lane >> 5;
   const int64_t nslot = a.causal ? (j < a.kp ? j : a.kp) : a.kp;
-  const float l_own = R.l + __shfl_xor(R.l, 32);
+  const float l_own = pair_sum(R.l);
   const int64_t local_row = (j * a.block + pos - a.t0) * a.hq + h;
   // an own block with no visible key (non-causal mode) carries no weight
   const float m_own = (l_own > 0.f) ? R.m : -__builtin_inff();
