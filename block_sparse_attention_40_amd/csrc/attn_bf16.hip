@@ -45,25 +45,30 @@ namespace moba {
 constexpr int HD = 128;                    // head dim of the bf16 path
 constexpr int KT = 64;                     // keys per LDS slice
 constexpr int KS_STRIDE = HD + 8;          // bf16 per K row in LDS (272 B: conflict-free 16 B reads)
-constexpr int VT_STRIDE = KT + 8;          // bf16 per V^T row in LDS (144 B, see vt_index)
+constexpr int VT_STRIDE = KT;              // bf16 per V^T row in LDS (128 B, see vt_index)
 constexpr int KS_ELEMS = KT * KS_STRIDE;
 constexpr int VT_ELEMS = HD * VT_STRIDE;
-constexpr int BUF_ELEMS = KS_ELEMS + VT_ELEMS;   // one slice buffer, 35840 B
+constexpr int BUF_ELEMS = KS_ELEMS + VT_ELEMS;   // one slice buffer, 33792 B
 constexpr float kLazyRescale = 8.0f;       // log2 units
 constexpr float kMInit = -1e30f;           // finite "minus infinity" for the running max
 
 // V^T layout in LDS.  Inside every 16-key step the key bits 2 and 3 are
 // swapped, so the 8 keys one MFMA lane needs (two groups of 4, 8 apart) form
-// one 16-byte unit; the unit index is XOR-swizzled with (d >> 4) & 7.  With
-// 144-byte rows the 16-byte operand reads are free of bank conflicts.
+// one 16-byte unit; rows are 128 bytes and the unit index of row d is XORed
+// with ((d >> 3) ^ d) & 7.  Measured on gfx950 with the LDS bank-conflict
+// counter, this keeps both the operand reads (16 consecutive rows, one unit
+// each) and the transposing staging writes (rows 8 apart) close to
+// conflict-free; padded rows without the XOR make the writes 9-32x slower.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 3) ^ d) & 7; }
 __device__ __forceinline__ int vt_index(int d, int key) {
   const int pk = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-  return d * VT_STRIDE + ((((pk >> 3) ^ (d >> 4)) & 7) << 3) + (pk & 7);
+  return d * VT_STRIDE + ((((pk >> 3) ^ vt_swz(d)) & 7) << 3) + (pk & 7);
 }
 
 // Per-thread registers that carry one slice from HBM to LDS.  K: 64 keys x
 // 16 chunks of 16 bytes.  V: units of KPU consecutive keys x 8 consecutive d,
-// written as 8 rows of V^T (KPU keys each).
+// written as 8 rows of V^T (KPU keys each).  Offsets inside a slice are fixed
+// per thread; a slice is addressed by its first key only.
 template <int NW>
 struct KVStager {
   static constexpr int NT = NW * 64;
@@ -72,36 +77,38 @@ struct KVStager {
   u32x4 kr[KCH];
   u32x4 vr[KPU];
 
-  __device__ __forceinline__ void load(const bf16raw* __restrict__ k, const bf16raw* __restrict__ v,
-                                       int64_t rs, int64_t key0, int64_t key_end) {
-    const int tid = threadIdx.x;
-    // Rows past key_end (a ragged last slice) repeat the last real row: their
-    // scores are masked to -inf, so they carry weight exactly 0.
+  __device__ __forceinline__ static int k_key(int x) { return (int)(threadIdx.x + NT * x) >> 4; }
+  __device__ __forceinline__ static int k_dc(int x) { return (int)(threadIdx.x + NT * x) & 15; }
+  __device__ __forceinline__ static int v_key(int y) { return (int)(threadIdx.x >> 4) * KPU + y; }
+  __device__ __forceinline__ static int v_dc() { return (int)threadIdx.x & 15; }
+
+  // Slice of 64 keys starting at the row pointers k0p / v0p (row stride rs).
+  // kClamp: rows at or beyond `avail` (a ragged last slice) repeat row
+  // avail - 1; their scores are masked to -inf, so they carry weight 0.
+  template <bool kClamp>
+  __device__ __forceinline__ void load(const bf16raw* __restrict__ k0p, const bf16raw* __restrict__ v0p, int rs,
+                                       int avail) {
 #pragma unroll
     for (int x = 0; x < KCH; ++x) {
-      const int c = tid + NT * x, key = c >> 4, dc = c & 15;
-      const int64_t kk = (key0 + key < key_end) ? key0 + key : key_end - 1;
-      kr[x] = *reinterpret_cast<const u32x4*>(k + kk * rs + dc * 8);
+      int key = k_key(x);
+      if (kClamp) key = key < avail ? key : avail - 1;
+      kr[x] = *reinterpret_cast<const u32x4*>(k0p + key * rs + k_dc(x) * 8);
     }
-    const int dc = tid & 15, kg = tid >> 4;
 #pragma unroll
     for (int y = 0; y < KPU; ++y) {
-      const int64_t key = key0 + kg * KPU + y;
-      const int64_t kk = key < key_end ? key : key_end - 1;
-      vr[y] = *reinterpret_cast<const u32x4*>(v + kk * rs + dc * 8);
+      int key = v_key(y);
+      if (kClamp) key = key < avail ? key : avail - 1;
+      vr[y] = *reinterpret_cast<const u32x4*>(v0p + key * rs + v_dc() * 8);
     }
   }
 
   __device__ __forceinline__ void store(bf16raw* buf) const {
-    const int tid = threadIdx.x;
     bf16raw* ks = buf;
     bf16raw* vts = buf + KS_ELEMS;
 #pragma unroll
-    for (int x = 0; x < KCH; ++x) {
-      const int c = tid + NT * x, key = c >> 4, dc = c & 15;
-      *reinterpret_cast<u32x4*>(ks + key * KS_STRIDE + dc * 8) = kr[x];
-    }
-    const int dc = tid & 15, kg = tid >> 4;
+    for (int x = 0; x < KCH; ++x)
+      *reinterpret_cast<u32x4*>(ks + k_key(x) * KS_STRIDE + k_dc(x) * 8) = kr[x];
+    const int dc = v_dc(), kg = (int)threadIdx.x >> 4;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       // V^T rows d = dc*8 + 2w (low bf16 of each word) and dc*8 + 2w + 1 (high bf16);
@@ -176,36 +183,46 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
 }
 
-// Byte offset of this lane's V^T operand unit for (b, kb, hs) = vt_lane_base +
-// vt_const(b, kb, hs): with d = 32 b + lr and unit (4 kb + 2 hs + lg) ^ ((d >> 4) & 7),
-// only bit 0 of the unit (lg ^ (lr >> 4)) depends on the lane.
-__device__ __forceinline__ int vt_lane_base(int lr, int lg) { return lr * VT_STRIDE * 2 + ((lg ^ (lr >> 4)) << 4); }
-__host__ __device__ constexpr int vt_const(int b, int kb, int hs) {
-  return b * 32 * VT_STRIDE * 2 + (((hs ^ (b & 1)) << 1) | ((kb ^ (b >> 1)) << 2)) * 16;
-}
+// Byte offsets of this lane's V^T operand units.  Row d = 32 b + lr holds
+// unit (4 kb + 2 hs + lg) at position unit ^ vt_swz(d), and
+// vt_swz(32 b + lr) = vt_swz(lr) ^ (4 (b & 1)); so the position is
+// c ^ x with the compile-time c = (4 kb + 2 hs) ^ 4 (b & 1) and the lane's
+// x = lg ^ vt_swz(lr).  VtOffsets keeps lr * 128 + 16 (c ^ x) for all 8 c;
+// the row block b adds the immediate b * 32 * 128.
+struct VtOffsets {
+  int off[8];
+  __device__ __forceinline__ void init(int lane) {
+    const int lr = lane & 31, x = (lane >> 5) ^ vt_swz(lr);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) off[c] = lr * VT_STRIDE * 2 + ((c ^ x) << 4);
+  }
+};
+__host__ __device__ constexpr int vt_c(int b, int kb, int hs) { return (4 * kb + 2 * hs) ^ (4 * (b & 1)); }
 
 // Slice-relative key index held in accumulator element e of 32-key block kb.
 __device__ __forceinline__ int key_of(int kb, int e, int lg) { return kb * 32 + 8 * (e >> 2) + lg * 4 + (e & 3); }
 
-// One 64-key slice.  masked(kr): key kr of the slice is invisible to this
-// lane's query.
-template <bool kMasked, typename Mask>
-__device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, float c, int lane, Mask masked) {
-  const bf16raw* ks = buf;
-  const char* vtb = reinterpret_cast<const char*>(buf + KS_ELEMS) + vt_lane_base(lane & 31, lane >> 5);
-  const int lr = lane & 31, lg = lane >> 5;
-  f32x16 s[2];
+// S^T for one 64-key slice: two 32-key blocks of 32 keys x 32 queries.
+__device__ __forceinline__ void qk_slice(const bf16raw* buf, const bf16x8* qb, f32x16* s, int lane) {
+  const bf16raw* krow0 = buf + (lane & 31) * KS_STRIDE + (lane >> 5) * 8;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-    const bf16raw* krow = ks + (kb * 32 + lr) * KS_STRIDE + lg * 8;
 #pragma unroll
     for (int step = 0; step < 8; ++step) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * step);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, R.qb[step], s[kb], 0, 0, 0);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow0 + kb * 32 * KS_STRIDE + 16 * step);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[step], s[kb], 0, 0, 0);
     }
   }
+}
+
+// Online-softmax update with the scores of one slice; returns P^T as packed
+// bf16 pairs (pk[kb][x] holds accumulator elements 2x and 2x+1 of block kb).
+// masked(kr): key kr of the slice is invisible to this lane's query.
+template <bool kMasked, typename Mask>
+__device__ __forceinline__ void softmax_p(f32x16* s, WaveRows& R, float c, int lane, Mask masked, uint32_t (*pk)[8]) {
+  const int lg = lane >> 5;
   float mx = -__builtin_inff();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -232,7 +249,6 @@ __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, fl
       for (int e = 0; e < 16; ++e) R.o[b][e] *= alpha;
   }
   const float negm = -R.m;
-  uint32_t pk[2][8];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -250,7 +266,11 @@ __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, fl
     ps1 = add_bf16_pair(pk[1][x], ps1);
   }
   R.l += ps0 + ps1;
-  // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]
+}
+
+// O^T[d][q] += sum_key V^T[d][key] P^T[key][q] for one slice.
+__device__ __forceinline__ void pv(const bf16raw* buf, const uint32_t (*pk)[8], WaveRows& R, const VtOffsets& vo) {
+  const char* vtb = reinterpret_cast<const char*>(buf + KS_ELEMS);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -260,10 +280,27 @@ __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, fl
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         // keys kb*32 + 16 hs + 8 (e/4) + 4 lg + e%4, e = 0..7: one 16-byte unit
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vtb + vt_const(b, kb, hs));
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vtb + vo.off[vt_c(b, kb, hs)] + b * 32 * VT_STRIDE * 2);
         R.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, R.o[b], 0, 0, 0);
       }
     }
+}
+
+template <bool kMasked, typename Mask>
+__device__ __forceinline__ void softmax_pv(const bf16raw* buf, f32x16* s, WaveRows& R, const VtOffsets& vo,
+                                           float c, int lane, Mask masked) {
+  uint32_t pk[2][8];
+  softmax_p<kMasked>(s, R, c, lane, masked, pk);
+  pv(buf, pk, R, vo);
+}
+
+// One 64-key slice without pipelining (scores, softmax, P V).
+template <bool kMasked, typename Mask>
+__device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, const VtOffsets& vo, float c, int lane,
+                                             Mask masked) {
+  f32x16 s[2];
+  qk_slice(buf, R.qb, s, lane);
+  softmax_pv<kMasked>(buf, s, R, vo, c, lane, masked);
 }
 
 struct NoMask {
@@ -278,9 +315,9 @@ struct CausalMask {  // key kr (slice-relative) is visible iff kr <= qpos
   __device__ __forceinline__ bool operator()(int kr) const { return kr > qpos; }
 };
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void attn_past_kernel(PastArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16raw smem[2 * BUF_ELEMS];
+template <int NW, bool kPipe>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_past_kernel(PastArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16raw smem[(kPipe ? 3 : 2) * BUF_ELEMS];
   constexpr int ROWS = NW * 32;
   // XCD-aware order: consecutive tiles of one list run on the same XCD
   const int32_t total = a.tiles[0];
@@ -309,30 +346,65 @@ __global__ __launch_bounds__(NW * 64) void attn_past_kernel(PastArgs a) {
     load_q(reinterpret_cast<const bf16raw*>(a.q) + ((a.bb * a.seqlen + t) * a.hq + h) * HD, lane, R.qb);
   }
   rows_init(R);
+  VtOffsets vo;
+  vo.init(lane);
 
-  const int64_t rs = (int64_t)a.hkv * HD;
-  const bf16raw* kbase = reinterpret_cast<const bf16raw*>(a.k) + (a.bb * a.seqlen) * rs + hk * HD;
-  const bf16raw* vbase = reinterpret_cast<const bf16raw*>(a.v) + (a.bb * a.seqlen) * rs + hk * HD;
-  const int64_t key_begin = blk * a.block, key_end = key_begin + a.block;
+  const int rs = a.hkv * HD;
+  const bf16raw* kblk = reinterpret_cast<const bf16raw*>(a.k) + ((a.bb * a.seqlen) + blk * a.block) * (int64_t)rs + hk * HD;
+  const bf16raw* vblk = reinterpret_cast<const bf16raw*>(a.v) + ((a.bb * a.seqlen) + blk * a.block) * (int64_t)rs + hk * HD;
   const int nsl = (a.block + KT - 1) / KT;
-
-  const int nfull = a.block / KT;  // slices with 64 real keys; a ragged tail slice follows
   KVStager<NW> st;
-  st.load(kbase, vbase, rs, key_begin, key_end);
-  st.store(smem);
-  __syncthreads();
-  // unmasked and masked slices run in separate loops, so the accumulators
-  // keep one register assignment through each loop
-  for (int sl = 0; sl < nfull; ++sl) {
-    const int64_t k0 = key_begin + (int64_t)sl * KT;
-    if (sl + 1 < nsl) st.load(kbase, vbase, rs, k0 + KT, key_end);
-    attend_slice<false>(smem + (sl & 1) * BUF_ELEMS, R, a.scale_log2, lane, NoMask{});
-    if (sl + 1 < nsl) st.store(smem + ((sl + 1) & 1) * BUF_ELEMS);
+  if constexpr (kPipe) {
+    // Every slice is full.  The two waves that share a SIMD (wave w and
+    // w + 4) run half a slice out of phase: waves 0-3 do scores, softmax,
+    // P V of slice s; waves 4-7 first finish P V of slice s-1 (P kept in
+    // registers across the barrier), then scores and softmax of slice s.
+    // So while one wave of the pair is in its softmax on the vector ALU the
+    // other issues matrix instructions.  Three slice buffers: s-1 (still
+    // read by waves 4-7), s, and s+1 being staged.
+    const bool lag = wave >= NW / 2;
+    auto bufp = [&](int sl) { return smem + (sl % 3) * BUF_ELEMS; };
+    st.template load<false>(kblk, vblk, rs, KT);
+    st.store(bufp(0));
     __syncthreads();
-  }
-  if (nfull < nsl) {
-    const int64_t k0 = key_begin + (int64_t)nfull * KT;
-    attend_slice<true>(smem + (nfull & 1) * BUF_ELEMS, R, a.scale_log2, lane, TailMask{(int)(key_end - k0)});
+    uint32_t pk[2][8];
+    for (int sl = 0; sl < nsl; ++sl) {
+      if (sl + 1 < nsl) st.template load<false>(kblk + (int64_t)(sl + 1) * KT * rs, vblk + (int64_t)(sl + 1) * KT * rs, rs, KT);
+      f32x16 sc[2];
+      if (!lag) {
+        qk_slice(bufp(sl), R.qb, sc, lane);
+        softmax_p<false>(sc, R, a.scale_log2, lane, NoMask{}, pk);
+        pv(bufp(sl), pk, R, vo);
+      } else {
+        if (sl > 0) pv(bufp(sl - 1), pk, R, vo);
+        qk_slice(bufp(sl), R.qb, sc, lane);
+        softmax_p<false>(sc, R, a.scale_log2, lane, NoMask{}, pk);
+      }
+      if (sl + 1 < nsl) st.store(bufp(sl + 1));
+      __syncthreads();
+    }
+    if (lag) pv(bufp(nsl - 1), pk, R, vo);
+  } else {
+    // any block size: double-buffered slices, a ragged last slice masked
+    const int nfull = a.block / KT;
+    auto fetch = [&](int sl) {
+      const int64_t off = (int64_t)sl * KT * rs;
+      if (sl < nfull)
+        st.template load<false>(kblk + off, vblk + off, rs, KT);
+      else
+        st.template load<true>(kblk + off, vblk + off, rs, a.block - sl * KT);
+    };
+    fetch(0);
+    st.store(smem);
+    __syncthreads();
+    for (int sl = 0; sl < nfull; ++sl) {
+      if (sl + 1 < nsl) fetch(sl + 1);
+      attend_slice<false>(smem + (sl & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, NoMask{});
+      if (sl + 1 < nsl) st.store(smem + ((sl + 1) & 1) * BUF_ELEMS);
+      __syncthreads();
+    }
+    if (nfull < nsl)
+      attend_slice<true>(smem + (nfull & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, TailMask{a.block - nfull * KT});
   }
 
   const int lg = lane >> 5;
@@ -375,6 +447,8 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
     load_q(reinterpret_cast<const bf16raw*>(a.q) + ((a.bb * a.seqlen + t) * a.hq + h) * HD, lane, R.qb);
   }
   rows_init(R);
+  VtOffsets vo;
+  vo.init(lane);
 
   const int64_t rs = (int64_t)a.hkv * HD;
   const bf16raw* kbase = reinterpret_cast<const bf16raw*>(a.k) + (a.bb * a.seqlen) * rs + hk * HD;
@@ -389,22 +463,31 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
     if (wmax > a.block - 1) wmax = a.block - 1;
     // slices wholly before the tile's first query need no mask
     const int nfree = (int)(p0 / KT);
+    const int rsi = (int)rs;
+    const bf16raw* kblk = kbase + kb0 * rs;
+    const bf16raw* vblk = vbase + kb0 * rs;
     KVStager<OWN_NW> st;
-    st.load(kbase, vbase, rs, kb0, kb0 + last);
+    auto fetch = [&](int sl) {
+      const int64_t off = (int64_t)sl * KT * rs;
+      if ((sl + 1) * KT <= last)
+        st.template load<false>(kblk + off, vblk + off, rsi, KT);
+      else
+        st.template load<true>(kblk + off, vblk + off, rsi, (int)(last - sl * KT));
+    };
+    fetch(0);
     st.store(smem);
     __syncthreads();
     for (int sl = 0; sl < nfree; ++sl) {
-      const int64_t k0 = (int64_t)sl * KT;
-      if (sl + 1 < nsl) st.load(kbase, vbase, rs, kb0 + k0 + KT, kb0 + last);
-      attend_slice<false>(smem + (sl & 1) * BUF_ELEMS, R, a.scale_log2, lane, NoMask{});
+      if (sl + 1 < nsl) fetch(sl + 1);
+      attend_slice<false>(smem + (sl & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, NoMask{});
       if (sl + 1 < nsl) st.store(smem + ((sl + 1) & 1) * BUF_ELEMS);
       __syncthreads();
     }
     for (int sl = nfree; sl < nsl; ++sl) {
       const int64_t k0 = (int64_t)sl * KT;
-      if (sl + 1 < nsl) st.load(kbase, vbase, rs, kb0 + k0 + KT, kb0 + last);
+      if (sl + 1 < nsl) fetch(sl + 1);
       if (k0 <= wmax)
-        attend_slice<true>(smem + (sl & 1) * BUF_ELEMS, R, a.scale_log2, lane, CausalMask{(int)(pos - k0)});
+        attend_slice<true>(smem + (sl & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, CausalMask{(int)(pos - k0)});
       if (sl + 1 < nsl) st.store(smem + ((sl + 1) & 1) * BUF_ELEMS);
       __syncthreads();
     }
@@ -455,10 +538,17 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
 }
 
 int launch_attn_past(const PastArgs& a, hipStream_t st) {
-  if (a.tile_rows == 256)
-    hipLaunchKernelGGL(attn_past_kernel<8>, dim3((unsigned)a.max_tiles), dim3(512), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_past_kernel<4>, dim3((unsigned)a.max_tiles), dim3(256), 0, st, a);
+  const dim3 grid((unsigned)a.max_tiles);
+  if (a.tile_rows == 256) {
+    // 8 waves, one work-group per CU: phase-offset wave pairs when every slice is full
+    if (a.block % KT == 0)
+      hipLaunchKernelGGL((attn_past_kernel<8, true>), grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_past_kernel<8, false>), grid, dim3(512), 0, st, a);
+  } else {
+    // 4 waves, two independent work-groups per CU
+    hipLaunchKernelGGL((attn_past_kernel<4, false>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
