@@ -130,6 +130,14 @@ struct KVStager {
   }
 };
 
+// Wait until every vector-memory load issued so far has returned
+// (s_waitcnt vmcnt(0)), and keep the scheduler from moving loads across.
+__device__ __forceinline__ void drain_vmem() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt = 0; expcnt, lgkmcnt unconstrained
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Softmax state and accumulators of one wave's 32 query rows.
 struct WaveRows {
   bf16x8 qb[8];   // B operand of S^T: step s holds d = (lane/32)*8 + 16 s .. +7
@@ -206,14 +214,17 @@ __device__ __forceinline__ int key_of(int kb, int e, int lg) { return kb * 32 + 
 __device__ __forceinline__ void qk_slice(const bf16raw* buf, const bf16x8* qb, f32x16* s, int lane) {
   const bf16raw* krow0 = buf + (lane & 31) * KS_STRIDE + (lane >> 5) * 8;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int e = 0; e < 16; ++e) { s[0][e] = 0.f; s[1][e] = 0.f; }
+  bf16x8 ka[8], kb_[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+  for (int step = 0; step < 8; ++step) {
+    ka[step] = *reinterpret_cast<const bf16x8*>(krow0 + 16 * step);
+    kb_[step] = *reinterpret_cast<const bf16x8*>(krow0 + 32 * KS_STRIDE + 16 * step);
+  }
 #pragma unroll
-    for (int step = 0; step < 8; ++step) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow0 + kb * 32 * KS_STRIDE + 16 * step);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[step], s[kb], 0, 0, 0);
-    }
+  for (int step = 0; step < 8; ++step) {
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[step], qb[step], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb_[step], qb[step], s[1], 0, 0, 0);
   }
 }
 
@@ -317,7 +328,7 @@ struct CausalMask {  // key kr (slice-relative) is visible iff kr <= qpos
 
 template <int NW, bool kPipe>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_past_kernel(PastArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16raw smem[(kPipe ? 3 : 2) * BUF_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16raw smem[2 * BUF_ELEMS];
   constexpr int ROWS = NW * 32;
   // XCD-aware order: consecutive tiles of one list run on the same XCD
   const int32_t total = a.tiles[0];
@@ -355,35 +366,37 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int nsl = (a.block + KT - 1) / KT;
   KVStager<NW> st;
   if constexpr (kPipe) {
-    // Every slice is full.  The two waves that share a SIMD (wave w and
-    // w + 4) run half a slice out of phase: waves 0-3 do scores, softmax,
-    // P V of slice s; waves 4-7 first finish P V of slice s-1 (P kept in
-    // registers across the barrier), then scores and softmax of slice s.
-    // So while one wave of the pair is in its softmax on the vector ALU the
-    // other issues matrix instructions.  Three slice buffers: s-1 (still
-    // read by waves 4-7), s, and s+1 being staged.
-    const bool lag = wave >= NW / 2;
-    auto bufp = [&](int sl) { return smem + (sl % 3) * BUF_ELEMS; };
+    // Every slice is full.  Two register sets carry slices from HBM: the
+    // loads of slice s+2 are issued at the start of iteration s and written
+    // to LDS only at the end of iteration s+1, so each load has two slice
+    // iterations to arrive.  LDS stays double-buffered.  The loads are issued
+    // unconditionally (past the end they re-read the last slice) so the
+    // number of loads in flight is the same in every iteration and the wait
+    // before each LDS store leaves the younger loads outstanding.
+    KVStager<NW> st2;
+    auto sptr = [&](int sl) { return (int64_t)(sl < nsl ? sl : nsl - 1) * KT * rs; };
     st.template load<false>(kblk, vblk, rs, KT);
-    st.store(bufp(0));
+    st.store(smem);
+    // Everything loaded so far (the query rows, slice 0) must be complete
+    // before the prefetch loads go out: the loop's MFMAs read the query
+    // registers, and a wait for them inside the loop would also wait for the
+    // younger prefetch loads (the load counter is in-order).
+    drain_vmem();
+    st2.template load<false>(kblk + sptr(1), vblk + sptr(1), rs, KT);
     __syncthreads();
-    uint32_t pk[2][8];
-    for (int sl = 0; sl < nsl; ++sl) {
-      if (sl + 1 < nsl) st.template load<false>(kblk + (int64_t)(sl + 1) * KT * rs, vblk + (int64_t)(sl + 1) * KT * rs, rs, KT);
-      f32x16 sc[2];
-      if (!lag) {
-        qk_slice(bufp(sl), R.qb, sc, lane);
-        softmax_p<false>(sc, R, a.scale_log2, lane, NoMask{}, pk);
-        pv(bufp(sl), pk, R, vo);
-      } else {
-        if (sl > 0) pv(bufp(sl - 1), pk, R, vo);
-        qk_slice(bufp(sl), R.qb, sc, lane);
-        softmax_p<false>(sc, R, a.scale_log2, lane, NoMask{}, pk);
-      }
-      if (sl + 1 < nsl) st.store(bufp(sl + 1));
+    for (int sl = 0; sl < nsl; sl += 2) {
+      // slice sl in buffer 0; slice sl+1 in flight in st2
+      st.template load<false>(kblk + sptr(sl + 2), vblk + sptr(sl + 2), rs, KT);
+      attend_slice<false>(smem, R, vo, a.scale_log2, lane, NoMask{});
+      if (sl + 1 < nsl) st2.store(smem + BUF_ELEMS);
+      __syncthreads();
+      if (sl + 1 >= nsl) break;
+      // slice sl+1 in buffer 1; slice sl+2 in flight in st
+      st2.template load<false>(kblk + sptr(sl + 3), vblk + sptr(sl + 3), rs, KT);
+      attend_slice<false>(smem + BUF_ELEMS, R, vo, a.scale_log2, lane, NoMask{});
+      if (sl + 2 < nsl) st.store(smem);
       __syncthreads();
     }
-    if (lag) pv(bufp(nsl - 1), pk, R, vo);
   } else {
     // any block size: double-buffered slices, a ragged last slice masked
     const int nfull = a.block / KT;
@@ -540,7 +553,7 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
 int launch_attn_past(const PastArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.max_tiles);
   if (a.tile_rows == 256) {
-    // 8 waves, one work-group per CU: phase-offset wave pairs when every slice is full
+    // 8 waves, one work-group per CU: loads two slices ahead when every slice is full
     if (a.block % KT == 0)
       hipLaunchKernelGGL((attn_past_kernel<8, true>), grid, dim3(512), 0, st, a);
     else
