@@ -10,7 +10,7 @@
 //       entries that all chose the same block i of the same KV head.  The
 //       gathered query rows stay in registers; the block's keys and values
 //       stream through LDS in 64-key slices.  Output per entry: the
-//       normalised partial o (fp32) and its log2-domain log-sum-exp.
+//       normalised partial o (bf16) and its log2-domain log-sum-exp (fp32).
 //   attn_own_kernel: one work-group per 256 query rows of one own block (all
 //       query heads of a KV-head group together): causal attention over the
 //       own block up to each query, then the merge of that row's partials,
@@ -423,15 +423,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int lg = lane >> 5;
   const float ltot = pair_sum(R.l);
   if (valid) {
+    // the normalised partial is a convex combination of value rows, so bf16
+    // keeps it to 2^-9 of the largest |v|
     const float inv = 1.f / ltot;
-    float* dst = a.part_o + (int64_t)entry * HD;
+    bf16raw* dst = a.part_o + (int64_t)entry * HD;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 o4 = {R.o[b][4 * q4] * inv, R.o[b][4 * q4 + 1] * inv, R.o[b][4 * q4 + 2] * inv,
-                          R.o[b][4 * q4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(dst + b * 32 + 8 * q4 + lg * 4) = o4;
+        const u32x2 w2 = {pack_bf16x2(R.o[b][4 * q4] * inv, R.o[b][4 * q4 + 1] * inv),
+                          pack_bf16x2(R.o[b][4 * q4 + 2] * inv, R.o[b][4 * q4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(dst + b * 32 + 8 * q4 + lg * 4) = w2;
       }
     if (lg == 0) a.part_lse[entry] = R.m + fast_log2(ltot);
   }
@@ -525,14 +527,16 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
     const int64_t p = local_row * a.kp + s;
     const float w = fast_exp2(a.part_lse[p] - M);
     Lsum += w;
-    const float* src = a.part_o + p * HD;
+    const bf16raw* src = a.part_o + p * HD;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 o4 = *reinterpret_cast<const f32x4*>(src + b * 32 + 8 * q4 + lg * 4);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) R.o[b][4 * q4 + x] += w * o4[x];
+        const u32x2 o2 = *reinterpret_cast<const u32x2*>(src + b * 32 + 8 * q4 + lg * 4);
+        R.o[b][4 * q4] += w * bf16lo(o2[0]);
+        R.o[b][4 * q4 + 1] += w * bf16hi(o2[0]);
+        R.o[b][4 * q4 + 2] += w * bf16lo(o2[1]);
+        R.o[b][4 * q4 + 3] += w * bf16hi(o2[1]);
       }
   }
   if (valid) {

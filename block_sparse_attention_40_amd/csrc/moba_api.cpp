@@ -166,7 +166,7 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
   int32_t* listoff = reinterpret_cast<int32_t*>(ws + p.off_listoff);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + p.off_tiles);
   int32_t* entries = reinterpret_cast<int32_t*>(ws + p.off_entries);
-  float* part_o = reinterpret_cast<float*>(ws + p.off_part_o);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + p.off_part_o);
   float* part_lse = reinterpret_cast<float*>(ws + p.off_part_lse);
   const bool bf16 = dtype == MOBA_DTYPE_BF16;
   const float sl2 = scale_log2_for(head_dim);

@@ -42,7 +42,7 @@ struct PastArgs {
   const int32_t* count;
   const int32_t* listoff;
   const int32_t* entries;
-  float* part_o;         // [pairs, D] normalised partial output
+  uint16_t* part_o;      // [pairs, D] normalised partial output, bf16
   float* part_lse;       // [pairs] log2-domain log-sum-exp of the scaled logits
   int64_t seqlen, n, t0;
   int32_t hq, hkv, block, kp, g, bb, max_tiles, tile_rows;
@@ -55,7 +55,7 @@ struct OwnArgs {
   const void* k;
   const void* v;
   void* out;
-  const float* part_o;
+  const uint16_t* part_o;  // [pairs, D] bf16
   const float* part_lse;
   int64_t seqlen, n, t0, cnt;
   int32_t hq, hkv, block, kp, g, own_t, bb, causal;

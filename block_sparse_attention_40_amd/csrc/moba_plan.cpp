@@ -42,8 +42,9 @@ int make_plan(const Shape& s, Plan* p) {
   q.gate_t = std::max(1, kGateRows / q.g);
   q.own_t = std::max(1, kOwnRows / q.g);
 
+  // per (row, past block) pair: the normalised partial o in bf16 plus its lse in fp32
   const uint64_t per_block_partial =
-      (uint64_t)s.block * s.hq * (uint64_t)std::max(q.kp, 0) * (uint64_t)(s.d + 1) * 4u;
+      (uint64_t)s.block * s.hq * (uint64_t)std::max(q.kp, 0) * (uint64_t)(s.d * 2 + 4);
   if (q.kp == 0) {
     q.chunk_blocks = q.n;
   } else {
@@ -68,7 +69,7 @@ int make_plan(const Shape& s, Plan* p) {
   q.off_listoff = take((size_t)(lists + 1) * sizeof(int32_t));
   q.off_tiles = take((size_t)(2 * q.max_tiles + 8) * sizeof(int32_t));
   q.off_entries = take((size_t)std::max<int64_t>(q.max_pairs, 1) * sizeof(int32_t));
-  q.off_part_o = take((size_t)std::max<int64_t>(q.max_pairs, 1) * s.d * sizeof(float));
+  q.off_part_o = take((size_t)std::max<int64_t>(q.max_pairs, 1) * s.d * sizeof(uint16_t));
   q.off_part_lse = take((size_t)std::max<int64_t>(q.max_pairs, 1) * sizeof(float));
   q.total = off;
   *p = q;

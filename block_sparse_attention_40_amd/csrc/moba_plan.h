@@ -19,7 +19,7 @@ constexpr int64_t kLargeTileMinRows = 2048;
 constexpr int kOwnRows = 256;
 // Largest query-head group (num_q_heads / num_kv_heads) the tiles support.
 constexpr int kMaxGroup = 128;
-// Upper bound on the fp32 partial-result buffer of one query chunk.
+// Upper bound on the partial-result buffer of one query chunk (bf16 o + fp32 lse).
 constexpr uint64_t kPartialCapBytes = 8ull << 30;
 
 struct Shape {
