@@ -117,7 +117,7 @@ def roofline(stages, steps):
             "flops_per_launch": flops_per_launch}
 
 
-def cpu_baseline(W, w, inputs, budget_s, log):
+def cpu_baseline(W, w, inputs, budget_s, log, per_call=64):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     block means over all of K, then seeded query rows until the budget is used."""
     import numpy as np
@@ -147,31 +147,146 @@ def cpu_baseline(W, w, inputs, budget_s, log):
         def __getitem__(self, idx):
             return qh[idx].to(torch.float64).numpy()
 
+    # the oracle converts one KV head's K and V to fp64 per call: feed it
+    # batches of rows that share a KV head, heads in turn
     rows = W.sample_rows(w, 256, seed=99)
+    g = w.num_q_heads // w.num_kv_heads
     rng = np.random.default_rng(99)
-    rng.shuffle(rows)
-    done, keys, t_rows = 0, 0, 0.0
+    groups = {}
+    for r in rows:
+        groups.setdefault((r[0], r[2] // g), []).append(r)
+    per_head = []
+    for key in sorted(groups):
+        grp = groups[key]
+        rng.shuffle(grp)
+        per_head.append([grp[i:i + per_call] for i in range(0, len(grp), per_call)])
+    batches = [hb[i] for i in range(max(len(hb) for hb in per_head)) for hb in per_head if i < len(hb)]
+    done, keys, t_rows, calls = 0, 0, 0.0, 0
     D, B = w.head_dim, w.block_size
-    # rows grouped per KV head inside moba_rows: feed small batches
-    batch = 16
-    while done < len(rows) and t_rows < budget_s:
-        chunk = rows[done:done + batch]
+    for chunk in batches:
+        if t_rows >= budget_s:
+            break
         t0 = time.perf_counter()
         O.moba_rows(Rows(), k32, v32, B, w.topk, w.causal, chunk, mu=mu)
         t_rows += time.perf_counter() - t0
+        calls += 1
         for (_, t, _) in chunk:
             j = t // B
             keys += min(w.topk - 1, j) * B + (t - j * B + 1)
         done += len(chunk)
+        log(f"[cpu] {done} rows, {t_rows:.1f}s")
     fl = 4.0 * D * keys
     total_rows = w.batch * w.seqlen * w.num_q_heads
     log(f"[cpu] {done} rows in {t_rows:.1f}s")
     return {"value": fl / t_rows / 1e12, "unit": "TFLOP/s", "cores": blas_threads, "kind": "oracle",
             "sample": f"fp64 numpy oracle: block means over all of K ({t_mu:.1f}s) plus {done} seeded query rows "
-                      f"of the {w.name} workload ({t_rows:.1f}s); value = useful FLOPs of those rows / their time",
+                      f"of the {w.name} workload in {calls} calls of up to {per_call} rows sharing a KV head "
+                      f"({t_rows:.1f}s, per-head fp64 conversion included); value = useful FLOPs of those rows "
+                      f"/ their time",
             "host_cpus_available": cores, "rows": done, "rows_seconds": t_rows, "block_means_seconds": t_mu,
             "tokens_per_s_equiv": done / w.num_q_heads / t_rows,
             "extrapolated_full_seconds": t_mu + t_rows / done * total_rows}
+
+
+# ---------------------------------------------------------------------------
+# Profile evidence: the commands whose output the committed summaries under
+# profiles/ come from, and the converters that write those summaries.
+# ---------------------------------------------------------------------------
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_1m -o run -- "
+             "python3 -u bench.py --steps 3 --warmup 1 --secondary '' --no-cpu-baseline > gpurun_out/trace_1m.json")
+PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d gpurun_out/pmc_{counter} -o run -- "
+           "python3 -u bench.py --steps 1 --warmup 0 --secondary '' --no-cpu-baseline --copy-calibration 1024 "
+           "> gpurun_out/pmc_{counter}.json")
+COPY_KERNEL_TAG = "neg_kernel"   # torch.neg(src, out=dst): reads and writes the buffer once
+
+
+def copy_calibration(mib, log):
+    """A plain elementwise copy (negation) of `mib` MiB, three times: the
+    reference dispatch that scales the HBM byte counters."""
+    import torch
+    n = mib * 2 ** 20 // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 3 x {mib} MiB")
+    del src, dst
+
+
+def _per_dispatch(d, counter):
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    key = (r["Kernel_Name"], r["Dispatch_Id"])
+                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    by_kernel = {}
+    for (name, _), v in vals.items():
+        by_kernel.setdefault(name, []).append(v)
+    return by_kernel
+
+
+def summarize_traffic(fetch_dir, write_dir, calib_mib, out_path):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the past-block kernel,
+    each scaled by what the same counter reads for the calibration copy."""
+    calib_kib = calib_mib * 1024.0
+    res = {"kernel": "moba::attn_past_kernel", "workload": "gqa32x8_1m",
+           "kernel_source_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
+           "commands": [PMC_CMD.format(counter="FETCH_SIZE"), PMC_CMD.format(counter="WRITE_SIZE")],
+           "calibration": {"kernel": "torch.neg (elementwise copy)", "bytes_read": calib_kib * 1024,
+                           "bytes_written": calib_kib * 1024}}
+    total = 0.0
+    for counter, d, field in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
+        per = _per_dispatch(d, counter)
+        cal = [v for name, vs in per.items() if COPY_KERNEL_TAG in name for v in vs]
+        past = [v for name, vs in per.items() if "attn_past_kernel" in name for v in vs]
+        if not cal or not past:
+            raise RuntimeError(f"{counter}: calibration or past-kernel dispatches missing in {d}")
+        cal_kib = sum(cal) / len(cal)
+        factor = calib_kib / cal_kib
+        kib = sum(past) / len(past)
+        res["calibration"][f"{counter}_kib"] = cal_kib
+        res["calibration"][f"{field}_factor"] = factor
+        res[f"{field}_kib_per_launch_raw"] = kib
+        res[f"{field}_bytes_per_launch"] = kib * factor * 1024
+        res["launches"] = len(past)
+        total += kib * factor * 1024
+    res["hbm_bytes_per_launch"] = total
+    with open(out_path, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    return res
+
+
+def summarize_trace(trace_dir, bench_json, out_path):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of bench.py,
+    with bench.py's own HIP-event average for the past-block kernel."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = list(csv.DictReader(open(f)))
+    line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    rf = line["roofline"]
+    out = ["# Kernel trace: MoBA forward, gqa32x8_1m workload (1M tokens, 32/8 heads, D 128, block 4096, top-12)",
+           "", "Command (run from the repository root on one MI355X):", "", "```", TRACE_CMD, "```", "",
+           f"{line['warmup'] + line['steps']} forward calls ({line['warmup']} warm-up + {line['steps']} timed); "
+           f"{rf['launches_per_step']:.0f} query chunks per call.", "",
+           "| Kernel | Calls | Total ns | Average ns | % | Min ns | Max ns |", "|---|---|---|---|---|---|---|"]
+    for r in rows[:12]:
+        name = r["Name"] if len(r["Name"]) < 72 else r["Name"][:69] + "..."
+        out.append(f"| {name} | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.0f} | "
+                   f"{float(r['Percentage']):.2f} | {r['MinNs']} | {r['MaxNs']} |")
+    past = [r for r in rows if "attn_past_kernel" in r["Name"]][0]
+    out += ["", f"bench.py in the same run, HIP events around each attn_past_kernel launch on its stream: "
+                f"average {rf['avg_launch_ms']:.2f} ms per launch (rocprofv3: {float(past['AverageNs']) / 1e6:.2f} ms); "
+                f"{rf['achieved']:.1f} TFLOP/s = {100 * rf['frac']:.1f}% of the {rf['peak']:.0f} TFLOP/s bf16 peak.",
+            f"Step: {line['ms_per_step']:.1f} ms, {line['value']:.1f} useful TFLOP/s."]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
 
 
 def main():
@@ -185,7 +300,19 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run a plain copy of MIB MiB first (reference dispatch for HBM byte counters)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from two rocprofv3 --pmc runs, then exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="write the kernel-trace summary from a rocprofv3 --stats run, then exit")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        print(json.dumps(summarize_traffic(*args.summarize_traffic, 1024, TRAFFIC_FILE), indent=1))
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, os.path.join(ROOT, "profiles", "kernel_trace_gqa32x8_1m.md"))
+        return
 
     def log(msg):
         if not args.quiet:
@@ -205,6 +332,8 @@ def main():
         sys.exit(1)
 
     w = W.WORKLOADS[args.workload]
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, log)
     res, inputs, stages = measure(M, W, w, args.steps, args.warmup, log)
     line = {
         "metric": METRIC,
