@@ -38,7 +38,7 @@ SIGNATURES = {
                                          ctypes.POINTER(ctypes.c_double), _c_i32]),
 }
 
-STAGES = ("meanpool", "gate", "dispatch", "attn_past", "attn_own", "attn_f32")
+STAGES = ("meanpool", "gate", "dispatch", "attn_past", "attn_own", "attn_f32", "kv_layout")
 
 
 class MobaError(RuntimeError):

@@ -280,8 +280,7 @@ __device__ __forceinline__ void softmax_p(f32x16* s, WaveRows& R, float c, int l
 }
 
 // O^T[d][q] += sum_key V^T[d][key] P^T[key][q] for one slice.
-__device__ __forceinline__ void pv(const bf16raw* buf, const uint32_t (*pk)[8], WaveRows& R, const VtOffsets& vo) {
-  const char* vtb = reinterpret_cast<const char*>(buf + KS_ELEMS);
+__device__ __forceinline__ void pv_vt(const char* vtb, const uint32_t (*pk)[8], WaveRows& R, const VtOffsets& vo) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -295,6 +294,10 @@ __device__ __forceinline__ void pv(const bf16raw* buf, const uint32_t (*pk)[8], 
         R.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, R.o[b], 0, 0, 0);
       }
     }
+}
+
+__device__ __forceinline__ void pv(const bf16raw* buf, const uint32_t (*pk)[8], WaveRows& R, const VtOffsets& vo) {
+  pv_vt(reinterpret_cast<const char*>(buf + KS_ELEMS), pk, R, vo);
 }
 
 template <bool kMasked, typename Mask>
@@ -439,6 +442,226 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+// ---------------------------------------------------------------------------
+// Image path (block a whole number of 64-key slices).
+//
+// K and V are first re-laid out once per call into per-slice images: slice
+// c of KV head hk is a 16 KiB K image and a 16 KiB V^T image, each exactly
+// the LDS layout the MFMA operand reads want, stored contiguously.  Staging
+// a slice is then a plain 16-byte copy per thread (no transposition on the
+// way), and the operand reads need no per-read address arithmetic.
+//
+// Both images are unit-major: 16-byte unit u of row r sits at slot
+// u * rows + r.  An operand read (32 lanes on 32 consecutive rows, same
+// unit) then touches 16 consecutive slots per 16 lanes, i.e. all 64 banks
+// once, and a lane's reads differ only by immediate offsets.
+//   K image:   unit u = 8 consecutive d (u = 0..15) of key row r (0..63):
+//              slot u * 64 + r.
+//   V^T image: unit U = 4 kb + 2 hs + lg (0..7) of d row (0..127): slot
+//              U * 128 + d, holding V[key][d] for the 8 keys
+//              32 kb + 16 hs + 8 (e >> 2) + 4 lg + (e & 3), e = 0..7 (the
+//              order in which P^T leaves the score accumulators).
+// ---------------------------------------------------------------------------
+constexpr int IMG_BYTES = KT * HD * 2;         // one K or V^T slice image, 16 KiB
+constexpr int SLICE_BYTES = 2 * IMG_BYTES;     // K image + V^T image
+
+__global__ __launch_bounds__(256) void kv_image_kernel(const bf16raw* __restrict__ k, const bf16raw* __restrict__ v,
+                                                       int64_t seqlen, int hkv, uint16_t* __restrict__ kimg,
+                                                       uint16_t* __restrict__ vimg) {
+  __shared__ __attribute__((aligned(16))) bf16raw kt[KT * KS_STRIDE];
+  __shared__ __attribute__((aligned(16))) bf16raw vt[KT * KS_STRIDE];
+  const int64_t sl = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int64_t bb = blockIdx.z;
+  const int64_t rs = (int64_t)hkv * HD;
+  const int64_t src = (bb * seqlen + sl * KT) * rs + hk * HD;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int u = threadIdx.x + 256 * x;  // 64 keys x 16 units of 8 d
+    const int key = u >> 4, dc = u & 15;
+    *reinterpret_cast<u32x4*>(kt + key * KS_STRIDE + dc * 8) = *reinterpret_cast<const u32x4*>(k + src + key * rs + dc * 8);
+    *reinterpret_cast<u32x4*>(vt + key * KS_STRIDE + dc * 8) = *reinterpret_cast<const u32x4*>(v + src + key * rs + dc * 8);
+  }
+  __syncthreads();
+  const int64_t img = ((bb * hkv + hk) * (seqlen / KT) + sl) * (KT * HD);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int slot = threadIdx.x + 256 * x;
+    // K image: slot = unit * 64 + key row
+    const int kr = slot & 63, ku = slot >> 6;
+    *reinterpret_cast<u32x4*>(kimg + img + slot * 8) = *reinterpret_cast<const u32x4*>(kt + kr * KS_STRIDE + ku * 8);
+    // V^T image: slot = U * 128 + d
+    const int d = slot & 127, U = slot >> 7;
+    const int kbase = 32 * (U >> 2) + 16 * ((U >> 1) & 1) + 4 * (U & 1);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int k0 = kbase + 8 * (e >> 2) + (e & 3);
+      w[e >> 1] = (uint32_t)vt[k0 * KS_STRIDE + d] | ((uint32_t)vt[(k0 + 1) * KS_STRIDE + d] << 16);
+    }
+    *reinterpret_cast<u32x4*>(vimg + img + slot * 8) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// O^T += V^T P^T for one slice from a V^T image; vb = this lane's base
+// (lg * 2048 + (lane & 31) * 16 bytes), everything else immediate.
+__device__ __forceinline__ void pv_img(const char* vb, const uint32_t (*pk)[8], WaveRows& R) {
+  bf16x8 va[16];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    const int kb = x >> 3, hs = (x >> 2) & 1, b = x & 3;
+    va[x] = *reinterpret_cast<const bf16x8*>(vb + (4 * kb + 2 * hs) * 2048 + b * 512);
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      const u32x4 pw = {pk[kb][4 * hs], pk[kb][4 * hs + 1], pk[kb][4 * hs + 2], pk[kb][4 * hs + 3]};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        R.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[8 * kb + 4 * hs + b], pb, R.o[b], 0, 0, 0);
+    }
+}
+
+// S^T = K Q^T for one slice from a K image; kb = this lane's base
+// (lg * 1024 + (lane & 31) * 16 bytes).
+__device__ __forceinline__ void qk_img(const char* kb, const bf16x8* qb, f32x16* s) {
+  bf16x8 ka[8], kc[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    ka[st] = *reinterpret_cast<const bf16x8*>(kb + st * 2048);
+    kc[st] = *reinterpret_cast<const bf16x8*>(kb + st * 2048 + 512);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) { s[0][e] = 0.f; s[1][e] = 0.f; }
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qb[st], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[st], qb[st], s[1], 0, 0, 0);
+  }
+}
+
+// Registers that carry one slice of the K and V^T images from HBM to LDS:
+// each thread moves 16-byte units tid + NT x of both 16 KiB images, loaded
+// and stored at the same offset (the images already are the LDS layout).
+template <int NW>
+struct ImgStager {
+  static constexpr int NT = NW * 64;
+  static constexpr int NU = 1024 / NT;  // units per image per thread
+  u32x4 kr[NU], vr[NU];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vs) {
+#pragma unroll
+    for (int x = 0; x < NU; ++x) {
+      const int u = (int)threadIdx.x + NT * x;
+      kr[x] = *reinterpret_cast<const u32x4*>(ks + u * 8);
+      vr[x] = *reinterpret_cast<const u32x4*>(vs + u * 8);
+    }
+  }
+  __device__ __forceinline__ void store(char* buf) const {
+#pragma unroll
+    for (int x = 0; x < NU; ++x) {
+      const int u = (int)threadIdx.x + NT * x;
+      *reinterpret_cast<u32x4*>(buf + u * 16) = kr[x];
+      *reinterpret_cast<u32x4*>(buf + IMG_BYTES + u * 16) = vr[x];
+    }
+  }
+};
+
+// Past-block tiles of 256 rows over a block that is a whole number of
+// slices, from the K and V^T images.  8 waves (two per SIMD) run in step:
+// per slice the scores, the softmax and P V, one barrier per slice; the
+// loads of slice s+2 are issued at the start of slice s into one of two
+// register sets and written to LDS (double-buffered) at the end of slice
+// s+1, so each load has two slice iterations to arrive.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_past_img_kernel(PastArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * SLICE_BYTES];
+  constexpr int ROWS = NW * 32;
+  const int32_t total = a.tiles[0];
+  const int32_t per_xcd = (total + 7) >> 3;
+  const int32_t loc = blockIdx.x >> 3;
+  if (loc >= per_xcd) return;
+  const int32_t tile = (int32_t)(blockIdx.x & 7) * per_xcd + loc;
+  if (tile >= total) return;
+  const int32_t L = a.tiles[8 + 2 * tile];
+  const int32_t start = a.tiles[9 + 2 * tile];
+  const int32_t end = a.listoff[L] + a.count[L];
+  const int32_t cnt = (end - start) < ROWS ? (end - start) : ROWS;
+  const int hk = (int)(L / a.n);
+  const int64_t blk = L % a.n;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  WaveRows R;
+  const int r = wave * 32 + (lane & 31);
+  const bool valid = r < cnt;
+  const int32_t entry = a.entries[start + (valid ? r : 0)];
+  {
+    const int64_t local_row = entry / a.kp;
+    const int64_t pic = local_row / a.hq;
+    const int h = (int)(local_row % a.hq);
+    const int64_t t = a.t0 + pic;
+    load_q(reinterpret_cast<const bf16raw*>(a.q) + ((a.bb * a.seqlen + t) * a.hq + h) * HD, lane, R.qb);
+  }
+  rows_init(R);
+
+  const int nsl = a.block / KT;
+  const int64_t img0 = (((int64_t)a.bb * a.hkv + hk) * (a.seqlen / KT) + blk * nsl) * (KT * HD);
+  const uint16_t* kimg = a.kimg + img0;
+  const uint16_t* vimg = a.vimg + img0;
+  const int lg = lane >> 5;
+  const int kofs = lg * 1024 + (lane & 31) * 16;
+  const int vofs = lg * 2048 + (lane & 31) * 16;
+  // past the last slice the loads repeat it, so every iteration issues the same loads
+  auto src = [&](int sl) { return (int64_t)(sl < nsl ? sl : nsl - 1) * (KT * HD); };
+  const float c = a.scale_log2;
+
+  ImgStager<NW> st, st2;
+  st.load(kimg, vimg);
+  st.store(smem);
+  // the query rows and slice 0 must be in before the prefetch loads go out:
+  // a wait for them inside the loop would also wait for the younger loads
+  drain_vmem();
+  st2.load(kimg + src(1), vimg + src(1));
+  __syncthreads();
+  auto slice = [&](const char* buf) {
+    f32x16 sc[2];
+    uint32_t pk[2][8];
+    qk_img(buf + kofs, R.qb, sc);
+    softmax_p<false>(sc, R, c, lane, NoMask{}, pk);
+    pv_img(buf + IMG_BYTES + vofs, pk, R);
+  };
+  for (int sl = 0; sl < nsl; sl += 2) {
+    // slice sl in buffer 0; slice sl+1 in flight in st2
+    st.load(kimg + src(sl + 2), vimg + src(sl + 2));
+    slice(smem);
+    if (sl + 1 < nsl) st2.store(smem + SLICE_BYTES);
+    __syncthreads();
+    if (sl + 1 >= nsl) break;
+    // slice sl+1 in buffer 1; slice sl+2 in flight in st
+    st2.load(kimg + src(sl + 3), vimg + src(sl + 3));
+    slice(smem + SLICE_BYTES);
+    if (sl + 2 < nsl) st.store(smem);
+    __syncthreads();
+  }
+  drain_vmem();
+
+  const float ltot = pair_sum(R.l);
+  if (valid) {
+    const float inv = 1.f / ltot;
+    bf16raw* dst = a.part_o + (int64_t)entry * HD;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x2 w2 = {pack_bf16x2(R.o[b][4 * q4] * inv, R.o[b][4 * q4 + 1] * inv),
+                          pack_bf16x2(R.o[b][4 * q4 + 2] * inv, R.o[b][4 * q4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(dst + b * 32 + 8 * q4 + lg * 4) = w2;
+      }
+    if (lg == 0) a.part_lse[entry] = R.m + fast_log2(ltot);
+  }
+}
+
 constexpr int OWN_NW = 8;  // own-block tiles: 8 waves x 32 rows
 
 __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
@@ -558,7 +781,9 @@ int launch_attn_past(const PastArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.max_tiles);
   if (a.tile_rows == 256) {
     // 8 waves, one work-group per CU: loads two slices ahead when every slice is full
-    if (a.block % KT == 0)
+    if (a.block % KT == 0 && a.kimg)
+      hipLaunchKernelGGL((attn_past_img_kernel<8>), grid, dim3(512), 0, st, a);
+    else if (a.block % KT == 0)
       hipLaunchKernelGGL((attn_past_kernel<8, true>), grid, dim3(512), 0, st, a);
     else
       hipLaunchKernelGGL((attn_past_kernel<8, false>), grid, dim3(512), 0, st, a);
@@ -566,6 +791,13 @@ int launch_attn_past(const PastArgs& a, hipStream_t st) {
     // 4 waves, two independent work-groups per CU
     hipLaunchKernelGGL((attn_past_kernel<4, false>), grid, dim3(256), 0, st, a);
   }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_kv_image(const void* k, const void* v, int64_t batch, int64_t seqlen, int hkv, uint16_t* kimg,
+                    uint16_t* vimg, hipStream_t st) {
+  hipLaunchKernelGGL(kv_image_kernel, dim3((unsigned)(seqlen / KT), (unsigned)hkv, (unsigned)batch), dim3(256), 0, st,
+                     reinterpret_cast<const bf16raw*>(k), reinterpret_cast<const bf16raw*>(v), seqlen, hkv, kimg, vimg);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -180,6 +180,13 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
     if (launch_meanpool(k, dtype, batch, seqlen, num_kv_heads, head_dim, block_size, mu, s)) return MOBA_ERR_HIP;
   }
 
+  uint16_t* kimg = p.kv_image ? reinterpret_cast<uint16_t*>(ws + p.off_kimg) : nullptr;
+  uint16_t* vimg = p.kv_image ? reinterpret_cast<uint16_t*>(ws + p.off_vimg) : nullptr;
+  if (kimg) {
+    StageScope sc(MOBA_STAGE_KVLAYOUT, s, 4.0 * (double)batch * seqlen * num_kv_heads * D * elt);
+    if (launch_kv_image(k, v, batch, seqlen, num_kv_heads, kimg, vimg, s)) return MOBA_ERR_HIP;
+  }
+
   // 2.. per query chunk: gate, dispatch, past blocks, own block + merge
   for (int64_t bb = 0; bb < batch; ++bb) {
     for (int64_t jc = 0; jc < p.n; jc += p.chunk_blocks) {
@@ -244,7 +251,7 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
         pa.entries = entries; pa.part_o = part_o; pa.part_lse = part_lse; pa.seqlen = seqlen; pa.n = p.n;
         pa.t0 = t0; pa.hq = num_q_heads; pa.hkv = num_kv_heads; pa.block = block_size; pa.kp = p.kp;
         pa.g = p.g; pa.bb = (int32_t)bb; pa.max_tiles = (int32_t)p.max_tiles; pa.tile_rows = p.tile_rows;
-        pa.scale_log2 = sl2;
+        pa.scale_log2 = sl2; pa.kimg = kimg; pa.vimg = vimg;
         {
           StageScope sc(MOBA_STAGE_PAST, s, 4.0 * D * past_rows * block_size);
           if (launch_attn_past(pa, s)) return MOBA_ERR_HIP;

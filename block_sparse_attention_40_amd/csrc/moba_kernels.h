@@ -44,6 +44,8 @@ struct PastArgs {
   const int32_t* entries;
   uint16_t* part_o;      // [pairs, D] normalised partial output, bf16
   float* part_lse;       // [pairs] log2-domain log-sum-exp of the scaled logits
+  const uint16_t* kimg;  // K slice images [batch, hkv, seqlen / 64, 64 x 128], or null
+  const uint16_t* vimg;  // V^T slice images, same shape
   int64_t seqlen, n, t0;
   int32_t hq, hkv, block, kp, g, bb, max_tiles, tile_rows;
   float scale_log2;      // log2(e) / sqrt(D)
@@ -75,6 +77,10 @@ struct F32Args {
   int32_t hq, hkv, d, block, topk, causal, g, bb;
   float scale_log2;
 };
+
+// K and V^T images of all 64-key slices (bf16 path, seqlen % 64 == 0).
+int launch_kv_image(const void* k, const void* v, int64_t batch, int64_t seqlen, int hkv, uint16_t* kimg,
+                    uint16_t* vimg, hipStream_t stream);
 
 int launch_meanpool(const void* k, int dtype, int64_t batch, int64_t seqlen, int hkv, int d, int block,
                     float* mu, hipStream_t stream);

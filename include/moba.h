@@ -81,7 +81,9 @@ const char* moba_status_string(int status);
  * moba_workspace_bytes: the size of the device workspace moba_attn_fwd needs
  * for these shapes (block means, per-block row lists, tile list and the
  * per-(row, past block) partial results, sized for the query chunk the
- * library processes at a time).  Pure host arithmetic; touches no device.
+ * library processes at a time; for bf16 with long per-block row lists also
+ * a copy of K and V re-laid out per 64-key slice, as large as K and V).
+ * Pure host arithmetic; touches no device.
  * Returns a status; on MOBA_OK *bytes holds the size.
  */
 int moba_workspace_bytes(int64_t batch, int64_t seqlen, int32_t num_q_heads,
@@ -143,7 +145,8 @@ enum moba_stage {
   MOBA_STAGE_PAST = 3,      /* attention over non-own blocks: FLOPs */
   MOBA_STAGE_OWN = 4,       /* own block + merge: FLOPs */
   MOBA_STAGE_F32 = 5,       /* fp32 attention path: FLOPs */
-  MOBA_NUM_STAGES = 6
+  MOBA_STAGE_KVLAYOUT = 6,  /* K and V re-laid out as per-slice LDS images: bytes */
+  MOBA_NUM_STAGES = 7
 };
 int moba_profile_enable(int on);
 int moba_profile_read(double* ms, int64_t* launches, double* work, int32_t n);
