@@ -191,6 +191,38 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
 }
 
+// A partial o (one (row, past block) pair, 128 bf16) is stored in the order
+// the O^T accumulators hold it: lane half lg owns d = 32 b + 8 q4 + 4 lg + i
+// (b, q4, i = 0..3) at position 64 lg + 16 b + 4 q4 + i, so each lane writes
+// and reads 128 contiguous bytes.  The layout is private to the two
+// attention kernels.
+__device__ __forceinline__ void store_partial(bf16raw* dst, const f32x16* o, float inv, int lg) {
+  u32x4* p = reinterpret_cast<u32x4*>(dst + 64 * lg);
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 8 * h;  // accumulator elements of q4 = 2h, 2h + 1
+      p[2 * b + h] = u32x4{pack_bf16x2(o[b][e] * inv, o[b][e + 1] * inv), pack_bf16x2(o[b][e + 2] * inv, o[b][e + 3] * inv),
+                           pack_bf16x2(o[b][e + 4] * inv, o[b][e + 5] * inv), pack_bf16x2(o[b][e + 6] * inv, o[b][e + 7] * inv)};
+    }
+}
+__device__ __forceinline__ void add_partial(const bf16raw* src, float w, f32x16* o, int lg) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(src + 64 * lg);
+  u32x4 v[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) v[x] = p[x];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[b][8 * h + 2 * j] += w * bf16lo(v[2 * b + h][j]);
+        o[b][8 * h + 2 * j + 1] += w * bf16hi(v[2 * b + h][j]);
+      }
+}
+
 // Byte offsets of this lane's V^T operand units.  Row d = 32 b + lr holds
 // unit (4 kb + 2 hs + lg) at position unit ^ vt_swz(d), and
 // vt_swz(32 b + lr) = vt_swz(lr) ^ (4 (b & 1)); so the position is
@@ -428,16 +460,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   if (valid) {
     // the normalised partial is a convex combination of value rows, so bf16
     // keeps it to 2^-9 of the largest |v|
-    const float inv = 1.f / ltot;
-    bf16raw* dst = a.part_o + (int64_t)entry * HD;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x2 w2 = {pack_bf16x2(R.o[b][4 * q4] * inv, R.o[b][4 * q4 + 1] * inv),
-                          pack_bf16x2(R.o[b][4 * q4 + 2] * inv, R.o[b][4 * q4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(dst + b * 32 + 8 * q4 + lg * 4) = w2;
-      }
+    store_partial(a.part_o + (int64_t)entry * HD, R.o, 1.f / ltot, lg);
     if (lg == 0) a.part_lse[entry] = R.m + fast_log2(ltot);
   }
 }
@@ -648,24 +671,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const float ltot = pair_sum(R.l);
   if (valid) {
-    const float inv = 1.f / ltot;
-    bf16raw* dst = a.part_o + (int64_t)entry * HD;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x2 w2 = {pack_bf16x2(R.o[b][4 * q4] * inv, R.o[b][4 * q4 + 1] * inv),
-                          pack_bf16x2(R.o[b][4 * q4 + 2] * inv, R.o[b][4 * q4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(dst + b * 32 + 8 * q4 + lg * 4) = w2;
-      }
+    store_partial(a.part_o + (int64_t)entry * HD, R.o, 1.f / ltot, lg);
     if (lg == 0) a.part_lse[entry] = R.m + fast_log2(ltot);
   }
 }
 
 constexpr int OWN_NW = 8;  // own-block tiles: 8 waves x 32 rows
 
+// One 64-key slice from a K / V^T image slice in LDS.
+template <bool kMasked, typename Mask>
+__device__ __forceinline__ void attend_slice_img(const char* buf, WaveRows& R, float c, int lane, int kofs, int vofs,
+                                                 Mask masked) {
+  f32x16 sc[2];
+  uint32_t pk[2][8];
+  qk_img(buf + kofs, R.qb, sc);
+  softmax_p<kMasked>(sc, R, c, lane, masked, pk);
+  pv_img(buf + IMG_BYTES + vofs, pk, R);
+}
+
+// Own block of each query (causal up to the query itself) plus the merge
+// of the row's partials.  kImg: K and V come from the slice images (block a
+// whole number of slices); otherwise from K and V directly.
+template <bool kImg>
 __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16raw smem[2 * BUF_ELEMS];
+  __shared__ __attribute__((aligned(16))) char smem[kImg ? 2 * SLICE_BYTES : 2 * BUF_ELEMS * 2];
   const int64_t tiles_per_block = (a.block + a.own_t - 1) / a.own_t;
   const int64_t jl = blockIdx.x / tiles_per_block;               // block inside the chunk
   const int64_t p0 = (blockIdx.x % tiles_per_block) * a.own_t;   // first position inside the block
@@ -674,6 +703,7 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
   const int G = a.g;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lg = lane >> 5;
   WaveRows R;
   const int rr = wave * 32 + (lane & 31);
   const int64_t pp = p0 + rr / G;
@@ -685,61 +715,87 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
     load_q(reinterpret_cast<const bf16raw*>(a.q) + ((a.bb * a.seqlen + t) * a.hq + h) * HD, lane, R.qb);
   }
   rows_init(R);
-  VtOffsets vo;
-  vo.init(lane);
-
-  const int64_t rs = (int64_t)a.hkv * HD;
-  const bf16raw* kbase = reinterpret_cast<const bf16raw*>(a.k) + (a.bb * a.seqlen) * rs + hk * HD;
-  const bf16raw* vbase = reinterpret_cast<const bf16raw*>(a.v) + (a.bb * a.seqlen) * rs + hk * HD;
 
   if (a.causal) {
     const int64_t last = (p0 + a.own_t < a.block ? p0 + a.own_t : a.block);  // keys [0, last) of the block
-    const int64_t kb0 = j * a.block;
     const int nsl = (int)((last + KT - 1) / KT);
     // last position any row of this wave holds: later slices are invisible to it
     int64_t wmax = p0 + (wave * 32 + 31) / G;
     if (wmax > a.block - 1) wmax = a.block - 1;
     // slices wholly before the tile's first query need no mask
     const int nfree = (int)(p0 / KT);
-    const int rsi = (int)rs;
-    const bf16raw* kblk = kbase + kb0 * rs;
-    const bf16raw* vblk = vbase + kb0 * rs;
-    KVStager<OWN_NW> st;
-    auto fetch = [&](int sl) {
-      const int64_t off = (int64_t)sl * KT * rs;
-      if ((sl + 1) * KT <= last)
-        st.template load<false>(kblk + off, vblk + off, rsi, KT);
-      else
-        st.template load<true>(kblk + off, vblk + off, rsi, (int)(last - sl * KT));
-    };
-    fetch(0);
-    st.store(smem);
-    __syncthreads();
-    for (int sl = 0; sl < nfree; ++sl) {
-      if (sl + 1 < nsl) fetch(sl + 1);
-      attend_slice<false>(smem + (sl & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, NoMask{});
-      if (sl + 1 < nsl) st.store(smem + ((sl + 1) & 1) * BUF_ELEMS);
+    const float c = a.scale_log2;
+    if constexpr (kImg) {
+      // keys past `last` in the last slice exist (the block is whole
+      // slices) and are masked like every key after the query
+      const int64_t img0 = (((int64_t)a.bb * a.hkv + hk) * (a.seqlen / KT) + j * (a.block / KT)) * (KT * HD);
+      const uint16_t* kimg = a.kimg + img0;
+      const uint16_t* vimg = a.vimg + img0;
+      const int kofs = lg * 1024 + (lane & 31) * 16;
+      const int vofs = lg * 2048 + (lane & 31) * 16;
+      ImgStager<OWN_NW> st;
+      auto bufp = [&](int sl) { return smem + (sl & 1) * SLICE_BYTES; };
+      st.load(kimg, vimg);
+      st.store(bufp(0));
       __syncthreads();
-    }
-    for (int sl = nfree; sl < nsl; ++sl) {
-      const int64_t k0 = (int64_t)sl * KT;
-      if (sl + 1 < nsl) fetch(sl + 1);
-      if (k0 <= wmax)
-        attend_slice<true>(smem + (sl & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, CausalMask{(int)(pos - k0)});
-      if (sl + 1 < nsl) st.store(smem + ((sl + 1) & 1) * BUF_ELEMS);
+      for (int sl = 0; sl < nfree; ++sl) {
+        if (sl + 1 < nsl) st.load(kimg + (int64_t)(sl + 1) * (KT * HD), vimg + (int64_t)(sl + 1) * (KT * HD));
+        attend_slice_img<false>(bufp(sl), R, c, lane, kofs, vofs, NoMask{});
+        if (sl + 1 < nsl) st.store(bufp(sl + 1));
+        __syncthreads();
+      }
+      for (int sl = nfree; sl < nsl; ++sl) {
+        const int64_t k0 = (int64_t)sl * KT;
+        if (sl + 1 < nsl) st.load(kimg + (int64_t)(sl + 1) * (KT * HD), vimg + (int64_t)(sl + 1) * (KT * HD));
+        if (k0 <= wmax) attend_slice_img<true>(bufp(sl), R, c, lane, kofs, vofs, CausalMask{(int)(pos - k0)});
+        if (sl + 1 < nsl) st.store(bufp(sl + 1));
+        __syncthreads();
+      }
+    } else {
+      bf16raw* sb = reinterpret_cast<bf16raw*>(smem);
+      VtOffsets vo;
+      vo.init(lane);
+      const int64_t rs = (int64_t)a.hkv * HD;
+      const int rsi = (int)rs;
+      const bf16raw* kblk = reinterpret_cast<const bf16raw*>(a.k) + (a.bb * a.seqlen + j * a.block) * rs + hk * HD;
+      const bf16raw* vblk = reinterpret_cast<const bf16raw*>(a.v) + (a.bb * a.seqlen + j * a.block) * rs + hk * HD;
+      KVStager<OWN_NW> st;
+      auto fetch = [&](int sl) {
+        const int64_t off = (int64_t)sl * KT * rs;
+        if ((sl + 1) * KT <= last)
+          st.template load<false>(kblk + off, vblk + off, rsi, KT);
+        else
+          st.template load<true>(kblk + off, vblk + off, rsi, (int)(last - sl * KT));
+      };
+      fetch(0);
+      st.store(sb);
       __syncthreads();
+      for (int sl = 0; sl < nfree; ++sl) {
+        if (sl + 1 < nsl) fetch(sl + 1);
+        attend_slice<false>(sb + (sl & 1) * BUF_ELEMS, R, vo, c, lane, NoMask{});
+        if (sl + 1 < nsl) st.store(sb + ((sl + 1) & 1) * BUF_ELEMS);
+        __syncthreads();
+      }
+      for (int sl = nfree; sl < nsl; ++sl) {
+        const int64_t k0 = (int64_t)sl * KT;
+        if (sl + 1 < nsl) fetch(sl + 1);
+        if (k0 <= wmax) attend_slice<true>(sb + (sl & 1) * BUF_ELEMS, R, vo, c, lane, CausalMask{(int)(pos - k0)});
+        if (sl + 1 < nsl) st.store(sb + ((sl + 1) & 1) * BUF_ELEMS);
+        __syncthreads();
+      }
     }
   }
 
   // merge this row's partials (log-sum-exp rule), normalise, store bf16
-  const int lg = lane >> 5;
   const int64_t nslot = a.causal ? (j < a.kp ? j : a.kp) : a.kp;
   const float l_own = pair_sum(R.l);
   const int64_t local_row = (j * a.block + pos - a.t0) * a.hq + h;
+  const float* lse = a.part_lse + local_row * a.kp;
+  const bf16raw* po = reinterpret_cast<const bf16raw*>(a.part_o) + local_row * a.kp * HD;
   // an own block with no visible key (non-causal mode) carries no weight
   const float m_own = (l_own > 0.f) ? R.m : -__builtin_inff();
   float M = m_own;
-  for (int64_t s = 0; s < nslot; ++s) M = __builtin_fmaxf(M, a.part_lse[local_row * a.kp + s]);
+  for (int64_t s = 0; s < nslot; ++s) M = __builtin_fmaxf(M, lse[s]);
   const float c_own = (l_own > 0.f) ? fast_exp2(m_own - M) : 0.f;
   float Lsum = l_own * c_own;
 #pragma unroll
@@ -747,20 +803,9 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) R.o[b][e] *= c_own;
   for (int64_t s = 0; s < nslot; ++s) {
-    const int64_t p = local_row * a.kp + s;
-    const float w = fast_exp2(a.part_lse[p] - M);
+    const float w = fast_exp2(lse[s] - M);
     Lsum += w;
-    const bf16raw* src = a.part_o + p * HD;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x2 o2 = *reinterpret_cast<const u32x2*>(src + b * 32 + 8 * q4 + lg * 4);
-        R.o[b][4 * q4] += w * bf16lo(o2[0]);
-        R.o[b][4 * q4 + 1] += w * bf16hi(o2[0]);
-        R.o[b][4 * q4 + 2] += w * bf16lo(o2[1]);
-        R.o[b][4 * q4 + 3] += w * bf16hi(o2[1]);
-      }
+    add_partial(po + s * HD, w, R.o, lg);
   }
   if (valid) {
     const float inv = 1.f / Lsum;
@@ -804,8 +849,11 @@ int launch_kv_image(const void* k, const void* v, int64_t batch, int64_t seqlen,
 int launch_attn_own(const OwnArgs& a, hipStream_t st) {
   const int64_t tiles_per_block = (a.block + a.own_t - 1) / a.own_t;
   const int64_t nblk = a.cnt / a.block;
-  hipLaunchKernelGGL(attn_own_kernel, dim3((unsigned)(nblk * tiles_per_block), (unsigned)a.hkv),
-                     dim3(OWN_NW * 64), 0, st, a);
+  const dim3 grid((unsigned)(nblk * tiles_per_block), (unsigned)a.hkv);
+  if (a.kimg && a.block % KT == 0)
+    hipLaunchKernelGGL(attn_own_kernel<true>, grid, dim3(OWN_NW * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_own_kernel<false>, grid, dim3(OWN_NW * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

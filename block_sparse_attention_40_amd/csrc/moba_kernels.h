@@ -59,6 +59,8 @@ struct OwnArgs {
   void* out;
   const uint16_t* part_o;  // [pairs, D] bf16
   const float* part_lse;
+  const uint16_t* kimg;    // K / V^T slice images, or null
+  const uint16_t* vimg;
   int64_t seqlen, n, t0, cnt;
   int32_t hq, hkv, block, kp, g, own_t, bb, causal;
   float scale_log2;
