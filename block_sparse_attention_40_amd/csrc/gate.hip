@@ -14,6 +14,7 @@
 // chose each block (used to build the per-block row lists).
 #include "moba_device.h"
 #include "moba_kernels.h"
+#include "moba_plan.h"
 
 namespace moba {
 
@@ -140,6 +141,227 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path: scores on the matrix cores.
+//
+// Each fp32 block mean is split into three bf16 parts hi + mid + lo that add
+// up to it exactly (hi = bf16(mu), mid = bf16(mu - hi), lo = mu - hi - mid,
+// each step exact in fp32).  With bf16 queries every product q_d * part_d is
+// exact in fp32, so <q, mu> = sum over the three parts of the MFMA dot
+// products, accumulated in fp32: the same fp32 rounding model as the plain
+// dot product over 3 D terms.
+//
+// Split means are stored per tile of 32 blocks as the LDS operand image
+// [part][16-byte unit u of 8 d][block] (unit-major, so the 32 lanes that read
+// 32 blocks of one unit hit every bank once), 24 KiB per tile.
+// ---------------------------------------------------------------------------
+constexpr int kMu3TileElems = 3 * 16 * kGateTile * 8;  // bf16 per tile image
+
+__global__ __launch_bounds__(256) void mu_split_kernel(const float* __restrict__ mu, int64_t n, int hkv,
+                                                       uint16_t* __restrict__ mu3) {
+  const int64_t tile = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int64_t bb = blockIdx.z;
+  const int64_t ntile = (n + kGateTile - 1) / kGateTile;
+  const float* src = mu + (bb * hkv + hk) * n * 128;
+  uint16_t* dst = mu3 + ((bb * hkv + hk) * ntile + tile) * kMu3TileElems;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int pair = threadIdx.x + 256 * x;  // (unit, block) of the tile
+    const int u = pair >> 5, blk = pair & 31;
+    const int64_t i = tile * kGateTile + blk;
+    float v[8];
+    if (i < n) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src + i * 128 + u * 8);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + i * 128 + u * 8 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    uint32_t w[3][4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t h2 = pack_bf16x2(v[e], v[e + 1]);
+      const float r0 = v[e] - bf16lo(h2), r1 = v[e + 1] - bf16hi(h2);
+      const uint32_t m2 = pack_bf16x2(r0, r1);
+      const uint32_t l2 = pack_bf16x2(r0 - bf16lo(m2), r1 - bf16hi(m2));
+      w[0][e >> 1] = h2;
+      w[1][e >> 1] = m2;
+      w[2][e >> 1] = l2;
+    }
+#pragma unroll
+    for (int part = 0; part < 3; ++part)
+      *reinterpret_cast<u32x4*>(dst + ((part * 16 + u) * kGateTile + blk) * 8) =
+          u32x4{w[part][0], w[part][1], w[part][2], w[part][3]};
+  }
+}
+
+// Insert a 64-bit key into a descending top list (ks[0] largest).
+template <int KCAP>
+__device__ __forceinline__ void topk_insert(uint64_t* ks, uint64_t key) {
+  if (key > ks[KCAP - 1]) {
+    ks[KCAP - 1] = key;
+#pragma unroll
+    for (int p = KCAP - 1; p > 0; --p) {
+      const uint64_t lo = ks[p], hi = ks[p - 1];
+      const bool sw = lo > hi;
+      ks[p] = sw ? hi : lo;
+      ks[p - 1] = sw ? lo : hi;
+    }
+  }
+}
+
+// One work-group = 256 rows (gate_t positions x the group's heads of one KV
+// head), 8 waves of 32 rows.  Per tile of 32 blocks a wave computes the
+// 32 x 32 score tile S^T = Mu Q^T (24 MFMAs: 3 parts x 8 steps of 16 d);
+// lane l then holds 16 of the 32 scores of row l % 32 (the other 16 are in
+// lane l ^ 32) and keeps its own top list; at the end the two lists of a
+// row are merged.
+template <int KCAP>
+__global__ __launch_bounds__(512) void gate_mfma_kernel(GateArgs a, const uint16_t* __restrict__ mu3) {
+  extern __shared__ __attribute__((aligned(16))) char gsm[];
+  char* tbuf = gsm;                                          // 2 tile images
+  int* lhist = reinterpret_cast<int*>(gsm + 2 * kMu3TileElems * 2);  // [n]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 5;
+  const int64_t w = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int64_t n = a.n;
+  const int g = a.g;
+
+  if (a.hist)
+    for (int64_t i = tid; i < n; i += 512) lhist[i] = 0;
+
+  const int r = wave * 32 + (lane & 31);
+  const int64_t pic = w * a.gate_t + r / g;  // position inside the chunk
+  const int h = hk * g + r % g;
+  const bool valid = r < a.gate_t * g && pic < a.cnt;
+  const int64_t t = a.t0 + (valid ? pic : 0);
+  const int64_t j = t / a.block;
+  const int64_t ncand = a.causal ? j : n;
+  const int m = (int)(a.causal ? (j < a.kp ? j : a.kp) : a.kp);
+  const bool rank = valid && m > 0 && (int64_t)m < ncand;
+
+  const int64_t last_pic = (w * a.gate_t + a.gate_t < a.cnt ? w * a.gate_t + a.gate_t : a.cnt) - 1;
+  const int64_t wg_cand = a.causal ? (a.t0 + last_pic) / a.block : n;
+  const int64_t ntile = (n + kGateTile - 1) / kGateTile;
+  const int64_t wg_tiles = (wg_cand + kGateTile - 1) / kGateTile;
+
+  uint64_t ks[KCAP];
+#pragma unroll
+  for (int p = 0; p < KCAP; ++p) ks[p] = (p < KCAP - m) ? ~0ull : 0ull;
+
+  const int any_rank = __syncthreads_or(rank ? 1 : 0);
+  if (any_rank) {
+    bf16x8 qb[8];
+    {
+      const bf16raw* qp = reinterpret_cast<const bf16raw*>(a.q) + ((a.bb * a.seqlen + t) * a.hq + h) * 128;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qp + lg * 8 + 16 * s);
+    }
+    const uint16_t* mt = mu3 + ((int64_t)a.bb * a.hkv + hk) * ntile * kMu3TileElems;
+    const int aofs = (lg * 32 + (lane & 31)) * 16;  // this lane's A-operand unit (part 0, step 0)
+    u32x4 stg[3];
+    auto load_tile = [&](int64_t c) {
+#pragma unroll
+      for (int x = 0; x < 3; ++x) stg[x] = *reinterpret_cast<const u32x4*>(mt + c * kMu3TileElems + (tid + 512 * x) * 8);
+    };
+    auto store_tile = [&](char* dst) {
+#pragma unroll
+      for (int x = 0; x < 3; ++x) *reinterpret_cast<u32x4*>(dst + (tid + 512 * x) * 16) = stg[x];
+    };
+    load_tile(0);
+    store_tile(tbuf);
+    __syncthreads();
+    for (int64_t c = 0; c < wg_tiles; ++c) {
+      char* cur = tbuf + (c & 1) * (kMu3TileElems * 2);
+      if (c + 1 < wg_tiles) load_tile(c + 1);
+      // the MFMAs run on the whole wave (wave-uniform branch); only the
+      // insertions depend on the row
+      if (__any(rank && c * kGateTile < ncand)) {
+        f32x16 s0, s1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+#pragma unroll
+        for (int part = 0; part < 3; ++part)
+#pragma unroll
+          for (int st = 0; st < 8; st += 2) {
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(cur + aofs + (part * 16 + 2 * st) * 512);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(cur + aofs + (part * 16 + 2 * st + 2) * 512);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[st], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[st + 1], s1, 0, 0, 0);
+          }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t i = c * kGateTile + 8 * (e >> 2) + 4 * lg + (e & 3);
+          float sc = s0[e] + s1[e];
+          if (sc != sc) sc = -__builtin_inff();  // NaN ranks lowest
+          const uint64_t key = ((uint64_t)orderable(sc) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
+          if (rank && i < ncand) topk_insert<KCAP>(ks, key);
+        }
+      }
+      if (c + 1 < wg_tiles) store_tile(tbuf + ((c + 1) & 1) * (kMu3TileElems * 2));
+      __syncthreads();
+    }
+    // merge the two half-row lists: each lane takes a copy of its partner's
+    // list (lane l ^ 32), then inserts the partner's kept keys into its own
+    uint64_t pk_[KCAP];
+#pragma unroll
+    for (int p = 0; p < KCAP; ++p) {
+      const uint32_t klo = (uint32_t)ks[p], khi = (uint32_t)(ks[p] >> 32);
+      const auto xl = __builtin_amdgcn_permlane32_swap(klo, klo, false, false);
+      const auto xh = __builtin_amdgcn_permlane32_swap(khi, khi, false, false);
+      const uint32_t l0 = xl[0], l1 = xl[1], h0 = xh[0], h1 = xh[1];
+      pk_[p] = lg ? (((uint64_t)h0 << 32) | l0) : (((uint64_t)h1 << 32) | l1);
+    }
+#pragma unroll
+    for (int p = 0; p < KCAP; ++p)
+      if (rank && p >= KCAP - m) topk_insert<KCAP>(ks, pk_[p]);
+  }
+
+  if (valid && lg == 0) {
+    int32_t* row = a.sel + (int64_t)h * a.sel_stride_h + (t - a.sel_pos_base) * a.topk;
+    int c = 0;
+    if (rank) {
+      // the m kept blocks sit in ks[KCAP-m .. KCAP-1]; emit them ascending
+      uint32_t idx[KCAP];
+#pragma unroll
+      for (int p = 0; p < KCAP; ++p)
+        idx[p] = (p >= KCAP - m) ? (0xffffffffu - (uint32_t)ks[p]) : 0xffffffffu;
+#pragma unroll
+      for (int pass = 0; pass < KCAP; ++pass) {
+#pragma unroll
+        for (int p = pass & 1; p + 1 < KCAP; p += 2) {
+          const uint32_t x = idx[p], y = idx[p + 1];
+          idx[p] = x < y ? x : y;
+          idx[p + 1] = x < y ? y : x;
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < KCAP; ++p) {
+        if (p < m) {
+          row[c++] = (int32_t)idx[p];
+          if (a.hist) atomicAdd(&lhist[idx[p]], 1);
+        }
+      }
+    } else if ((int64_t)m >= ncand) {
+      for (int64_t i = 0; i < ncand; ++i) {
+        row[c++] = (int32_t)i;
+        if (a.hist) atomicAdd(&lhist[i], 1);
+      }
+    }
+    if (a.causal) row[c++] = (int32_t)j;  // the own block, always kept
+    for (; c < a.topk; ++c) row[c] = -1;
+  }
+
+  if (a.hist) {
+    __syncthreads();
+    int32_t* dst = a.hist + ((int64_t)hk * a.gate_wg + w) * n;
+    for (int64_t i = tid; i < n; i += 512) dst[i] = lhist[i];
+  }
+}
+
 template <typename T, int D>
 static void launch_gate_kcap(const GateArgs& a, int kcap, size_t shmem, hipStream_t st, dim3 grid) {
   if (kcap <= 4)
@@ -150,8 +372,25 @@ static void launch_gate_kcap(const GateArgs& a, int kcap, size_t shmem, hipStrea
     hipLaunchKernelGGL((gate_kernel<T, D, 32>), grid, dim3(256), shmem, st, a);
 }
 
+int launch_mu_split(const float* mu, int64_t batch, int64_t n, int hkv, uint16_t* mu3, hipStream_t st) {
+  hipLaunchKernelGGL(mu_split_kernel, dim3((unsigned)((n + kGateTile - 1) / kGateTile), (unsigned)hkv, (unsigned)batch),
+                     dim3(256), 0, st, mu, n, hkv, mu3);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_gate(const GateArgs& a, int dtype, int d, hipStream_t st) {
   dim3 grid((unsigned)a.gate_wg, (unsigned)a.hkv);
+  if (dtype == 1 && a.mu3 && a.gate_t * a.g <= 256) {
+    const size_t sh = (size_t)2 * kMu3TileElems * 2 + (a.hist ? (size_t)a.n * sizeof(int) : 0);
+    const int kc = a.kp < 1 ? 1 : a.kp;
+    if (kc <= 4)
+      hipLaunchKernelGGL(gate_mfma_kernel<4>, grid, dim3(512), sh, st, a, a.mu3);
+    else if (kc <= 16)
+      hipLaunchKernelGGL(gate_mfma_kernel<16>, grid, dim3(512), sh, st, a, a.mu3);
+    else
+      hipLaunchKernelGGL(gate_mfma_kernel<32>, grid, dim3(512), sh, st, a, a.mu3);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const size_t shmem = (size_t)kMuSlice * d * sizeof(float) + (a.hist ? (size_t)a.n * sizeof(int) : 0);
   const int kcap = a.kp < 1 ? 1 : a.kp;
   if (dtype == 1) {

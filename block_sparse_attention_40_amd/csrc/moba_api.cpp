@@ -179,6 +179,13 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
                   (double)batch * seqlen * num_kv_heads * D * elt + (double)batch * num_kv_heads * p.n * D * 4.0);
     if (launch_meanpool(k, dtype, batch, seqlen, num_kv_heads, head_dim, block_size, mu, s)) return MOBA_ERR_HIP;
   }
+  // bf16 gate: the means split into three bf16 parts for the score MFMAs
+  uint16_t* mu3 = nullptr;
+  if (bf16 && p.selective) {
+    mu3 = reinterpret_cast<uint16_t*>(ws + p.off_mu3);
+    StageScope sc(MOBA_STAGE_MEANPOOL, s, (double)batch * num_kv_heads * p.n * D * (4.0 + 6.0));
+    if (launch_mu_split(mu, batch, p.n, num_kv_heads, mu3, s)) return MOBA_ERR_HIP;
+  }
 
   uint16_t* kimg = p.kv_image ? reinterpret_cast<uint16_t*>(ws + p.off_kimg) : nullptr;
   uint16_t* vimg = p.kv_image ? reinterpret_cast<uint16_t*>(ws + p.off_vimg) : nullptr;
@@ -207,7 +214,7 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
       const bool need_lists = bf16 && p.kp > 0;
 
       GateArgs ga{};
-      ga.q = q; ga.mu = mu; ga.sel = sel_base; ga.sel_stride_h = sel_stride_h; ga.sel_pos_base = sel_pos_base;
+      ga.q = q; ga.mu = mu; ga.mu3 = mu3; ga.sel = sel_base; ga.sel_stride_h = sel_stride_h; ga.sel_pos_base = sel_pos_base;
       ga.hist = need_lists ? hist : nullptr;
       ga.seqlen = seqlen; ga.n = p.n; ga.t0 = t0; ga.cnt = cnt; ga.gate_wg = gate_wg;
       ga.hq = num_q_heads; ga.hkv = num_kv_heads; ga.block = block_size; ga.topk = topk; ga.kp = p.kp;

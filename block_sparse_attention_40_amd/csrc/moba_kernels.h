@@ -10,6 +10,7 @@ namespace moba {
 struct GateArgs {
   const void* q;
   const float* mu;       // [batch, hkv, n, D]
+  const uint16_t* mu3;   // split means as MFMA tile images (bf16 path), or null
   int32_t* sel;          // row (h, t) at sel + h * sel_stride_h + (t - sel_pos_base) * topk
   int64_t sel_stride_h;
   int64_t sel_pos_base;
@@ -87,6 +88,8 @@ int launch_kv_image(const void* k, const void* v, int64_t batch, int64_t seqlen,
 int launch_meanpool(const void* k, int dtype, int64_t batch, int64_t seqlen, int hkv, int d, int block,
                     float* mu, hipStream_t stream);
 int launch_gate(const GateArgs& a, int dtype, int d, hipStream_t stream);
+// Block means split into three bf16 parts, as the gate's MFMA tile images.
+int launch_mu_split(const float* mu, int64_t batch, int64_t n, int hkv, uint16_t* mu3, hipStream_t stream);
 int launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 int launch_attn_past(const PastArgs& a, hipStream_t stream);
 int launch_attn_own(const OwnArgs& a, hipStream_t stream);

@@ -77,6 +77,11 @@ int make_plan(const Shape& s, Plan* p) {
   const size_t img = q.kv_image ? (size_t)s.batch * s.hkv * s.seqlen * s.d * sizeof(uint16_t) : 0;
   q.off_kimg = take(img);
   q.off_vimg = take(img);
+  // bf16 gate: block means split into three bf16 parts, per tile of 32 blocks
+  const size_t mu3 = s.dtype == MOBA_DTYPE_BF16 && q.selective
+                         ? (size_t)s.batch * s.hkv * ((q.n + kGateTile - 1) / kGateTile) * kGateTile * 3 * s.d * 2
+                         : 0;
+  q.off_mu3 = take(mu3);
   q.total = off;
   *p = q;
   return MOBA_OK;

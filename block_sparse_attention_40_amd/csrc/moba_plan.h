@@ -19,6 +19,8 @@ constexpr int64_t kLargeTileMinRows = 2048;
 constexpr int kOwnRows = 256;
 // Largest query-head group (num_q_heads / num_kv_heads) the tiles support.
 constexpr int kMaxGroup = 128;
+// Blocks per tile of the bf16 gate's score MFMAs.
+constexpr int kGateTile = 32;
 // Keys per K / V^T image slice (the attention kernels' LDS slice).
 constexpr int kSliceKeys = 64;
 // Upper bound on the partial-result buffer of one query chunk (bf16 o + fp32 lse).
@@ -46,7 +48,7 @@ struct Plan {
   bool kv_image;        // K and V are re-laid out per 64-key slice for direct LDS loads (bf16, block % 64 == 0)
   // workspace layout (byte offsets, 256-aligned)
   size_t off_mu, off_sel, off_hist, off_count, off_listoff, off_tiles, off_entries;
-  size_t off_part_o, off_part_lse, off_kimg, off_vimg, total;
+  size_t off_part_o, off_part_lse, off_kimg, off_vimg, off_mu3, total;
 };
 
 // Validate `s` and fill `p`.  Returns a moba_status code.
