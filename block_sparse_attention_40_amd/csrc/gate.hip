@@ -385,6 +385,10 @@ int launch_gate(const GateArgs& a, int dtype, int d, hipStream_t st) {
     const int kc = a.kp < 1 ? 1 : a.kp;
     if (kc <= 4)
       hipLaunchKernelGGL(gate_mfma_kernel<4>, grid, dim3(512), sh, st, a, a.mu3);
+    else if (kc <= 8)
+      hipLaunchKernelGGL(gate_mfma_kernel<8>, grid, dim3(512), sh, st, a, a.mu3);
+    else if (kc <= 12)
+      hipLaunchKernelGGL(gate_mfma_kernel<12>, grid, dim3(512), sh, st, a, a.mu3);
     else if (kc <= 16)
       hipLaunchKernelGGL(gate_mfma_kernel<16>, grid, dim3(512), sh, st, a, a.mu3);
     else
