@@ -27,6 +27,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (datasheet)
 METRIC = "MoBA prefill fwd useful TFLOP/s + tokens/s at 32K and 1M; MFMA util %"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_past_gqa32x8_1m.json")
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_40_amd", "csrc", "attn_bf16.hip")
+# the past-block attention kernel the 1M workload runs (256-row tiles fed from the K/V slice images)
+PAST_KERNEL = "moba::attn_past_img_kernel<8>"
+PAST_TAG = "attn_past"
 
 
 def useful_flops(w) -> float:
@@ -111,7 +114,7 @@ def roofline(stages, steps):
         src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
         if rec.get("kernel_source_sha256") == src_hash:
             traffic = rec.get("hbm_bytes_per_launch")
-    return {"kernel": "attn_past_kernel", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+    return {"kernel": PAST_KERNEL, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
             "avg_launch_ms": avg_ms, "launches_per_step": past["launches"] / steps,
             "flops_per_launch": flops_per_launch}
@@ -234,7 +237,7 @@ def summarize_traffic(fetch_dir, write_dir, calib_mib, out_path):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the past-block kernel,
     each scaled by what the same counter reads for the calibration copy."""
     calib_kib = calib_mib * 1024.0
-    res = {"kernel": "moba::attn_past_kernel", "workload": "gqa32x8_1m",
+    res = {"kernel": PAST_KERNEL, "workload": "gqa32x8_1m",
            "kernel_source_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
            "commands": [PMC_CMD.format(counter="FETCH_SIZE"), PMC_CMD.format(counter="WRITE_SIZE")],
            "calibration": {"kernel": "torch.neg (elementwise copy)", "bytes_read": calib_kib * 1024,
@@ -243,7 +246,7 @@ def summarize_traffic(fetch_dir, write_dir, calib_mib, out_path):
     for counter, d, field in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
         per = _per_dispatch(d, counter)
         cal = [v for name, vs in per.items() if COPY_KERNEL_TAG in name for v in vs]
-        past = [v for name, vs in per.items() if "attn_past_kernel" in name for v in vs]
+        past = [v for name, vs in per.items() if PAST_TAG in name for v in vs]
         if not cal or not past:
             raise RuntimeError(f"{counter}: calibration or past-kernel dispatches missing in {d}")
         cal_kib = sum(cal) / len(cal)
@@ -280,8 +283,8 @@ def summarize_trace(trace_dir, bench_json, out_path):
         name = r["Name"] if len(r["Name"]) < 72 else r["Name"][:69] + "..."
         out.append(f"| {name} | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.0f} | "
                    f"{float(r['Percentage']):.2f} | {r['MinNs']} | {r['MaxNs']} |")
-    past = [r for r in rows if "attn_past_kernel" in r["Name"]][0]
-    out += ["", f"bench.py in the same run, HIP events around each attn_past_kernel launch on its stream: "
+    past = [r for r in rows if PAST_TAG in r["Name"]][0]
+    out += ["", f"bench.py in the same run, HIP events around each {PAST_KERNEL} launch on its stream: "
                 f"average {rf['avg_launch_ms']:.2f} ms per launch (rocprofv3: {float(past['AverageNs']) / 1e6:.2f} ms); "
                 f"{rf['achieved']:.1f} TFLOP/s = {100 * rf['frac']:.1f}% of the {rf['peak']:.0f} TFLOP/s bf16 peak.",
             f"Step: {line['ms_per_step']:.1f} ms, {line['value']:.1f} useful TFLOP/s."]
