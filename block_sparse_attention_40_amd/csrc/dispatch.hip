@@ -5,8 +5,9 @@
 // For one query chunk, list (hk, i) collects every (row, slot) whose row is
 // served by KV head hk and chose block i as a non-own block.  Three steps,
 // all on the device (no host round trip):
-//   1. list_scan:  per list, exclusive prefix over the gate work-groups of
-//                  their per-block counts (gate writes the counts);
+//   1. list_scan:  per list (one work-group each), exclusive prefix over the
+//                  gate work-groups of their counts for that list (the gate
+//                  writes them contiguous per list);
 //   2. tile_plan:  one work-group scans the list sizes into list offsets and
 //                  cuts every list into tiles of tile_rows rows;
 //   3. scatter:    every row writes its (row, slot) entries into its lists at
@@ -18,29 +19,6 @@
 #include "moba_plan.h"
 
 namespace moba {
-
-__global__ __launch_bounds__(256) void list_scan_kernel(int32_t* __restrict__ hist, int32_t* __restrict__ count,
-                                                        int64_t n, int64_t gate_wg, int64_t lists) {
-  const int64_t L = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (L >= lists) return;
-  const int64_t hk = L / n, i = L % n;
-  int32_t* col = hist + hk * gate_wg * n + i;
-  int32_t run = 0;
-  int64_t w = 0;
-  for (; w + 4 <= gate_wg; w += 4) {
-    const int32_t c0 = col[(w + 0) * n], c1 = col[(w + 1) * n], c2 = col[(w + 2) * n], c3 = col[(w + 3) * n];
-    col[(w + 0) * n] = run; run += c0;
-    col[(w + 1) * n] = run; run += c1;
-    col[(w + 2) * n] = run; run += c2;
-    col[(w + 3) * n] = run; run += c3;
-  }
-  for (; w < gate_wg; ++w) {
-    const int32_t c = col[w * n];
-    col[w * n] = run;
-    run += c;
-  }
-  count[L] = run;
-}
 
 // Exclusive block scan of 1024 values in LDS (Hillis-Steele).
 __device__ __forceinline__ int32_t block_excl_scan_1024(int32_t x, int32_t* buf, int32_t* total) {
@@ -57,6 +35,25 @@ __device__ __forceinline__ int32_t block_excl_scan_1024(int32_t x, int32_t* buf,
   *total = buf[1023];
   __syncthreads();
   return incl - x;
+}
+
+// One work-group per list: exclusive prefix over the gate work-groups of
+// their counts for this list (contiguous), in place; the total goes to count.
+__global__ __launch_bounds__(1024) void list_scan_kernel(int32_t* __restrict__ hist, int32_t* __restrict__ count,
+                                                         int64_t gate_wg) {
+  __shared__ int32_t buf[1024];
+  const int64_t L = blockIdx.x;
+  int32_t* col = hist + L * gate_wg;
+  int32_t carry = 0;
+  for (int64_t base = 0; base < gate_wg; base += 1024) {
+    const int64_t w = base + threadIdx.x;
+    const int32_t c = w < gate_wg ? col[w] : 0;
+    int32_t tot;
+    const int32_t ex = block_excl_scan_1024(c, buf, &tot);
+    if (w < gate_wg) col[w] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) count[L] = carry;
 }
 
 __global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restrict__ count,
@@ -105,7 +102,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(DispatchArgs a) {
   const int64_t t = a.t0 + pic;
   const int64_t j = t / a.block;
   const int32_t* row = a.sel + (int64_t)h * a.sel_stride_h + (t - a.sel_pos_base) * a.topk;
-  const int32_t* wstart = a.hist + ((int64_t)hk * a.gate_wg + w) * n;
+  const int32_t* wstart = a.hist + (int64_t)hk * n * a.gate_wg + w;  // list i: wstart[i * gate_wg]
   const int64_t local_row = pic * a.hq + h;
   int slot = 0;
   for (int c = 0; c < a.topk && slot < a.kp; ++c) {
@@ -114,15 +111,14 @@ __global__ __launch_bounds__(256) void scatter_kernel(DispatchArgs a) {
     if (a.causal && i == j) continue;  // own block: handled by the own-block kernel
     const int32_t r = atomicAdd(&lcnt[i], 1);
     const int64_t L = (int64_t)hk * n + i;
-    a.entries[a.listoff[L] + wstart[i] + r] = (int32_t)(local_row * a.kp + slot);
+    a.entries[a.listoff[L] + wstart[(int64_t)i * a.gate_wg] + r] = (int32_t)(local_row * a.kp + slot);
     ++slot;
   }
 }
 
 int launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   const int64_t lists = (int64_t)a.hkv * a.n;
-  hipLaunchKernelGGL(list_scan_kernel, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, st, a.hist, a.count,
-                     a.n, a.gate_wg, lists);
+  hipLaunchKernelGGL(list_scan_kernel, dim3((unsigned)lists), dim3(1024), 0, st, a.hist, a.count, a.gate_wg);
   hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, st, a.count, a.listoff, a.tiles, lists,
                      a.tile_rows);
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)a.gate_wg, (unsigned)a.hkv), dim3(256),

@@ -11,7 +11,8 @@
 // index, which is exactly the tie rule.
 //
 // Besides sel_idx the kernel writes, per work-group, how many of its rows
-// chose each block (used to build the per-block row lists).
+// chose each block (used to build the per-block row lists), stored as
+// [KV head, block, work-group] so that each list's counts are contiguous.
 #include "moba_device.h"
 #include "moba_kernels.h"
 #include "moba_plan.h"
@@ -136,8 +137,8 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
 
   if (a.hist) {
     __syncthreads();
-    int32_t* dst = a.hist + ((int64_t)hk * a.gate_wg + w) * n;
-    for (int64_t i = tid; i < n; i += 256) dst[i] = lhist[i];
+    int32_t* dst = a.hist + (int64_t)hk * n * a.gate_wg + w;  // [hkv, n, gate_wg]
+    for (int64_t i = tid; i < n; i += 256) dst[i * a.gate_wg] = lhist[i];
   }
 }
 
@@ -357,8 +358,8 @@ __global__ __launch_bounds__(512) void gate_mfma_kernel(GateArgs a, const uint16
 
   if (a.hist) {
     __syncthreads();
-    int32_t* dst = a.hist + ((int64_t)hk * a.gate_wg + w) * n;
-    for (int64_t i = tid; i < n; i += 512) dst[i] = lhist[i];
+    int32_t* dst = a.hist + (int64_t)hk * n * a.gate_wg + w;  // [hkv, n, gate_wg]
+    for (int64_t i = tid; i < n; i += 512) dst[i * a.gate_wg] = lhist[i];
   }
 }
 

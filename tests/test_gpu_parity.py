@@ -108,6 +108,13 @@ SMALL = [
     small("b16_tiny_blocks", "bf16", 1, 512, 2, 2, 128, 16, 4),
     small("b2048_long", "bf16", 1, 8192, 4, 1, 128, 2048, 2),
     small("single_block", "bf16", 1, 256, 2, 2, 128, 256, 3),
+    # bf16 gate on MFMA: several 32-block score tiles with a ragged last one,
+    # and each top-k list capacity (kept past blocks 8, 11, 15, 19)
+    small("gate_n50_k9", "bf16", 1, 2400, 4, 2, 128, 48, 9),
+    small("gate_n96_k12", "bf16", 1, 6144, 4, 1, 128, 64, 12),
+    small("gate_n64_k16", "bf16", 1, 4096, 4, 1, 128, 64, 16),
+    small("gate_n64_k20", "bf16", 1, 4096, 2, 2, 128, 64, 20),
+    small("gate_noncausal_n40", "bf16", 1, 2560, 2, 1, 128, 64, 6, causal=False),
     small("f32_d128_gqa", "f32", 1, 1024, 4, 2, 128, 128, 3),
     small("f32_noncausal", "f32", 1, 512, 2, 1, 64, 64, 3, causal=False),
 ]
