@@ -167,6 +167,13 @@ def test_workload_tiny_f32_1k_both_topk():
     run(w.with_(topk=8))
 
 
+def test_forward_batch2_slice_images_sampled():
+    """Long per-block row lists at batch 2: 256-row tiles fed from the K/V
+    slice images, whose offsets depend on the batch entry."""
+    w = small("gqa_b2_images", "bf16", 2, 8192, 32, 8, 128, 256, 8, seed=23)
+    run(w, rows=W.sample_rows(w, 48, seed=24), device_inputs=True)
+
+
 def test_workload_mha16_8k_sampled():
     w = W.WORKLOADS["mha16_8k"]
     run(w, rows=W.sample_rows(w, 256, seed=21), device_inputs=True)
