@@ -292,6 +292,53 @@ def summarize_trace(trace_dir, bench_json, out_path):
         fh.write("\n".join(out) + "\n")
 
 
+def curve(M, W, lengths, log, budget_s=4.0):
+    """Speedup of MoBA over dense causal attention, both from this library
+    (report §4.5: the attention layer forward only, MoBA with the block count
+    and top-k fixed, n = 256 blocks and top-12, so the block size grows with
+    the sequence; dense = block_size = seqlen, topk = 1: one causal block).
+    One JSON line per length; steps adapt to about budget_s of GPU time."""
+    import torch
+    out_lines = []
+    for S in lengths:
+        res = {"seqlen": S}
+        for tag, w in (("moba", W.Workload(f"gqa32x8_{S}_moba", "bf16", 1, 32, 8, S, 128, S // 256, 12, seed=1100)),
+                       ("dense", W.Workload(f"gqa32x8_{S}_dense", "bf16", 1, 32, 8, S, 128, S, 1, seed=1100))):
+            q, k, v, _ = W.make_inputs(w, device="cuda")
+            out = torch.empty_like(q)
+            nbytes = M.workspace_bytes(1, S, 32, 8, 128, M.DTYPE_BF16, w.block_size, w.topk, True)
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            call = lambda: M.moba_attn_fwd(q, k, v, w.block_size, w.topk, True, out=out, workspace=ws,
+                                           return_sel=False)
+            call()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            call()
+            torch.cuda.synchronize()
+            one = time.perf_counter() - t0
+            steps = max(1, min(20, int(budget_s / max(one, 1e-6))))
+            M.profile_read()
+            M.profile_enable(True)
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                call()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) / steps * 1e3
+            M.profile_enable(False)
+            st = M.profile_read()
+            fl = useful_flops(w)
+            res[tag] = {"block_size": w.block_size, "topk": w.topk, "ms": ms, "steps": steps,
+                        "useful_tflops": fl / (ms * 1e-3) / 1e12,
+                        "stages_ms": {n: x["ms"] / steps for n, x in st.items() if x["launches"]}}
+            log(f"[curve] S={S} {tag}: {ms:.3f} ms ({steps} steps)")
+            del q, k, v, out, ws
+            torch.cuda.empty_cache()
+        res["speedup"] = res["dense"]["ms"] / res["moba"]["ms"]
+        print(json.dumps(res), flush=True)
+        out_lines.append(res)
+    return out_lines
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -305,6 +352,8 @@ def main():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain copy of MIB MiB first (reference dispatch for HBM byte counters)")
+    ap.add_argument("--curve", nargs="*", type=int, metavar="SEQLEN",
+                    help="MoBA (256 blocks, top-12) vs dense causal attention at these lengths, one JSON line each")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc runs, then exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
@@ -334,6 +383,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.curve is not None:
+        curve(M, W, args.curve or [32768, 65536, 131072, 262144, 524288, 1048576], log)
+        return
     w = W.WORKLOADS[args.workload]
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, log)

@@ -697,7 +697,9 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kImg ? 2 * SLICE_BYTES : 2 * BUF_ELEMS * 2];
   const int64_t tiles_per_block = (a.block + a.own_t - 1) / a.own_t;
   const int64_t jl = blockIdx.x / tiles_per_block;               // block inside the chunk
-  const int64_t p0 = (blockIdx.x % tiles_per_block) * a.own_t;   // first position inside the block
+  // the tiles of a block launch last position first: the longest causal
+  // ranges start earliest, so the grid does not end on them
+  const int64_t p0 = (tiles_per_block - 1 - blockIdx.x % tiles_per_block) * a.own_t;  // first position
   const int hk = blockIdx.y;
   const int64_t j = a.t0 / a.block + jl;
   const int G = a.g;

@@ -71,9 +71,12 @@ int make_plan(const Shape& s, Plan* p) {
   q.off_entries = take((size_t)std::max<int64_t>(q.max_pairs, 1) * sizeof(int32_t));
   q.off_part_o = take((size_t)std::max<int64_t>(q.max_pairs, 1) * s.d * sizeof(uint16_t));
   q.off_part_lse = take((size_t)std::max<int64_t>(q.max_pairs, 1) * sizeof(float));
-  // K and V^T slice images for the 256-row direct-load tiles:
+  // K and V^T slice images for the 256-row past-block tiles:
   // [batch, hkv, seqlen / 64, 64 x 128] bf16 each, as large as K and V
-  q.kv_image = s.dtype == MOBA_DTYPE_BF16 && s.block % kSliceKeys == 0 && q.kp > 0 && q.tile_rows == kTileRowsLarge;
+  // (and for the own-block kernel alone when no past block is chosen and the
+  // blocks are long, e.g. block_size = seqlen: dense causal attention)
+  q.kv_image = s.dtype == MOBA_DTYPE_BF16 && s.block % kSliceKeys == 0 &&
+               (q.kp > 0 ? q.tile_rows == kTileRowsLarge : s.block >= kOwnImageMinBlock);
   const size_t img = q.kv_image ? (size_t)s.batch * s.hkv * s.seqlen * s.d * sizeof(uint16_t) : 0;
   q.off_kimg = take(img);
   q.off_vimg = take(img);

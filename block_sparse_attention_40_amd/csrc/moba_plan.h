@@ -21,6 +21,9 @@ constexpr int kOwnRows = 256;
 constexpr int kMaxGroup = 128;
 // Blocks per tile of the bf16 gate's score MFMAs.
 constexpr int kGateTile = 32;
+// Block size from which the own-block kernel alone (no past blocks) reads
+// K and V through the slice images.
+constexpr int64_t kOwnImageMinBlock = 1024;
 // Keys per K / V^T image slice (the attention kernels' LDS slice).
 constexpr int kSliceKeys = 64;
 // Upper bound on the partial-result buffer of one query chunk (bf16 o + fp32 lse).

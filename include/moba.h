@@ -81,8 +81,9 @@ const char* moba_status_string(int status);
  * moba_workspace_bytes: the size of the device workspace moba_attn_fwd needs
  * for these shapes (block means, per-block row lists, tile list and the
  * per-(row, past block) partial results, sized for the query chunk the
- * library processes at a time; for bf16 with long per-block row lists also
- * a copy of K and V re-laid out per 64-key slice, as large as K and V).
+ * library processes at a time; for bf16 with long per-block row lists, or
+ * with no past block and blocks of at least 1024 keys, also a copy of K and
+ * V re-laid out per 64-key slice, as large as K and V).
  * Pure host arithmetic; touches no device.
  * Returns a status; on MOBA_OK *bytes holds the size.
  */

@@ -174,6 +174,20 @@ def test_forward_batch2_slice_images_sampled():
     run(w, rows=W.sample_rows(w, 48, seed=24), device_inputs=True)
 
 
+def test_forward_dense_one_block_sampled():
+    """block_size = seqlen, topk = 1: dense causal attention through the own-block
+    kernel alone (fed from the slice images); the dense baseline of the speedup curve."""
+    w = small("dense_one_block", "bf16", 1, 16384, 8, 2, 128, 16384, 1, seed=25)
+    run(w, rows=W.sample_rows(w, 48, seed=26), device_inputs=True)
+
+
+def test_forward_curve_config_32k_sampled():
+    """The speedup curve's MoBA configuration at its shortest length: 256 blocks
+    of 128, top-12, GQA 32/8."""
+    w = small("curve_32k", "bf16", 1, 32768, 32, 8, 128, 128, 12, seed=27)
+    run(w, rows=W.sample_rows(w, 24, seed=28), device_inputs=True)
+
+
 def test_workload_mha16_8k_sampled():
     w = W.WORKLOADS["mha16_8k"]
     run(w, rows=W.sample_rows(w, 256, seed=21), device_inputs=True)
