@@ -41,6 +41,14 @@ Readings where the pages leave a step open (each listed in the design notes):
     and routes with its own q (course exercise: per-head routing).
   * non-causal mode (causal = False): no future mask, no forced block, plain
     top-k over all n blocks, no mask inside blocks.
+
+Gate variant (report §1.3 and §5: Quest is placed in the family as MoBA with
+small blocks and min/max pooling of the block's keys):
+  * gate = "minmax": block i is summarised by the element-wise minimum lo_i
+    and maximum hi_i of its keys; its score is the largest value q.k can take
+    for any k inside that box, sum_d max(q_d lo_id, q_d hi_id).  This is the
+    plainest score that uses both summaries; it bounds every q.k_s of the
+    block from above.  Causal rules, forced block and top-k are unchanged.
 """
 from __future__ import annotations
 
@@ -77,12 +85,35 @@ def block_means(k: np.ndarray, block_size: int) -> np.ndarray:
     return mu
 
 
+def block_minmax(k: np.ndarray, block_size: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Element-wise minimum and maximum of each block's keys (the min/max
+    pooling of the Quest-style gate, report §1.3): lo, hi [batch, Hkv, n, D]
+    fp64 (exact: they are input values)."""
+    b, S, Hkv, D = k.shape
+    n = num_blocks(S, block_size)
+    lo = np.empty((b, Hkv, n, D), dtype=np.float64)
+    hi = np.empty((b, Hkv, n, D), dtype=np.float64)
+    for bb in range(b):
+        for i in range(n):
+            blk = np.asarray(k[bb, i * block_size:(i + 1) * block_size], dtype=np.float64)  # [B, Hkv, D]
+            lo[bb, :, i, :] = blk.min(axis=0)
+            hi[bb, :, i, :] = blk.max(axis=0)
+    return lo, hi
+
+
 # ----------------------------------------------------------------------------
 # Step 3 and 4: gate scores, causal rules, top-k (report §2.2, §2.3)
 # ----------------------------------------------------------------------------
 def gate_scores(q_row: np.ndarray, mu_head: np.ndarray) -> np.ndarray:
     """s_i = <q, mu_i> for every block i  (report §2.2).  mu_head: [n, D]."""
     return mu_head @ np.asarray(q_row, dtype=np.float64)
+
+
+def gate_scores_minmax(q_row: np.ndarray, lo_head: np.ndarray, hi_head: np.ndarray) -> np.ndarray:
+    """s_i = sum_d max(q_d lo_id, q_d hi_id): the largest q.k over the box
+    [lo_i, hi_i] (the Quest-style gate's score).  lo_head, hi_head: [n, D]."""
+    q64 = np.asarray(q_row, dtype=np.float64)
+    return np.maximum(lo_head * q64, hi_head * q64).sum(axis=1)
 
 
 def select_blocks(scores: np.ndarray, j: int, topk: int, causal: bool) -> List[int]:
@@ -181,14 +212,14 @@ def _check_shapes(q, k, v, block_size, topk):
 
 
 def moba_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_size: int,
-                 topk: int, causal: bool = True) -> Tuple[np.ndarray, np.ndarray]:
+                 topk: int, causal: bool = True, gate: str = "mean") -> Tuple[np.ndarray, np.ndarray]:
     """Full MoBA forward on small inputs.
 
     Returns out [batch, S, Hq, D] fp64 and sel_idx [batch, Hq, S, topk] int32
     (chosen blocks ascending, padded with -1)."""
     b, S, Hq, Hkv, D = _check_shapes(q, k, v, block_size, topk)
     rows = [(bb, t, h) for bb in range(b) for h in range(Hq) for t in range(S)]
-    res = moba_rows(q, k, v, block_size, topk, causal, rows)
+    res = moba_rows(q, k, v, block_size, topk, causal, rows, gate=gate)
     out = np.zeros((b, S, Hq, D), dtype=np.float64)
     sel_idx = np.full((b, Hq, S, topk), -1, dtype=np.int32)
     for r, (bb, t, h) in enumerate(rows):
@@ -214,10 +245,13 @@ class RowResult:
 def moba_rows(q, k, v, block_size: int, topk: int, causal: bool,
               rows: Sequence[Tuple[int, int, int]], mu: Optional[np.ndarray] = None,
               given_sel: Optional[Sequence[Sequence[int]]] = None,
-              keep_scores: bool = False) -> RowResult:
+              keep_scores: bool = False, gate: str = "mean",
+              minmax: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> RowResult:
     """MoBA forward for the listed rows (b, t, h) only.
 
-    `mu` may be passed in (block_means of k) to avoid recomputing it.
+    gate: "mean" (report §2.2) or "minmax" (the Quest-style variant, see the
+    header).  `mu` (block_means of k) or `minmax` (block_minmax of k) may be
+    passed in to avoid recomputing them.
     `given_sel`, if set, replaces the gate's choice for each row (used to check
     a row's output under another valid top-k set after a near tie).
     q, k, v can be any array type with numpy indexing (torch CPU tensors are
@@ -226,8 +260,12 @@ def moba_rows(q, k, v, block_size: int, topk: int, causal: bool,
     B = block_size
     g = Hq // Hkv
     scale = 1.0 / math.sqrt(D)
-    if mu is None:
+    if gate not in ("mean", "minmax"):
+        raise ValueError("gate must be 'mean' or 'minmax'")
+    if gate == "mean" and mu is None:
         mu = block_means(k, B)
+    if gate == "minmax" and minmax is None:
+        minmax = block_minmax(k, B)
     absk = None
     res = RowResult(len(rows), D, topk)
     # group rows by (batch, kv head) so each head's K/V is converted once
@@ -243,7 +281,10 @@ def moba_rows(q, k, v, block_size: int, topk: int, causal: bool,
             absk = np.abs(k_head).reshape(S // B, B, D).mean(axis=1)  # [n, D] mean |K| per block
         q64 = np.asarray(q[bb, t, h], dtype=np.float64)
         j = t // B
-        scores = gate_scores(q64, mu[bb, hk])
+        if gate == "mean":
+            scores = gate_scores(q64, mu[bb, hk])
+        else:
+            scores = gate_scores_minmax(q64, minmax[0][bb, hk], minmax[1][bb, hk])
         if given_sel is None:
             sel = select_blocks(scores, j, topk, causal)
         else:
@@ -259,7 +300,10 @@ def moba_rows(q, k, v, block_size: int, topk: int, causal: bool,
             ranked = sorted(cand, key=lambda i: (-float(scores[i]), i))
             res.gap[r] = float(scores[ranked[m - 1]] - scores[ranked[m]])
             res.boundary[r] = (scores[ranked[m - 1]], scores[ranked[m]])
-        res.score_eps[r] = score_error_bound(q64, mu[bb, hk], absk, B)
+        if gate == "mean":
+            res.score_eps[r] = score_error_bound(q64, mu[bb, hk], absk, B)
+        else:
+            res.score_eps[r] = score_error_bound_minmax(q64, minmax[0][bb, hk], minmax[1][bb, hk])
     return res
 
 
@@ -289,6 +333,16 @@ def score_error_bound(q64: np.ndarray, mu_head: np.ndarray, absk_mean: np.ndarra
     dot = _gamma(3 * D + 1) * (np.abs(mu_head) @ np.abs(q64))
     mean = _gamma(B + 2) * (absk_mean @ np.abs(q64))
     return float(np.max(dot + mean))
+
+
+def score_error_bound_minmax(q64: np.ndarray, lo_head: np.ndarray, hi_head: np.ndarray) -> float:
+    """An upper bound, over all blocks of this row, on |fp32 score - exact
+    score| for the min/max gate when the score is formed in fp32 in any order
+    from exact products (q_d times the chosen bound, or the bf16 split
+    q+ . hi + q- . lo over 2 D terms): gamma_{2D+1} * sum_d |q_d| max(|lo_d|, |hi_d|)."""
+    D = q64.shape[0]
+    mag = np.maximum(np.abs(lo_head), np.abs(hi_head)) @ np.abs(q64)
+    return float(np.max(_gamma(2 * D + 1) * mag))
 
 
 def valid_topk_set(scores: np.ndarray, chosen_past: Iterable[int], j: int, m: int, eps: float) -> bool:

@@ -439,3 +439,127 @@ def test_planted_own_block_off_by_one_is_caught(monkeypatch):
     monkeypatch.setattr(O, "_attend_blocks", leak)
     out, _ = O.moba_forward(q, k, v, 16, 4, True)
     assert np.max(np.abs(out - sdpa_fp64(q, k, v, causal=True))) > 1e-6
+
+
+# ----------------------------------------------------------------------------
+# the Quest-style min/max gate (report §1.3: MoBA with min/max pooling)
+# ----------------------------------------------------------------------------
+def test_minmax_score_is_the_largest_logit_over_the_box():
+    """The min/max score bounds q.k from above for every key of the block,
+    equals it when the block has one key, and is attained at the box corner
+    that takes the upper bound where q_d >= 0 and the lower one elsewhere."""
+    rng = np.random.default_rng(31)
+    D, B, n = 6, 5, 7
+    keys = rng.standard_normal((n, B, D))
+    lo = np.array([[min(keys[i, s, d] for s in range(B)) for d in range(D)] for i in range(n)])
+    hi = np.array([[max(keys[i, s, d] for s in range(B)) for d in range(D)] for i in range(n)])
+    for _ in range(20):
+        q = rng.standard_normal(D)
+        sc = O.gate_scores_minmax(q, lo, hi)
+        for i in range(n):
+            best_key = max(float(keys[i, s] @ q) for s in range(B))
+            assert sc[i] >= best_key - 1e-12
+            corner = np.array([hi[i, d] if q[d] >= 0 else lo[i, d] for d in range(D)])
+            assert abs(sc[i] - float(corner @ q)) < 1e-12
+    # one key per block: the box is a point and the score is the logit itself
+    one = rng.standard_normal((n, D))
+    q = rng.standard_normal(D)
+    assert np.max(np.abs(O.gate_scores_minmax(q, one, one) - one @ q)) < 1e-12
+
+
+def test_block_minmax_definition():
+    rng = np.random.default_rng(32)
+    k = rng.standard_normal((2, 24, 3, 4))
+    lo, hi = O.block_minmax(k, 8)
+    for bb in range(2):
+        for hk in range(3):
+            for i in range(3):
+                for d in range(4):
+                    vals = [k[bb, s, hk, d] for s in range(i * 8, (i + 1) * 8)]
+                    assert lo[bb, hk, i, d] == min(vals) and hi[bb, hk, i, d] == max(vals)
+
+
+def brute_force_minmax_selection(q, k, B, topk):
+    """Causal selection with the min/max gate, by explicit loops and subset
+    enumeration (max score sum, ties to the lexicographically smallest)."""
+    b, S, Hq, D = q.shape
+    g = Hq // k.shape[2]
+    n = S // B
+    sels = np.full((b, Hq, S, topk), -1, dtype=np.int32)
+    for bb in range(b):
+        for h in range(Hq):
+            hk = h // g
+            for t in range(S):
+                j = t // B
+                score = []
+                for i in range(n):
+                    tot = 0.0
+                    for d in range(D):
+                        col = [k[bb, s, hk, d] for s in range(i * B, (i + 1) * B)]
+                        tot += q[bb, t, h, d] * (max(col) if q[bb, t, h, d] >= 0 else min(col))
+                    score.append(tot)
+                m = min(topk - 1, j)
+                best = None
+                for sub in itertools.combinations(range(j), m):
+                    key = (sum(score[i] for i in sub), tuple(-i for i in sub))
+                    if best is None or key > best[0]:
+                        best = (key, sub)
+                chosen = sorted(best[1] + (j,))
+                sels[bb, h, t, :len(chosen)] = chosen
+    return sels
+
+
+@pytest.mark.parametrize("S,B,topk,Hq,Hkv", [(32, 4, 3, 2, 1), (24, 4, 4, 1, 1), (32, 8, 2, 2, 2)])
+def test_minmax_gate_bruteforce_tiny(S, B, topk, Hq, Hkv):
+    rng = np.random.default_rng(33 + S + B)
+    q, k, v = rand_qkv(rng, 1, S, Hq, Hkv, 4)
+    out, sel = O.moba_forward(q, k, v, B, topk, True, gate="minmax")
+    assert np.array_equal(sel, brute_force_minmax_selection(q, k, B, topk))
+    # the attention itself is the method's, given the selection
+    ref = O.moba_rows(q, k, v, B, topk, True, [(0, t, h) for h in range(Hq) for t in range(S)],
+                      given_sel=[sel[0, h, t] for h in range(Hq) for t in range(S)])
+    got = np.stack([out[0, t, h] for h in range(Hq) for t in range(S)])
+    assert np.max(np.abs(got - ref.out)) == 0.0
+
+
+def test_minmax_gate_dense_and_shift_invariance():
+    """With topk >= n the gate does not matter: dense causal attention; and
+    K + c leaves every min/max score shifted by q.c, so nothing changes."""
+    rng = np.random.default_rng(34)
+    q, k, v = rand_qkv(rng, 1, 64, 2, 1, 8)
+    out, _ = O.moba_forward(q, k, v, 16, 4, True, gate="minmax")
+    dense, _ = O.moba_forward(q, k, v, 64, 1, True)
+    assert np.max(np.abs(out - dense)) < 1e-12
+    q, k, v = rand_qkv(rng, 1, 96, 2, 1, 8)
+    out, sel = O.moba_forward(q, k, v, 16, 3, True, gate="minmax")
+    c = rng.standard_normal(8)
+    out2, sel2 = O.moba_forward(q, k + c, v, 16, 3, True, gate="minmax")
+    assert np.array_equal(sel, sel2)
+    assert np.max(np.abs(out - out2)) < 1e-9
+
+
+def test_minmax_gate_finds_the_block_the_mean_hides():
+    """One key of block 1 points along q while the rest cancel it (its mean
+    is ~0); block 2 has a small positive mean.  The mean gate takes block 2,
+    the min/max gate block 1."""
+    D, B = 4, 4
+    q = np.zeros((1, 4 * B, 1, D)); q[0, :, 0, 0] = 1.0
+    k = np.zeros((1, 4 * B, 1, D))
+    k[0, B + 0, 0, 0] = 3.0
+    k[0, B + 1:2 * B, 0, 0] = -1.0
+    k[0, 2 * B:3 * B, 0, 0] = 0.1
+    v = np.random.default_rng(35).standard_normal((1, 4 * B, 1, D))
+    t = 4 * B - 1  # own block 3; one past slot
+    _, sel_mean = O.moba_forward(q, k, v, B, 2, True)
+    _, sel_mm = O.moba_forward(q, k, v, B, 2, True, gate="minmax")
+    assert list(sel_mean[0, 0, t]) == [2, 3]
+    assert list(sel_mm[0, 0, t]) == [1, 3]
+
+
+def test_planted_swapped_minmax_bounds_are_caught(monkeypatch):
+    """A gate that takes the smaller product per dimension is a lower bound:
+    the upper-bound pin must fail for it."""
+    monkeypatch.setattr(O, "gate_scores_minmax",
+                        lambda q, lo, hi: np.minimum(lo * q, hi * q).sum(axis=1))
+    with pytest.raises(AssertionError):
+        test_minmax_score_is_the_largest_logit_over_the_box()
