@@ -47,7 +47,7 @@ def useful_flops(w) -> float:
     return 4.0 * D * keys * w.batch * w.num_q_heads
 
 
-def measure(M, W, w, steps, warmup, log):
+def measure(M, W, w, steps, warmup, log, gate="mean"):
     import torch
     dev = "cuda"
     t0 = time.perf_counter()
@@ -60,7 +60,7 @@ def measure(M, W, w, steps, warmup, log):
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: inputs ready in {time.perf_counter() - t0:.1f}s, workspace {nbytes / 2**30:.2f} GiB")
     for i in range(warmup):
-        M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal, out=out, sel_idx=sel, workspace=ws)
+        M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal, out=out, sel_idx=sel, workspace=ws, gate=gate)
         torch.cuda.synchronize()
         log(f"[bench] {w.name}: warmup {i + 1}/{warmup} done")
     M.profile_read()  # drop anything recorded earlier
@@ -68,7 +68,7 @@ def measure(M, W, w, steps, warmup, log):
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
-        M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal, out=out, sel_idx=sel, workspace=ws)
+        M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal, out=out, sel_idx=sel, workspace=ws, gate=gate)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     M.profile_enable(False)
@@ -80,6 +80,7 @@ def measure(M, W, w, steps, warmup, log):
     attn_fl = (stages["attn_past"]["work"] + stages["attn_own"]["work"] + stages["attn_f32"]["work"]) / steps
     res = {
         "workload": w.name,
+        "gate": gate,
         "ms_per_step": ms,
         "useful_tflops": fl / (ms * 1e-3) / 1e12,
         "tokens_per_s": w.batch * w.seqlen / (ms * 1e-3),
@@ -120,9 +121,10 @@ def roofline(stages, steps):
             "flops_per_launch": flops_per_launch}
 
 
-def cpu_baseline(W, w, inputs, budget_s, log, per_call=64):
+def cpu_baseline(W, w, inputs, budget_s, log, per_call=64, gate="mean"):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
-    block means over all of K, then seeded query rows until the budget is used."""
+    block summaries (means, or min / max) over all of K, then seeded query rows
+    until the budget is used."""
     import numpy as np
     import torch
     import oracle.moba_oracle as O
@@ -140,9 +142,10 @@ def cpu_baseline(W, w, inputs, budget_s, log, per_call=64):
     t_copy = time.perf_counter() - t0
     log(f"[cpu] host copies {t_copy:.1f}s")
     t0 = time.perf_counter()
-    mu = O.block_means(k32, w.block_size)
+    mu = O.block_means(k32, w.block_size) if gate == "mean" else None
+    mm = O.block_minmax(k32, w.block_size) if gate == "minmax" else None
     t_mu = time.perf_counter() - t0
-    log(f"[cpu] block means {t_mu:.1f}s")
+    log(f"[cpu] block summaries ({gate}) {t_mu:.1f}s")
 
     class Rows:
         shape, ndim = tuple(qh.shape), qh.ndim
@@ -170,7 +173,7 @@ def cpu_baseline(W, w, inputs, budget_s, log, per_call=64):
         if t_rows >= budget_s:
             break
         t0 = time.perf_counter()
-        O.moba_rows(Rows(), k32, v32, B, w.topk, w.causal, chunk, mu=mu)
+        O.moba_rows(Rows(), k32, v32, B, w.topk, w.causal, chunk, mu=mu, gate=gate, minmax=mm)
         t_rows += time.perf_counter() - t0
         calls += 1
         for (_, t, _) in chunk:
@@ -182,7 +185,8 @@ def cpu_baseline(W, w, inputs, budget_s, log, per_call=64):
     total_rows = w.batch * w.seqlen * w.num_q_heads
     log(f"[cpu] {done} rows in {t_rows:.1f}s")
     return {"value": fl / t_rows / 1e12, "unit": "TFLOP/s", "cores": blas_threads, "kind": "oracle",
-            "sample": f"fp64 numpy oracle: block means over all of K ({t_mu:.1f}s) plus {done} seeded query rows "
+            "sample": f"fp64 numpy oracle: block {'means' if gate == 'mean' else 'min / max'} over all of K "
+                      f"({t_mu:.1f}s) plus {done} seeded query rows "
                       f"of the {w.name} workload in {calls} calls of up to {per_call} rows sharing a KV head "
                       f"({t_rows:.1f}s, per-head fp64 conversion included); value = useful FLOPs of those rows "
                       f"/ their time",
@@ -350,6 +354,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--gate", choices=("mean", "minmax"), default="mean",
+                    help="block gate: block means (the method's) or element-wise key min / max")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain copy of MIB MiB first (reference dispatch for HBM byte counters)")
     ap.add_argument("--curve", nargs="*", type=int, metavar="SEQLEN",
@@ -389,7 +395,7 @@ def main():
     w = W.WORKLOADS[args.workload]
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, log)
-    res, inputs, stages = measure(M, W, w, args.steps, args.warmup, log)
+    res, inputs, stages = measure(M, W, w, args.steps, args.warmup, log, gate=args.gate)
     line = {
         "metric": METRIC,
         "value": res["useful_tflops"],
@@ -405,7 +411,7 @@ def main():
         "data": "synthetic (seeded N(0,1), bf16-rounded; no dataset)",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
-                   "topk": w.topk, "causal": w.causal, "parallelism": "none (1 GPU)"},
+                   "topk": w.topk, "causal": w.causal, "gate": args.gate, "parallelism": "none (1 GPU)"},
         "tokens_per_s": res["tokens_per_s"],
         "attention_tflops": res["attention_tflops"],
         "mfma_util_attention": res["mfma_util_attention"],
@@ -414,11 +420,11 @@ def main():
     }
     if args.secondary:
         w2 = W.WORKLOADS[args.secondary]
-        res2, inputs2, _ = measure(M, W, w2, args.secondary_steps, max(args.warmup, 3), log)
+        res2, inputs2, _ = measure(M, W, w2, args.secondary_steps, max(args.warmup, 3), log, gate=args.gate)
         del inputs2
         line["secondary"] = res2
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(W, w, inputs, args.cpu_seconds, log)
+        line["cpu_baseline"] = cpu_baseline(W, w, inputs, args.cpu_seconds, log, gate=args.gate)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

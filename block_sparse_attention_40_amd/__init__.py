@@ -6,12 +6,14 @@ include/moba.h (libmoba.so, built in-tree); this package is a thin binding.
 from ._lib import (  # noqa: F401
     DTYPE_BF16,
     DTYPE_F32,
+    GATE_KINDS,
     LIB_PATH,
     MAX_SELECTIVE_TOPK,
     MobaError,
     moba_attn_fwd,
     moba_gate,
     moba_meanpool,
+    moba_minmaxpool,
     profile_enable,
     profile_read,
     STAGES,

@@ -30,6 +30,9 @@ SIGNATURES = {
                                             _c_i32, ctypes.POINTER(_c_sz)]),
     "moba_attn_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "moba_attn_fwd_gate": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "moba_minmaxpool": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p]),
     "moba_meanpool": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p]),
     "moba_gate": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                  _c_i32, _c_p, _c_p]),
@@ -37,6 +40,9 @@ SIGNATURES = {
     "moba_profile_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_i64),
                                          ctypes.POINTER(ctypes.c_double), _c_i32]),
 }
+
+# gate kinds (enum moba_gate_kind)
+GATE_KINDS = {"mean": 0, "minmax": 1}
 
 STAGES = ("meanpool", "gate", "dispatch", "attn_past", "attn_own", "attn_f32", "kv_layout")
 
@@ -103,11 +109,15 @@ def workspace_bytes(batch: int, seqlen: int, num_q_heads: int, num_kv_heads: int
 def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int, topk: int,
                   causal: bool = True, out: Optional[torch.Tensor] = None,
                   sel_idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  return_sel: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  return_sel: bool = True, gate: str = "mean") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """MoBA prefill forward.  q [b, S, Hq, D], k/v [b, S, Hkv, D] (bf16 with
     D = 128, or fp32 with D in {64, 128}).  Returns (out, sel_idx) where
     sel_idx is [b, Hq, S, topk] int32 (None if return_sel is False and no
-    sel_idx tensor was passed)."""
+    sel_idx tensor was passed).  gate: "mean" (block means) or "minmax"
+    (element-wise key min / max per block, score = largest q.k over the box);
+    "mean" calls moba_attn_fwd, "minmax" moba_attn_fwd_gate."""
+    if gate not in GATE_KINDS:
+        raise ValueError(f"gate must be one of {sorted(GATE_KINDS)}")
     _check_dev(q, k, v)
     b, S, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -124,12 +134,20 @@ def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size:
     _check_dev(out, workspace)
     if sel_idx is not None:
         _check_dev(sel_idx)
-    st = lib.moba_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, S, Hq, Hkv, D, dt, block_size, topk,
-                           int(bool(causal)), out.data_ptr(), sel_idx.data_ptr() if sel_idx is not None else None,
-                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                           _stream_ptr(q.device))
+    sel_ptr = sel_idx.data_ptr() if sel_idx is not None else None
+    ws_len = workspace.numel() * workspace.element_size()
+    if gate == "mean":
+        st = lib.moba_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, S, Hq, Hkv, D, dt, block_size, topk,
+                               int(bool(causal)), out.data_ptr(), sel_ptr, workspace.data_ptr(), ws_len,
+                               _stream_ptr(q.device))
+        where = "moba_attn_fwd"
+    else:
+        st = lib.moba_attn_fwd_gate(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, S, Hq, Hkv, D, dt, block_size,
+                                    topk, int(bool(causal)), GATE_KINDS[gate], out.data_ptr(), sel_ptr,
+                                    workspace.data_ptr(), ws_len, _stream_ptr(q.device))
+        where = "moba_attn_fwd_gate"
     if st != MOBA_OK:
-        raise MobaError(st, "moba_attn_fwd")
+        raise MobaError(st, where)
     return out, sel_idx
 
 
@@ -161,6 +179,20 @@ def moba_meanpool(k: torch.Tensor, block_size: int, mu: Optional[torch.Tensor] =
     if st != MOBA_OK:
         raise MobaError(st, "moba_meanpool")
     return mu
+
+
+def moba_minmaxpool(k: torch.Tensor, block_size: int, lohi: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Element-wise key min and max per block: lohi [b, Hkv, S / block_size,
+    2, D] fp32 (index 0 the min, 1 the max)."""
+    _check_dev(k)
+    b, S, Hkv, D = k.shape
+    if lohi is None:
+        lohi = torch.empty((b, Hkv, S // max(block_size, 1), 2, D), dtype=torch.float32, device=k.device)
+    st = lib.moba_minmaxpool(k.data_ptr(), b, S, Hkv, D, _dtype_code(k), block_size, lohi.data_ptr(),
+                             _stream_ptr(k.device))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_minmaxpool")
+    return lohi
 
 
 def moba_gate(q: torch.Tensor, mu: torch.Tensor, block_size: int, topk: int, causal: bool = True,

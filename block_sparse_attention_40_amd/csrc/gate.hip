@@ -21,11 +21,13 @@ namespace moba {
 
 constexpr int kMuSlice = 32;  // block means staged in LDS at a time
 
-template <typename T, int D, int KCAP>
+template <typename T, int D, int KCAP, bool kMinMax>
 __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
+  // per block: D floats of the mean, or 2 D (min, then max) for min/max
+  constexpr int SD = kMinMax ? 2 * D : D;
   extern __shared__ float smem[];
-  float* mu_s = smem;                                      // [kMuSlice][D]
-  int* lhist = reinterpret_cast<int*>(smem + kMuSlice * D);  // [n]
+  float* mu_s = smem;                                       // [kMuSlice][SD]
+  int* lhist = reinterpret_cast<int*>(smem + kMuSlice * SD);  // [n]
   const int tid = threadIdx.x;
   const int64_t w = blockIdx.x;
   const int hk = blockIdx.y;
@@ -60,26 +62,37 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
 #pragma unroll
       for (int d0 = 0; d0 < D; d0 += 8) load8(qp + d0, qr + d0);
     }
-    const float* mu_h = a.mu + ((int64_t)a.bb * a.hkv + hk) * n * D;
+    const float* mu_h = (kMinMax ? a.lohi : a.mu) + ((int64_t)a.bb * a.hkv + hk) * n * SD;
     for (int64_t c0 = 0; c0 < wg_cand; c0 += kMuSlice) {
       const int64_t c1 = (c0 + kMuSlice < wg_cand) ? c0 + kMuSlice : wg_cand;
       __syncthreads();
-      const int nel = (int)(c1 - c0) * D;
+      const int nel = (int)(c1 - c0) * SD;
       for (int e = tid * 4; e < nel; e += 256 * 4)
-        *reinterpret_cast<f32x4*>(mu_s + e) = *reinterpret_cast<const f32x4*>(mu_h + c0 * D + e);
+        *reinterpret_cast<f32x4*>(mu_s + e) = *reinterpret_cast<const f32x4*>(mu_h + c0 * SD + e);
       __syncthreads();
       if (rank) {
         const int64_t cend = ncand < c1 ? ncand : c1;
         for (int64_t i = c0; i < cend; ++i) {
-          const float* mrow = mu_s + (i - c0) * D;
+          const float* mrow = mu_s + (i - c0) * SD;
           float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
           for (int d0 = 0; d0 < D; d0 += 4) {
-            f32x4 mv = *reinterpret_cast<const f32x4*>(mrow + d0);
-            s0 = __builtin_fmaf(qr[d0 + 0], mv[0], s0);
-            s1 = __builtin_fmaf(qr[d0 + 1], mv[1], s1);
-            s2 = __builtin_fmaf(qr[d0 + 2], mv[2], s2);
-            s3 = __builtin_fmaf(qr[d0 + 3], mv[3], s3);
+            const f32x4 mv = *reinterpret_cast<const f32x4*>(mrow + d0);
+            if constexpr (kMinMax) {
+              // term d: max(q_d lo_d, q_d hi_d), each product rounded once
+              // (a per-d select on the sign of q would keep 128 lane masks
+              // live across the block loop)
+              const f32x4 hv = *reinterpret_cast<const f32x4*>(mrow + D + d0);
+              s0 += __builtin_fmaxf(qr[d0 + 0] * mv[0], qr[d0 + 0] * hv[0]);
+              s1 += __builtin_fmaxf(qr[d0 + 1] * mv[1], qr[d0 + 1] * hv[1]);
+              s2 += __builtin_fmaxf(qr[d0 + 2] * mv[2], qr[d0 + 2] * hv[2]);
+              s3 += __builtin_fmaxf(qr[d0 + 3] * mv[3], qr[d0 + 3] * hv[3]);
+            } else {
+              s0 = __builtin_fmaf(qr[d0 + 0], mv[0], s0);
+              s1 = __builtin_fmaf(qr[d0 + 1], mv[1], s1);
+              s2 = __builtin_fmaf(qr[d0 + 2], mv[2], s2);
+              s3 = __builtin_fmaf(qr[d0 + 3], mv[3], s3);
+            }
           }
           float s = (s0 + s1) + (s2 + s3);
           if (s != s) s = -__builtin_inff();  // NaN ranks lowest
@@ -157,6 +170,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
 // 32 blocks of one unit hit every bank once), 24 KiB per tile.
 // ---------------------------------------------------------------------------
 constexpr int kMu3TileElems = 3 * 16 * kGateTile * 8;  // bf16 per tile image
+static_assert(16 * kGateTile * 8 == 512 * 8, "the MFMA gate stages one part per 512 threads x 8 bf16");
 
 __global__ __launch_bounds__(256) void mu_split_kernel(const float* __restrict__ mu, int64_t n, int hkv,
                                                        uint16_t* __restrict__ mu3) {
@@ -199,6 +213,55 @@ __global__ __launch_bounds__(256) void mu_split_kernel(const float* __restrict__
   }
 }
 
+// Min/max gate on the matrix cores: max(q_d lo_d, q_d hi_d) = q+_d hi_d +
+// q-_d lo_d with q+ = max(q, 0) and q- = min(q, 0), both exact in bf16; with
+// bf16 keys, lo and hi are bf16 values, so the score is two exact-product
+// dot products (2 D terms) accumulated in fp32.  Images as above with two
+// parts: part 0 = hi (paired with q+), part 1 = lo (paired with q-).
+__global__ __launch_bounds__(256) void mm_split_kernel(const float* __restrict__ lohi, int64_t n, int hkv,
+                                                       uint16_t* __restrict__ mu3) {
+  const int64_t tile = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int64_t bb = blockIdx.z;
+  const int64_t ntile = (n + kGateTile - 1) / kGateTile;
+  const float* src = lohi + (bb * hkv + hk) * n * 256;
+  uint16_t* dst = mu3 + ((bb * hkv + hk) * ntile + tile) * kMu3TileElems;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int pair = threadIdx.x + 256 * x;  // (unit, block) of the tile
+    const int u = pair >> 5, blk = pair & 31;
+    const int64_t i = tile * kGateTile + blk;
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (i < n) {
+        const float* row = src + i * 256 + (part == 0 ? 128 : 0) + u * 8;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(row);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(row + 4);
+        w[0] = pack_bf16x2(a[0], a[1]);
+        w[1] = pack_bf16x2(a[2], a[3]);
+        w[2] = pack_bf16x2(b[0], b[1]);
+        w[3] = pack_bf16x2(b[2], b[3]);
+      }
+      *reinterpret_cast<u32x4*>(dst + ((part * 16 + u) * kGateTile + blk) * 8) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+// q+ and q- of eight packed bf16: q+ keeps the halves whose sign bit is
+// clear, q- those whose sign bit is set (the other halves become +0).
+__device__ __forceinline__ void sign_split(u32x4 w, bf16x8& pos, bf16x8& neg) {
+  u32x4 p, n;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t m = ((w[i] >> 15) & 0x00010001u) * 0xffffu;  // 0xffff in each negative half
+    n[i] = w[i] & m;
+    p[i] = w[i] ^ n[i];
+  }
+  pos = __builtin_bit_cast(bf16x8, p);
+  neg = __builtin_bit_cast(bf16x8, n);
+}
+
 // Insert a 64-bit key into a descending top list (ks[0] largest).
 template <int KCAP>
 __device__ __forceinline__ void topk_insert(uint64_t* ks, uint64_t key) {
@@ -220,8 +283,10 @@ __device__ __forceinline__ void topk_insert(uint64_t* ks, uint64_t key) {
 // lane l then holds 16 of the 32 scores of row l % 32 (the other 16 are in
 // lane l ^ 32) and keeps its own top list; at the end the two lists of a
 // row are merged.
-template <int KCAP>
-__global__ __launch_bounds__(512) void gate_mfma_kernel(GateArgs a, const uint16_t* __restrict__ mu3) {
+template <int KCAP, bool kMinMax>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(KCAP <= 12 ? 4 : 1))) void gate_mfma_kernel(
+    GateArgs a, const uint16_t* __restrict__ mu3) {
+  constexpr int NPART = kMinMax ? 2 : 3;
   extern __shared__ __attribute__((aligned(16))) char gsm[];
   char* tbuf = gsm;                                          // 2 tile images
   int* lhist = reinterpret_cast<int*>(gsm + 2 * kMu3TileElems * 2);  // [n]
@@ -263,14 +328,16 @@ __global__ __launch_bounds__(512) void gate_mfma_kernel(GateArgs a, const uint16
     }
     const uint16_t* mt = mu3 + ((int64_t)a.bb * a.hkv + hk) * ntile * kMu3TileElems;
     const int aofs = (lg * 32 + (lane & 31)) * 16;  // this lane's A-operand unit (part 0, step 0)
-    u32x4 stg[3];
+    // one 16-byte unit per thread and part (512 threads x 8 bf16 = one part)
+    u32x4 stg[NPART];
     auto load_tile = [&](int64_t c) {
 #pragma unroll
-      for (int x = 0; x < 3; ++x) stg[x] = *reinterpret_cast<const u32x4*>(mt + c * kMu3TileElems + (tid + 512 * x) * 8);
+      for (int x = 0; x < NPART; ++x)
+        stg[x] = *reinterpret_cast<const u32x4*>(mt + c * kMu3TileElems + (tid + 512 * x) * 8);
     };
     auto store_tile = [&](char* dst) {
 #pragma unroll
-      for (int x = 0; x < 3; ++x) *reinterpret_cast<u32x4*>(dst + (tid + 512 * x) * 16) = stg[x];
+      for (int x = 0; x < NPART; ++x) *reinterpret_cast<u32x4*>(dst + (tid + 512 * x) * 16) = stg[x];
     };
     load_tile(0);
     store_tile(tbuf);
@@ -284,19 +351,43 @@ __global__ __launch_bounds__(512) void gate_mfma_kernel(GateArgs a, const uint16
         f32x16 s0, s1;
 #pragma unroll
         for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
-#pragma unroll
-        for (int part = 0; part < 3; ++part)
+        if constexpr (kMinMax) {
+          // B operands q+ (with hi, part 0) and q- (with lo, part 1), formed
+          // from q per tile: the opaque copy keeps the compiler from holding
+          // all 16 of them live across the loop (32 more VGPRs, half the
+          // work-groups per CU)
 #pragma unroll
           for (int st = 0; st < 8; st += 2) {
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(cur + aofs + (part * 16 + 2 * st) * 512);
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(cur + aofs + (part * 16 + 2 * st + 2) * 512);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[st], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[st + 1], s1, 0, 0, 0);
+            u32x4 w0 = __builtin_bit_cast(u32x4, qb[st]), w1 = __builtin_bit_cast(u32x4, qb[st + 1]);
+            asm volatile("" : "+v"(w0));
+            asm volatile("" : "+v"(w1));
+            bf16x8 p0, n0, p1, n1;
+            sign_split(w0, p0, n0);
+            sign_split(w1, p1, n1);
+            const bf16x8 h0 = *reinterpret_cast<const bf16x8*>(cur + aofs + (2 * st) * 512);
+            const bf16x8 h1 = *reinterpret_cast<const bf16x8*>(cur + aofs + (2 * st + 2) * 512);
+            const bf16x8 l0 = *reinterpret_cast<const bf16x8*>(cur + aofs + (16 + 2 * st) * 512);
+            const bf16x8 l1 = *reinterpret_cast<const bf16x8*>(cur + aofs + (16 + 2 * st + 2) * 512);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, p0, s0, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, p1, s0, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l0, n0, s0, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l1, n1, s0, 0, 0, 0);
           }
+        } else {
+#pragma unroll
+          for (int part = 0; part < NPART; ++part)
+#pragma unroll
+            for (int st = 0; st < 8; st += 2) {
+              const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(cur + aofs + (part * 16 + 2 * st) * 512);
+              const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(cur + aofs + (part * 16 + 2 * st + 2) * 512);
+              s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[st], s0, 0, 0, 0);
+              s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[st + 1], s1, 0, 0, 0);
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int64_t i = c * kGateTile + 8 * (e >> 2) + 4 * lg + (e & 3);
-          float sc = s0[e] + s1[e];
+          float sc = kMinMax ? s0[e] : s0[e] + s1[e];
           if (sc != sc) sc = -__builtin_inff();  // NaN ranks lowest
           const uint64_t key = ((uint64_t)orderable(sc) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
           if (rank && i < ncand) topk_insert<KCAP>(ks, key);
@@ -363,14 +454,42 @@ __global__ __launch_bounds__(512) void gate_mfma_kernel(GateArgs a, const uint16
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kMinMax>
 static void launch_gate_kcap(const GateArgs& a, int kcap, size_t shmem, hipStream_t st, dim3 grid) {
   if (kcap <= 4)
-    hipLaunchKernelGGL((gate_kernel<T, D, 4>), grid, dim3(256), shmem, st, a);
+    hipLaunchKernelGGL((gate_kernel<T, D, 4, kMinMax>), grid, dim3(256), shmem, st, a);
   else if (kcap <= 16)
-    hipLaunchKernelGGL((gate_kernel<T, D, 16>), grid, dim3(256), shmem, st, a);
+    hipLaunchKernelGGL((gate_kernel<T, D, 16, kMinMax>), grid, dim3(256), shmem, st, a);
   else
-    hipLaunchKernelGGL((gate_kernel<T, D, 32>), grid, dim3(256), shmem, st, a);
+    hipLaunchKernelGGL((gate_kernel<T, D, 32, kMinMax>), grid, dim3(256), shmem, st, a);
+}
+template <typename T, int D>
+static void launch_gate_valu(const GateArgs& a, int kcap, hipStream_t st, dim3 grid) {
+  const size_t hist = a.hist ? (size_t)a.n * sizeof(int) : 0;
+  if (a.minmax)
+    launch_gate_kcap<T, D, true>(a, kcap, (size_t)kMuSlice * 2 * D * sizeof(float) + hist, st, grid);
+  else
+    launch_gate_kcap<T, D, false>(a, kcap, (size_t)kMuSlice * D * sizeof(float) + hist, st, grid);
+}
+
+template <bool kMinMax>
+static void launch_gate_mfma(const GateArgs& a, int kc, size_t sh, hipStream_t st, dim3 grid) {
+  if (kc <= 4)
+    hipLaunchKernelGGL((gate_mfma_kernel<4, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);
+  else if (kc <= 8)
+    hipLaunchKernelGGL((gate_mfma_kernel<8, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);
+  else if (kc <= 12)
+    hipLaunchKernelGGL((gate_mfma_kernel<12, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);
+  else if (kc <= 16)
+    hipLaunchKernelGGL((gate_mfma_kernel<16, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);
+  else
+    hipLaunchKernelGGL((gate_mfma_kernel<32, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);
+}
+
+int launch_mm_split(const float* lohi, int64_t batch, int64_t n, int hkv, uint16_t* mu3, hipStream_t st) {
+  hipLaunchKernelGGL(mm_split_kernel, dim3((unsigned)((n + kGateTile - 1) / kGateTile), (unsigned)hkv, (unsigned)batch),
+                     dim3(256), 0, st, lohi, n, hkv, mu3);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_mu_split(const float* mu, int64_t batch, int64_t n, int hkv, uint16_t* mu3, hipStream_t st) {
@@ -384,26 +503,19 @@ int launch_gate(const GateArgs& a, int dtype, int d, hipStream_t st) {
   if (dtype == 1 && a.mu3 && a.gate_t * a.g <= 256) {
     const size_t sh = (size_t)2 * kMu3TileElems * 2 + (a.hist ? (size_t)a.n * sizeof(int) : 0);
     const int kc = a.kp < 1 ? 1 : a.kp;
-    if (kc <= 4)
-      hipLaunchKernelGGL(gate_mfma_kernel<4>, grid, dim3(512), sh, st, a, a.mu3);
-    else if (kc <= 8)
-      hipLaunchKernelGGL(gate_mfma_kernel<8>, grid, dim3(512), sh, st, a, a.mu3);
-    else if (kc <= 12)
-      hipLaunchKernelGGL(gate_mfma_kernel<12>, grid, dim3(512), sh, st, a, a.mu3);
-    else if (kc <= 16)
-      hipLaunchKernelGGL(gate_mfma_kernel<16>, grid, dim3(512), sh, st, a, a.mu3);
+    if (a.minmax)
+      launch_gate_mfma<true>(a, kc, sh, st, grid);
     else
-      hipLaunchKernelGGL(gate_mfma_kernel<32>, grid, dim3(512), sh, st, a, a.mu3);
+      launch_gate_mfma<false>(a, kc, sh, st, grid);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  const size_t shmem = (size_t)kMuSlice * d * sizeof(float) + (a.hist ? (size_t)a.n * sizeof(int) : 0);
   const int kcap = a.kp < 1 ? 1 : a.kp;
   if (dtype == 1) {
-    launch_gate_kcap<bf16raw, 128>(a, kcap, shmem, st, grid);
+    launch_gate_valu<bf16raw, 128>(a, kcap, st, grid);
   } else if (d == 64) {
-    launch_gate_kcap<float, 64>(a, kcap, shmem, st, grid);
+    launch_gate_valu<float, 64>(a, kcap, st, grid);
   } else {
-    launch_gate_kcap<float, 128>(a, kcap, shmem, st, grid);
+    launch_gate_valu<float, 128>(a, kcap, st, grid);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -146,6 +146,16 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                   int32_t block_size, int32_t topk, int32_t causal, void* out, int32_t* sel_idx,
                   void* workspace, size_t workspace_bytes, void* stream) {
+  return moba_attn_fwd_gate(q, k, v, batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
+                            causal, MOBA_GATE_MEAN, out, sel_idx, workspace, workspace_bytes, stream);
+}
+
+int moba_attn_fwd_gate(const void* q, const void* k, const void* v, int64_t batch, int64_t seqlen,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                       int32_t block_size, int32_t topk, int32_t causal, int32_t gate_kind, void* out,
+                       int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  if (gate_kind != MOBA_GATE_MEAN && gate_kind != MOBA_GATE_MINMAX) return MOBA_ERR_SHAPE;
+  const bool minmax = gate_kind == MOBA_GATE_MINMAX;
   Plan p;
   const int st = make_plan(Shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
                                  causal ? 1 : 0},
@@ -173,18 +183,28 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
 
   const double elt = bf16 ? 2.0 : 4.0;
   const double D = head_dim;
-  // 1. block means of the keys, all blocks of all batch entries
+  float* lohi = reinterpret_cast<float*>(ws + p.off_lohi);
+  // 1. block summaries of the keys (means, or min / max), all blocks of all batch entries
   {
     StageScope sc(MOBA_STAGE_MEANPOOL, s,
-                  (double)batch * seqlen * num_kv_heads * D * elt + (double)batch * num_kv_heads * p.n * D * 4.0);
-    if (launch_meanpool(k, dtype, batch, seqlen, num_kv_heads, head_dim, block_size, mu, s)) return MOBA_ERR_HIP;
+                  (double)batch * seqlen * num_kv_heads * D * elt +
+                      (double)batch * num_kv_heads * p.n * D * (minmax ? 8.0 : 4.0));
+    if (minmax) {
+      if (launch_minmaxpool(k, dtype, batch, seqlen, num_kv_heads, head_dim, block_size, lohi, s))
+        return MOBA_ERR_HIP;
+    } else if (launch_meanpool(k, dtype, batch, seqlen, num_kv_heads, head_dim, block_size, mu, s)) {
+      return MOBA_ERR_HIP;
+    }
   }
-  // bf16 gate: the means split into three bf16 parts for the score MFMAs
+  // bf16 gate: the summaries as MFMA tile images (means split into three
+  // bf16 parts; max and min as they are)
   uint16_t* mu3 = nullptr;
   if (bf16 && p.selective) {
     mu3 = reinterpret_cast<uint16_t*>(ws + p.off_mu3);
-    StageScope sc(MOBA_STAGE_MEANPOOL, s, (double)batch * num_kv_heads * p.n * D * (4.0 + 6.0));
-    if (launch_mu_split(mu, batch, p.n, num_kv_heads, mu3, s)) return MOBA_ERR_HIP;
+    StageScope sc(MOBA_STAGE_MEANPOOL, s, (double)batch * num_kv_heads * p.n * D * (minmax ? 8.0 + 4.0 : 4.0 + 6.0));
+    if (minmax ? launch_mm_split(lohi, batch, p.n, num_kv_heads, mu3, s)
+               : launch_mu_split(mu, batch, p.n, num_kv_heads, mu3, s))
+      return MOBA_ERR_HIP;
   }
 
   uint16_t* kimg = p.kv_image ? reinterpret_cast<uint16_t*>(ws + p.off_kimg) : nullptr;
@@ -214,7 +234,7 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
       const bool need_lists = bf16 && p.kp > 0;
 
       GateArgs ga{};
-      ga.q = q; ga.mu = mu; ga.mu3 = mu3; ga.sel = sel_base; ga.sel_stride_h = sel_stride_h; ga.sel_pos_base = sel_pos_base;
+      ga.q = q; ga.mu = mu; ga.lohi = lohi; ga.minmax = minmax ? 1 : 0; ga.mu3 = mu3; ga.sel = sel_base; ga.sel_stride_h = sel_stride_h; ga.sel_pos_base = sel_pos_base;
       ga.hist = need_lists ? hist : nullptr;
       ga.seqlen = seqlen; ga.n = p.n; ga.t0 = t0; ga.cnt = cnt; ga.gate_wg = gate_wg;
       ga.hq = num_q_heads; ga.hkv = num_kv_heads; ga.block = block_size; ga.topk = topk; ga.kp = p.kp;
@@ -288,6 +308,19 @@ int moba_meanpool(const void* k, int64_t batch, int64_t seqlen, int32_t num_kv_h
   if (misaligned(k) || misaligned(mu)) return MOBA_ERR_ALIGN;
   if (launch_meanpool(k, dtype, batch, seqlen, num_kv_heads, head_dim, block_size, mu,
                       reinterpret_cast<hipStream_t>(stream)))
+    return MOBA_ERR_HIP;
+  return MOBA_OK;
+}
+
+int moba_minmaxpool(const void* k, int64_t batch, int64_t seqlen, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t dtype, int32_t block_size, float* lohi, void* stream) {
+  Plan p;
+  const int st = make_plan(Shape{batch, seqlen, num_kv_heads, num_kv_heads, head_dim, dtype, block_size, 1, 1}, &p);
+  if (st != MOBA_OK) return st;
+  if (!k || !lohi) return MOBA_ERR_NULL;
+  if (misaligned(k) || misaligned(lohi)) return MOBA_ERR_ALIGN;
+  if (launch_minmaxpool(k, dtype, batch, seqlen, num_kv_heads, head_dim, block_size, lohi,
+                        reinterpret_cast<hipStream_t>(stream)))
     return MOBA_ERR_HIP;
   return MOBA_OK;
 }

@@ -9,8 +9,10 @@ namespace moba {
 // Gate over one query chunk: positions [t0, t0 + cnt) of batch entry bb.
 struct GateArgs {
   const void* q;
-  const float* mu;       // [batch, hkv, n, D]
-  const uint16_t* mu3;   // split means as MFMA tile images (bf16 path), or null
+  const float* mu;       // [batch, hkv, n, D] block means (mean gate)
+  const float* lohi;     // [batch, hkv, n, 2, D] block key min / max (min/max gate)
+  const uint16_t* mu3;   // the bf16 path's MFMA tile images of the summaries, or null
+  int32_t minmax;        // 1: the min/max gate, 0: the mean gate
   int32_t* sel;          // row (h, t) at sel + h * sel_stride_h + (t - sel_pos_base) * topk
   int64_t sel_stride_h;
   int64_t sel_pos_base;
@@ -90,6 +92,11 @@ int launch_meanpool(const void* k, int dtype, int64_t batch, int64_t seqlen, int
 int launch_gate(const GateArgs& a, int dtype, int d, hipStream_t stream);
 // Block means split into three bf16 parts, as the gate's MFMA tile images.
 int launch_mu_split(const float* mu, int64_t batch, int64_t n, int hkv, uint16_t* mu3, hipStream_t stream);
+// Block key max and min (bf16 values) as the min/max gate's MFMA tile images.
+int launch_mm_split(const float* lohi, int64_t batch, int64_t n, int hkv, uint16_t* mu3, hipStream_t stream);
+// Element-wise min / max of each block's keys: lohi [batch, hkv, n, 2, d].
+int launch_minmaxpool(const void* k, int dtype, int64_t batch, int64_t seqlen, int hkv, int d, int block,
+                      float* lohi, hipStream_t stream);
 int launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 int launch_attn_past(const PastArgs& a, hipStream_t stream);
 int launch_attn_own(const OwnArgs& a, hipStream_t stream);

@@ -85,6 +85,8 @@ int make_plan(const Shape& s, Plan* p) {
                          ? (size_t)s.batch * s.hkv * ((q.n + kGateTile - 1) / kGateTile) * kGateTile * 3 * s.d * 2
                          : 0;
   q.off_mu3 = take(mu3);
+  // min/max gate: the element-wise key min and max per block, fp32
+  q.off_lohi = take((size_t)s.batch * s.hkv * q.n * 2 * s.d * sizeof(float));
   q.total = off;
   *p = q;
   return MOBA_OK;

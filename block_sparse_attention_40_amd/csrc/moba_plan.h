@@ -51,7 +51,7 @@ struct Plan {
   bool kv_image;        // K and V are re-laid out per 64-key slice for direct LDS loads (bf16, block % 64 == 0)
   // workspace layout (byte offsets, 256-aligned)
   size_t off_mu, off_sel, off_hist, off_count, off_listoff, off_tiles, off_entries;
-  size_t off_part_o, off_part_lse, off_kimg, off_vimg, off_mu3, total;
+  size_t off_part_o, off_part_lse, off_kimg, off_vimg, off_mu3, off_lohi, total;
 };
 
 // Validate `s` and fill `p`.  Returns a moba_status code.

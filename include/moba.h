@@ -110,6 +110,43 @@ int moba_attn_fwd(const void* q, const void* k, const void* v,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Block summary and gate score (the method's gate, report 2.2, or the
+ * Quest-style variant the report places in the same family, report 1.3:
+ * min/max pooling of the block's keys).
+ */
+enum moba_gate_kind {
+  MOBA_GATE_MEAN = 0,   /* mu_i = mean of block i's keys; s_i = <q, mu_i> */
+  MOBA_GATE_MINMAX = 1  /* lo_i / hi_i = element-wise min / max of block i's keys;
+                           s_i = sum_d max(q_d lo_id, q_d hi_id), the largest q.k
+                           over the box [lo_i, hi_i] */
+};
+
+/*
+ * moba_attn_fwd_gate: moba_attn_fwd with the gate chosen by gate_kind (a
+ * moba_gate_kind; moba_attn_fwd is this call with MOBA_GATE_MEAN).  The causal
+ * rules, the forced own block, the top-k and the attention are unchanged.
+ * Same arguments, workspace size (moba_workspace_bytes covers both gates),
+ * ownership and errors as moba_attn_fwd; an unknown gate_kind returns
+ * MOBA_ERR_SHAPE.
+ */
+int moba_attn_fwd_gate(const void* q, const void* k, const void* v,
+                       int64_t batch, int64_t seqlen, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                       int32_t block_size, int32_t topk, int32_t causal,
+                       int32_t gate_kind, void* out, int32_t* sel_idx,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moba_minmaxpool: the min/max gate's pooling alone: lohi[b, hk, i, 0, :] =
+ * element-wise minimum and lohi[b, hk, i, 1, :] = maximum of the B keys of
+ * block i (exact: they are input values), fp32 [b, Hkv, n, 2, D], written in
+ * full.  k and its layout as for moba_attn_fwd.
+ */
+int moba_minmaxpool(const void* k, int64_t batch, int64_t seqlen,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                    int32_t block_size, float* lohi, void* stream);
+
+/*
  * moba_meanpool: stage 1 alone (report 2.2): mu[b, hk, i, :] = mean of the B
  * keys of block i, summed in fp32.  k as above; mu is written in full.
  */

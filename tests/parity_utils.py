@@ -51,8 +51,9 @@ class ParityReport:
 
 def compare(q_dev, k_dev, v_dev, out_dev, sel_dev, block_size: int, topk: int, causal: bool,
             rows: Optional[Sequence[Tuple[int, int, int]]] = None, tol: float = 2e-2,
-            mu: Optional[np.ndarray] = None) -> ParityReport:
-    """Compare GPU out / sel_idx with the oracle on `rows` (all rows if None).
+            mu: Optional[np.ndarray] = None, gate: str = "mean") -> ParityReport:
+    """Compare GPU out / sel_idx with the oracle on `rows` (all rows if None),
+    the oracle scoring blocks with `gate` ("mean" or "minmax").
     Raises AssertionError on any violation."""
     qh = q_dev.detach().cpu()
     k32, v32 = to_np32(k_dev), to_np32(v_dev)
@@ -63,9 +64,13 @@ def compare(q_dev, k_dev, v_dev, out_dev, sel_dev, block_size: int, topk: int, c
     outh = out_dev.detach().cpu().to(torch.float32)
     selh = sel_dev.detach().cpu()
     t0 = time.perf_counter()
-    if mu is None:
+    mm = None
+    if gate == "minmax":
+        mm = O.block_minmax(k32, block_size)
+    elif mu is None:
         mu = O.block_means(k32, block_size)
-    res = O.moba_rows(RowSource(qh), k32, v32, block_size, topk, causal, rows, mu=mu, keep_scores=True)
+    res = O.moba_rows(RowSource(qh), k32, v32, block_size, topk, causal, rows, mu=mu, keep_scores=True,
+                      gate=gate, minmax=mm)
     ties = O.near_tie_rows(res)
     gsel = np.stack([selh[bb, h, t].numpy() for (bb, t, h) in rows])
     mismatch = [r for r in range(len(rows)) if not np.array_equal(gsel[r], res.sel[r])]
@@ -88,7 +93,7 @@ def compare(q_dev, k_dev, v_dev, out_dev, sel_dev, block_size: int, topk: int, c
     if redo:
         sub_rows = [rows[r] for r in redo]
         sub = O.moba_rows(RowSource(qh), k32, v32, block_size, topk, causal, sub_rows, mu=mu,
-                          given_sel=[gsel[r] for r in redo])
+                          given_sel=[gsel[r] for r in redo], gate=gate, minmax=mm)
         for x, r in enumerate(redo):
             ref_out[r] = sub.out[x]
     secs = time.perf_counter() - t0

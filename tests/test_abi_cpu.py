@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import block_sparse_attention_40_amd as M
 from block_sparse_attention_40_amd import _lib
@@ -120,3 +121,31 @@ def test_stage_entry_points_reject_bad_arguments():
     assert L.moba_gate(FAKE, None, 1, 1024, 4, 2, 128, BF16, 128, 3, 1, FAKE, None) == NULL
     assert L.moba_gate(FAKE, FAKE, 1, 1024, 4, 2, 128, BF16, 128, 0, 1, FAKE, None) == TOPK
     assert L.moba_gate(FAKE, FAKE, 1, 1024, 4, 3, 128, BF16, 128, 3, 1, FAKE, None) == GQA
+
+
+def call_fwd_gate(gate_kind, q=FAKE, out=FAKE, **kw):
+    a = dict(b=1, S=1024, Hq=4, Hkv=2, D=128, dt=BF16, B=128, topk=3, causal=1)
+    a.update(kw)
+    st, wsb = ws(a["b"], a["S"], a["Hq"], a["Hkv"], a["D"], a["dt"], a["B"], a["topk"], a["causal"])
+    return _lib.lib.moba_attn_fwd_gate(q, FAKE, FAKE, a["b"], a["S"], a["Hq"], a["Hkv"], a["D"], a["dt"], a["B"],
+                                       a["topk"], a["causal"], gate_kind, out, None, FAKE, wsb, None)
+
+
+def test_gate_kind_entry_point_rejects_bad_arguments():
+    assert _lib.GATE_KINDS == {"mean": 0, "minmax": 1}
+    assert call_fwd_gate(2) == SHAPE
+    assert call_fwd_gate(-1) == SHAPE
+    for kind in (0, 1):
+        assert call_fwd_gate(kind, q=None) == NULL
+        assert call_fwd_gate(kind, out=FAKE + 4) == ALIGN
+        assert call_fwd_gate(kind, S=1000) == SEQ
+        assert call_fwd_gate(kind, topk=0) == TOPK
+    L = _lib.lib
+    assert L.moba_minmaxpool(None, 1, 1024, 2, 128, BF16, 128, FAKE, None) == NULL
+    assert L.moba_minmaxpool(FAKE, 1, 1000, 2, 128, BF16, 128, FAKE, None) == SEQ
+    assert L.moba_minmaxpool(FAKE, 1, 1024, 2, 128, BF16, 128, FAKE + 4, None) == ALIGN
+
+
+def test_python_binding_rejects_unknown_gate():
+    with pytest.raises(ValueError):
+        M.moba_attn_fwd(torch.zeros(1), torch.zeros(1), torch.zeros(1), 128, 3, gate="max")

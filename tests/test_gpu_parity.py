@@ -31,13 +31,13 @@ def small(name, dtype, b, S, Hq, Hkv, D, B, topk, causal=True, seed=7):
     return W.Workload(name, dtype, b, Hq, Hkv, S, D, B, topk, causal=causal, seed=seed)
 
 
-def run(w: W.Workload, rows=None, device_inputs=False):
-    say(f"[case] {w}")
+def run(w: W.Workload, rows=None, device_inputs=False, gate="mean"):
+    say(f"[case] {w} gate={gate}")
     q, k, v, _ = W.make_inputs(w, device=DEV if device_inputs else "cpu")
     q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
-    out, sel = M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal)
+    out, sel = M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal, gate=gate)
     torch.cuda.synchronize()
-    rep = compare(q, k, v, out, sel, w.block_size, w.topk, w.causal, rows=rows, tol=TOL[w.dtype])
+    rep = compare(q, k, v, out, sel, w.block_size, w.topk, w.causal, rows=rows, tol=TOL[w.dtype], gate=gate)
     say(f"[parity] {w.name}: {rep.as_dict()}")
     return rep, (q, k, v, out, sel)
 
@@ -62,6 +62,23 @@ def test_meanpool_matches_oracle(dtype, b, S, Hkv, D, B):
     gam = (B + 2) * u / (1 - (B + 2) * u)
     err = np.abs(mu.cpu().numpy().astype(np.float64) - ref)
     assert np.all(err <= gam * absmean + 1e-30), float((err - gam * absmean).max())
+
+
+@pytest.mark.parametrize("dtype,b,S,Hkv,D,B", [
+    ("bf16", 1, 2048, 2, 128, 256), ("bf16", 2, 1536, 3, 128, 96), ("f32", 1, 1024, 1, 64, 128),
+    ("f32", 1, 512, 2, 128, 16), ("bf16", 1, 8192, 8, 128, 1024),
+])
+def test_minmaxpool_matches_oracle(dtype, b, S, Hkv, D, B):
+    """Element-wise block min / max: input values, so bit-exact."""
+    w = small("mm", dtype, b, S, Hkv, Hkv, D, B, 1, seed=5)
+    say(f"[case] minmaxpool {w}")
+    _, k, _, _ = W.make_inputs(w, device="cpu")
+    lohi = M.moba_minmaxpool(k.to(DEV), B)
+    torch.cuda.synchronize()
+    lo, hi = O.block_minmax(to_np32(k), B)
+    got = lohi.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got[:, :, :, 0], lo)
+    assert np.array_equal(got[:, :, :, 1], hi)
 
 
 @pytest.mark.parametrize("dtype,S,Hq,Hkv,D,B,topk,causal", [
@@ -123,6 +140,48 @@ SMALL = [
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_forward_small(w):
     run(w)
+
+
+# min/max gate: the bf16 MFMA gate over several score tiles (ragged last
+# tile, each list capacity), non-causal, batch 2, and the fp32 VALU gate
+SMALL_MINMAX = [
+    small("mm_gqa_s2k", "bf16", 1, 2048, 4, 2, 128, 256, 3),
+    small("mm_n50_k9", "bf16", 1, 2400, 4, 2, 128, 48, 9),
+    small("mm_n96_k12", "bf16", 1, 6144, 4, 1, 128, 64, 12),
+    small("mm_n64_k20", "bf16", 1, 4096, 2, 2, 128, 64, 20),
+    small("mm_topk2_b16", "bf16", 1, 512, 2, 2, 128, 16, 2),
+    small("mm_batch2", "bf16", 2, 1024, 2, 2, 128, 128, 3),
+    small("mm_noncausal_n40", "bf16", 1, 2560, 2, 1, 128, 64, 6, causal=False),
+    small("mm_f32_d128_gqa", "f32", 1, 1024, 4, 2, 128, 128, 3),
+    small("mm_f32_d64_k20", "f32", 1, 2048, 2, 1, 64, 32, 20),
+    small("mm_f32_noncausal", "f32", 1, 512, 2, 1, 64, 64, 3, causal=False),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_MINMAX, ids=[w.name for w in SMALL_MINMAX])
+def test_forward_minmax_small(w):
+    run(w, gate="minmax")
+
+
+def test_forward_minmax_gqa32x8_32k_sampled():
+    """Min/max gate at 32K, 32 query / 8 KV heads, 128-key blocks, top-12
+    (a selective configuration with 256 candidate blocks)."""
+    w = small("mm_32k", "bf16", 1, 32768, 32, 8, 128, 128, 12, seed=21)
+    rng = np.random.default_rng(5)
+    rows = [(0, int(t), h) for h in range(32) for t in rng.integers(0, 32768, 16)]
+    run(w, rows=rows, device_inputs=True, gate="minmax")
+
+
+def test_forward_minmax_differs_from_mean():
+    """The two gates are different selections on the same input (so the
+    entry point does not silently run the mean gate)."""
+    w = small("mm_vs_mean", "bf16", 1, 4096, 2, 1, 128, 64, 4, seed=9)
+    q, k, v, _ = W.make_inputs(w, device="cpu")
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    _, s_mean = M.moba_attn_fwd(q, k, v, 64, 4, True, gate="mean")
+    _, s_mm = M.moba_attn_fwd(q, k, v, 64, 4, True, gate="minmax")
+    torch.cuda.synchronize()
+    assert not torch.equal(s_mean, s_mm)
 
 
 def test_forward_dense_equals_sdpa():
