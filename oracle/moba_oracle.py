@@ -42,6 +42,12 @@ Readings where the pages leave a step open (each listed in the design notes):
   * non-causal mode (causal = False): no future mask, no forced block, plain
     top-k over all n blocks, no mask inside blocks.
 
+Decode (decode_rows): one new query per sequence, at position t = L - 1 of
+a cache of L keys and values, is routed and attended exactly as prefill row t
+(the pages leave sparse decode open, report §6.3; this is the plainest
+reading): its own block j = t // B is cut at t, the past blocks 0..j-1 are
+complete and ranked by their mean keys.
+
 Gate variant (report §1.3 and §5: Quest is placed in the family as MoBA with
 small blocks and min/max pooling of the block's keys):
   * gate = "minmax": block i is summarised by the element-wise minimum lo_i
@@ -226,6 +232,58 @@ def moba_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_size: int,
         out[bb, t, h] = res.out[r]
         sel_idx[bb, h, t] = res.sel[r]
     return out, sel_idx
+
+
+# ----------------------------------------------------------------------------
+# Decode: one new query per sequence against a cache of its keys and values
+# ----------------------------------------------------------------------------
+def decode_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, lens: Sequence[int],
+                block_size: int, topk: int, keep_scores: bool = False) -> "RowResult":
+    """Decode-time MoBA: for sequence b with L = lens[b] cached positions (the
+    new token's own key and value included), the new query q[b, h] sits at
+    position t = L - 1 and is routed exactly as prefill row t would be
+    (report §2.2 and §2.3): own block j = t // B (its keys jB..t), the top
+    min(k-1, j) of the complete past blocks 0..j-1 by <q, mean key>, ties to
+    the lower index, softmax over the union.  The pages evaluate MoBA with
+    full attention during generation (report §4.4, §5.1) and name sparse
+    decode as future work (report §6.3) without fixing its rule; this is the
+    prefill rule applied to the last row.
+
+    q: [batch, Hq, D]; k_cache, v_cache: [batch, Lmax, Hkv, D]; rows are
+    returned in (b, h) order, b-major."""
+    b, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    g = Hq // Hkv
+    B = block_size
+    scale = 1.0 / math.sqrt(D)
+    res = RowResult(b * Hq, D, topk)
+    for bb in range(b):
+        L = int(lens[bb])
+        if not 1 <= L <= k_cache.shape[1]:
+            raise ValueError(f"cache length {L} outside [1, {k_cache.shape[1]}]")
+        t = L - 1
+        j = t // B
+        for hk in range(Hkv):
+            k_head = np.asarray(k_cache[bb, :L, hk, :], dtype=np.float64)
+            v_head = np.asarray(v_cache[bb, :L, hk, :], dtype=np.float64)
+            mu = k_head[:j * B].reshape(j, B, D).mean(axis=1)  # the complete past blocks
+            for h in range(hk * g, (hk + 1) * g):
+                r = bb * Hq + h
+                q64 = np.asarray(q[bb, h], dtype=np.float64)
+                scores = mu @ q64
+                sel = select_blocks(np.concatenate([scores, [0.0]]), j, topk, True)
+                res.out[r] = _attend_blocks(q64, k_head, v_head, sel, t, B, True, scale)
+                res.sel[r, :len(sel)] = sel
+                if keep_scores:
+                    res.scores[r] = scores
+                m = min(topk - 1, j)
+                if 0 < m < j:
+                    ranked = sorted(range(j), key=lambda i: (-float(scores[i]), i))
+                    res.gap[r] = float(scores[ranked[m - 1]] - scores[ranked[m]])
+                    res.boundary[r] = (scores[ranked[m - 1]], scores[ranked[m]])
+                absk = np.abs(k_head[:j * B]).reshape(j, B, D).mean(axis=1)
+                res.score_eps[r] = score_error_bound(q64, mu, absk, B) if j else 0.0
+    return res
 
 
 class RowResult:

@@ -563,3 +563,109 @@ def test_planted_swapped_minmax_bounds_are_caught(monkeypatch):
                         lambda q, lo, hi: np.minimum(lo * q, hi * q).sum(axis=1))
     with pytest.raises(AssertionError):
         test_minmax_score_is_the_largest_logit_over_the_box()
+
+
+# ----------------------------------------------------------------------------
+# decode: one new query per sequence against its cache (prefill rule at t = L-1)
+# ----------------------------------------------------------------------------
+def _decode_case(rng, b, Lmax, Hq, Hkv, D):
+    q = rng.standard_normal((b, Hq, D))
+    kc = rng.standard_normal((b, Lmax, Hkv, D))
+    vc = rng.standard_normal((b, Lmax, Hkv, D))
+    return q, kc, vc
+
+
+@pytest.mark.parametrize("lens,B,topk,Hq,Hkv", [
+    ([1, 7, 16, 17], 16, 3, 2, 1), ([64, 63, 48, 33], 16, 2, 4, 2), ([80, 95, 96, 5], 16, 4, 2, 2),
+    ([40, 41], 8, 20, 2, 1),
+])
+def test_decode_equals_prefill_last_row_with_any_future(lens, B, topk, Hq, Hkv):
+    """Decode at cache length L is prefill row L-1 of a sequence padded to a
+    whole number of blocks with arbitrary keys and values after L-1."""
+    rng = np.random.default_rng(sum(lens) + B)
+    b, D, Lmax = len(lens), 8, 96
+    q, kc, vc = _decode_case(rng, b, Lmax, Hq, Hkv, D)
+    res = O.decode_rows(q, kc, vc, lens, B, topk)
+    for bb, L in enumerate(lens):
+        S = -(-L // B) * B
+        qp = rng.standard_normal((1, S, Hq, D))
+        qp[0, L - 1] = q[bb]
+        kp = rng.standard_normal((1, S, Hkv, D)) * 5.0
+        vp = rng.standard_normal((1, S, Hkv, D)) * 5.0
+        kp[0, :L], vp[0, :L] = kc[bb, :L], vc[bb, :L]
+        pre = O.moba_rows(qp, kp, vp, B, topk, True, [(0, L - 1, h) for h in range(Hq)])
+        for h in range(Hq):
+            r = bb * Hq + h
+            assert np.array_equal(res.sel[r], pre.sel[h])
+            np.testing.assert_allclose(res.out[r], pre.out[h], rtol=0, atol=1e-12)
+
+
+def test_decode_dense_and_own_block_only_match_sdpa():
+    """topk >= number of blocks: softmax over all L cached keys; topk = 1: over
+    the own block's keys jB..L-1 only (torch fp64 SDPA, one query)."""
+    rng = np.random.default_rng(4)
+    b, Lmax, Hq, Hkv, D, B = 3, 64, 4, 2, 8, 8
+    q, kc, vc = _decode_case(rng, b, Lmax, Hq, Hkv, D)
+    lens = [64, 37, 9]
+    dense = O.decode_rows(q, kc, vc, lens, B, 8)
+    own = O.decode_rows(q, kc, vc, lens, B, 1)
+    for bb, L in enumerate(lens):
+        j = (L - 1) // B
+        for res, lo in ((dense, 0), (own, j * B)):
+            ref = sdpa_fp64(q[bb][None, None], kc[bb, lo:L][None], vc[bb, lo:L][None])[0, 0]
+            np.testing.assert_allclose(res.out[bb * Hq:(bb + 1) * Hq], ref, rtol=0, atol=1e-12)
+        assert all(own.sel[bb * Hq + h].tolist() == [j] for h in range(Hq))
+
+
+def test_decode_never_reads_past_the_cache_length():
+    """Cache entries at positions >= L (stale or unwritten) never change the
+    result: a decode that attended the own block in full would fail this."""
+    rng = np.random.default_rng(12)
+    b, Lmax, Hq, Hkv, D, B = 2, 48, 2, 1, 8, 16
+    q, kc, vc = _decode_case(rng, b, Lmax, Hq, Hkv, D)
+    lens = [21, 40]
+    ref = O.decode_rows(q, kc, vc, lens, B, 2)
+    kc2, vc2 = kc.copy(), vc.copy()
+    for bb, L in enumerate(lens):
+        kc2[bb, L:] = 100.0
+        vc2[bb, L:] = -100.0
+    got = O.decode_rows(q, kc2, vc2, lens, B, 2)
+    assert np.array_equal(got.out, ref.out) and np.array_equal(got.sel, ref.sel)
+
+
+def test_decode_selection_by_brute_force():
+    """The chosen past blocks maximise the summed mean-key score among all
+    min(k-1, j)-subsets of the complete blocks (explicit loops), ties to the
+    lexicographically smallest subset."""
+    rng = np.random.default_rng(21)
+    b, Lmax, Hq, Hkv, D, B, topk = 2, 80, 2, 1, 4, 8, 4
+    q, kc, vc = _decode_case(rng, b, Lmax, Hq, Hkv, D)
+    lens = [80, 53]
+    res = O.decode_rows(q, kc, vc, lens, B, topk)
+    for bb, L in enumerate(lens):
+        j = (L - 1) // B
+        for h in range(Hq):
+            score = []
+            for i in range(j):
+                s = 0.0
+                for d in range(D):
+                    tot = 0.0
+                    for x in range(B):
+                        tot += kc[bb, i * B + x, 0, d]
+                    s += q[bb, h, d] * (tot / B)
+                score.append(s)
+            best, best_set = None, None
+            for sub in itertools.combinations(range(j), min(topk - 1, j)):
+                val = sum(score[i] for i in sub)
+                if best is None or val > best + 1e-12:
+                    best, best_set = val, sub
+            want = list(best_set) + [j] + [-1] * (topk - 1 - len(best_set))
+            assert res.sel[bb * Hq + h].tolist() == want
+
+
+def test_decode_rejects_bad_lengths():
+    rng = np.random.default_rng(1)
+    q, kc, vc = _decode_case(rng, 1, 32, 2, 1, 4)
+    for L in (0, 33):
+        with pytest.raises(ValueError):
+            O.decode_rows(q, kc, vc, [L], 8, 2)
