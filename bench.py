@@ -269,6 +269,44 @@ def summarize_traffic(fetch_dir, write_dir, calib_mib, out_path):
     return res
 
 
+DECODE_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_decode -o run -- "
+                    "python3 -u bench.py --decode --decode-skip-dense --steps 20 --warmup 3 --no-cpu-baseline "
+                    "> gpurun_out/trace_decode.json")
+
+
+def summarize_decode_trace(trace_dir, bench_json, out_path):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of
+    bench.py --decode, with bench.py's own HIP-event average for the decode
+    attention kernel."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = list(csv.DictReader(open(f)))
+    line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    m = line["moba"]
+    cfg = line["config"]
+    out = [f"# Kernel trace: MoBA decode, {cfg['workload']} workload ({cfg['batch']} sequences of up to "
+           f"{cfg['max_len']} cached positions, {cfg['num_q_heads']}/{cfg['num_kv_heads']} heads, D {cfg['head_dim']}, "
+           f"block {cfg['block_size']}, top-{cfg['topk']})",
+           "", "Command (run from the repository root on one MI355X):", "", "```", DECODE_TRACE_CMD, "```", "",
+           f"{line['warmup'] + line['steps']} decode calls ({line['warmup']} untimed + {line['steps']} timed).",
+           "", "| Kernel | Calls | Total ns | Average ns | % | Min ns | Max ns |", "|---|---|---|---|---|---|---|"]
+    for r in rows[:12]:
+        name = r["Name"] if len(r["Name"]) < 72 else r["Name"][:69] + "..."
+        out.append(f"| {name} | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.0f} | "
+                   f"{float(r['Percentage']):.2f} | {r['MinNs']} | {r['MaxNs']} |")
+    att = [r for r in rows if "decode_attn_kernel" in r["Name"]][0]
+    by = m["bytes_per_step"]
+    out += ["", f"bench.py in the same run, HIP events around each decode attention launch on its stream: average "
+                f"{m['attn_kernel_ms']:.3f} ms (rocprofv3: {float(att['AverageNs']) / 1e6:.3f} ms); algorithmic bytes "
+                f"{by['attn_kernel'] / 1e9:.3f} GB per launch (the chosen blocks' K and V, each block read once per "
+                f"KV-head group, plus queries and partials) = {m['attn_kernel_gbs']:.0f} GB/s, "
+                f"{100 * line['roofline']['frac']:.1f}% of the 8000 GB/s HBM peak.",
+            f"Step: {line['ms_per_step']:.3f} ms, {line['value']:.0f} sequences decoded per second."]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+
+
 def summarize_trace(trace_dir, bench_json, out_path):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run of bench.py,
     with bench.py's own HIP-event average for the past-block kernel."""
@@ -343,6 +381,129 @@ def curve(M, W, lengths, log, budget_s=4.0):
     return out_lines
 
 
+def decode_bytes(w, sel, lens, chunk):
+    """Algorithmic HBM bytes of one decode step, from the step's own selection:
+    per (sequence, KV head) the union of the group's chosen blocks is read once
+    (K and V; the own block up to the new token), plus the queries, the gate's
+    cached means of the complete past blocks, the output, and the attention
+    kernel's partials (written once, read once by the merge)."""
+    import numpy as np
+    elt = 2 if w.dtype == "bf16" else 4
+    B, D, g = w.block_size, w.head_dim, w.num_q_heads // w.num_kv_heads
+    nchunk = -(-B // chunk)
+    kv = gate = partial = 0
+    for bb, L in enumerate(lens):
+        j = (L - 1) // B
+        for hk in range(w.num_kv_heads):
+            blocks = set(int(i) for i in np.unique(sel[bb, hk * g:(hk + 1) * g]) if i >= 0)
+            for i in blocks:
+                keys = B if i < j else L - j * B
+                kv += keys * D * elt * 2
+            gate += j * D * 4
+        for h in range(w.num_q_heads):
+            for i in sel[bb, h]:
+                if i < 0:
+                    continue
+                keys = B if i < j else L - j * B
+                partial += -(-keys // chunk) * (D + 2) * 4
+    qo = w.batch * w.num_q_heads * D * elt * 2
+    return {"kv": kv, "gate": gate, "partials": partial, "q_out": qo,
+            "attn_kernel": kv + partial + w.batch * w.num_q_heads * D * elt,
+            "total": kv + gate + 2 * partial + qo, "nchunk": nchunk}
+
+
+def measure_decode(M, W, w, steps, warmup, log, cpu_seconds=0.0, dense=True):
+    """One decode step per call for every sequence of the batch (cache
+    lengths fixed across steps), then the same caches decoded densely by this
+    library (block_size = max_len, topk = 1: one causal block of L keys)."""
+    import numpy as np
+    import torch
+    t0 = time.perf_counter()
+    q, kc, vc, lens = W.make_decode_inputs(w, device="cuda")
+    dt = M.DTYPE_BF16 if w.dtype == "bf16" else M.DTYPE_F32
+    res = {"workload": w.name}
+    for tag, B, k in (("moba", w.block_size, w.topk), ("dense", w.max_len, 1))[:2 if dense else 1]:
+        mu = M.moba_decode_means(kc, lens, B)
+        out = torch.empty_like(q)
+        sel = torch.empty((w.batch, w.num_q_heads, k), dtype=torch.int32, device="cuda")
+        ws = torch.empty(M.decode_workspace_bytes(w.batch, w.max_len, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                                  dt, B, k), dtype=torch.uint8, device="cuda")
+        call = lambda: M.moba_decode_fwd(q, kc, vc, mu, lens, B, k, out=out, sel_idx=sel, workspace=ws)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        log(f"[decode] {tag}: inputs and warmup in {time.perf_counter() - t0:.1f}s")
+        M.profile_read()
+        M.profile_enable(True)
+        torch.cuda.synchronize()
+        ts = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - ts
+        M.profile_enable(False)
+        st = M.profile_read()
+        ms = el / steps * 1e3
+        wb = W.DecodeWorkload(w.name, w.dtype, w.num_q_heads, w.num_kv_heads, w.max_len, w.head_dim, B, k, w.lens)
+        by = decode_bytes(wb, sel.cpu().numpy(), list(w.lens), M.DECODE_CHUNK)
+        attn = st["decode_attn"]
+        attn_ms = attn["ms"] / max(attn["launches"], 1)
+        res[tag] = {"block_size": B, "topk": k, "ms_per_step": ms, "steps": steps,
+                    "tokens_per_s": w.batch / (ms * 1e-3), "bytes_per_step": by,
+                    "hbm_gbs_step": by["total"] / (ms * 1e-3) / 1e9,
+                    "attn_kernel_ms": attn_ms, "attn_kernel_gbs": by["attn_kernel"] / (attn_ms * 1e-3) / 1e9,
+                    "stages_ms": {n: x["ms"] / steps for n, x in st.items() if x["launches"]}}
+        log(f"[decode] {tag}: {ms:.3f} ms/step, attention kernel {attn_ms:.3f} ms "
+            f"({res[tag]['attn_kernel_gbs']:.0f} GB/s)")
+        del out, sel, ws, mu
+        torch.cuda.empty_cache()
+    moba = res["moba"]
+    line = {
+        "metric": "MoBA decode step: sequences decoded per second (one new token each)",
+        "value": moba["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": moba["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1), bf16-rounded caches; no dataset)",
+        "config": {"workload": w.name, "batch": w.batch, "max_len": w.max_len, "cache_lens": list(w.lens),
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "topk": w.topk},
+        "moba": moba, "dense": res.get("dense"),
+        "speedup_vs_dense": res["dense"]["ms_per_step"] / moba["ms_per_step"] if dense else None,
+        "roofline": {"bound": "hbm", "kernel": "moba::decode_attn_kernel<unsigned short, 128>",
+                     "achieved": moba["attn_kernel_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": moba["attn_kernel_gbs"] / PEAK_HBM_GBS, "traffic": None},
+    }
+    if cpu_seconds > 0:
+        import oracle.moba_oracle as O
+        qh = q.cpu()
+        kh, vh = kc[0].cpu(), vc[0].cpu()  # sequence 0 only
+
+        class Src:
+            def __init__(self, t):
+                self.t, self.shape = t, (1,) + tuple(t.shape)
+
+            def __getitem__(self, idx):
+                return self.t[idx[1:]].to(torch.float64).numpy()
+
+        g = w.num_q_heads // w.num_kv_heads
+        done, tsum = 0, 0.0
+        for hk in range(w.num_kv_heads):
+            if tsum >= cpu_seconds:
+                break
+            rows = [(0, h) for h in range(hk * g, (hk + 1) * g)]
+            ts = time.perf_counter()
+            O.decode_rows(qh[:1].to(torch.float64).numpy(), Src(kh), Src(vh), [w.lens[0]], w.block_size,
+                          w.topk, rows=rows)
+            tsum += time.perf_counter() - ts
+            done += len(rows)
+        line["cpu_baseline"] = {"value": done / w.num_q_heads / tsum, "unit": "tokens/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"fp64 numpy oracle decode_rows on sequence 0: {done} of its "
+                                          f"{w.num_q_heads} heads in {tsum:.1f}s (per-KV-head fp64 conversion "
+                                          f"of the cached prefix and its block means included); value = "
+                                          f"sequences per second at that rate"}
+    return line
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +517,12 @@ def main():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--gate", choices=("mean", "minmax"), default="mean",
                     help="block gate: block means (the method's) or element-wise key min / max")
+    ap.add_argument("--decode", nargs="?", const="decode_gqa32x8_1m_b8", default=None, metavar="WORKLOAD",
+                    help="measure decode-time MoBA on a decode workload instead, then exit")
+    ap.add_argument("--decode-skip-dense", action="store_true",
+                    help="with --decode: skip the dense-decode comparison")
+    ap.add_argument("--summarize-decode-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="write the decode kernel-trace summary from a rocprofv3 --stats run, then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain copy of MIB MiB first (reference dispatch for HBM byte counters)")
     ap.add_argument("--curve", nargs="*", type=int, metavar="SEQLEN",
@@ -367,6 +534,10 @@ def main():
     args = ap.parse_args()
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic, 1024, TRAFFIC_FILE), indent=1))
+        return
+    if args.summarize_decode_trace:
+        summarize_decode_trace(*args.summarize_decode_trace,
+                               os.path.join(ROOT, "profiles", "kernel_trace_decode_gqa32x8_1m_b8.md"))
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, os.path.join(ROOT, "profiles", "kernel_trace_gqa32x8_1m.md"))
@@ -389,6 +560,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.decode:
+        print(json.dumps(measure_decode(M, W, W.DECODE_WORKLOADS[args.decode], args.steps, args.warmup, log,
+                                        0.0 if args.no_cpu_baseline else min(args.cpu_seconds, 10.0),
+                                        dense=not args.decode_skip_dense)),
+              flush=True)
+        return
     if args.curve is not None:
         curve(M, W, args.curve or [32768, 65536, 131072, 262144, 524288, 1048576], log)
         return

@@ -5,11 +5,17 @@ include/moba.h (libmoba.so, built in-tree); this package is a thin binding.
 """
 from ._lib import (  # noqa: F401
     DTYPE_BF16,
+    DECODE_CHUNK,
     DTYPE_F32,
     GATE_KINDS,
     LIB_PATH,
+    MAX_DECODE_GROUP,
+    MAX_DECODE_TOPK,
     MAX_SELECTIVE_TOPK,
     MobaError,
+    decode_workspace_bytes,
+    moba_decode_fwd,
+    moba_decode_means,
     moba_attn_fwd,
     moba_gate,
     moba_meanpool,

@@ -36,6 +36,11 @@ SIGNATURES = {
     "moba_meanpool": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p]),
     "moba_gate": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                  _c_i32, _c_p, _c_p]),
+    "moba_decode_workspace_bytes": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                   _c_i32, ctypes.POINTER(_c_sz)]),
+    "moba_decode_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                       _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "moba_decode_means": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p]),
     "moba_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "moba_profile_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_i64),
                                          ctypes.POINTER(ctypes.c_double), _c_i32]),
@@ -44,7 +49,8 @@ SIGNATURES = {
 # gate kinds (enum moba_gate_kind)
 GATE_KINDS = {"mean": 0, "minmax": 1}
 
-STAGES = ("meanpool", "gate", "dispatch", "attn_past", "attn_own", "attn_f32", "kv_layout")
+STAGES = ("meanpool", "gate", "dispatch", "attn_past", "attn_own", "attn_f32", "kv_layout",
+          "decode_gate", "decode_attn", "decode_merge")
 
 
 class MobaError(RuntimeError):
@@ -208,3 +214,71 @@ def moba_gate(q: torch.Tensor, mu: torch.Tensor, block_size: int, topk: int, cau
     if st != MOBA_OK:
         raise MobaError(st, "moba_gate")
     return sel_idx
+
+
+MAX_DECODE_TOPK = 64
+MAX_DECODE_GROUP = 16
+DECODE_CHUNK = 512  # keys per decode attention work-group (one partial per head, slot and chunk)
+
+
+def decode_workspace_bytes(batch: int, max_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           dtype: int, block_size: int, topk: int) -> int:
+    out = _c_sz(0)
+    st = lib.moba_decode_workspace_bytes(batch, max_len, num_q_heads, num_kv_heads, head_dim, dtype, block_size,
+                                         topk, ctypes.byref(out))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_decode_workspace_bytes")
+    return int(out.value)
+
+
+def moba_decode_means(k_cache: torch.Tensor, cache_lens: torch.Tensor, block_size: int,
+                      mu_cache: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Mean key of every complete block of every cached sequence:
+    mu_cache [b, Hkv, max_len / block_size, D] fp32 (entries of incomplete or
+    unused blocks are left as they are; a new tensor starts at zero)."""
+    _check_dev(k_cache, cache_lens)
+    b, Lmax, Hkv, D = k_cache.shape
+    if cache_lens.dtype != torch.int32 or cache_lens.numel() != b:
+        raise ValueError("cache_lens must be int32 [batch]")
+    if mu_cache is None:
+        mu_cache = torch.zeros((b, Hkv, Lmax // max(block_size, 1), D), dtype=torch.float32, device=k_cache.device)
+    st = lib.moba_decode_means(k_cache.data_ptr(), cache_lens.data_ptr(), b, Lmax, Hkv, D, _dtype_code(k_cache),
+                               block_size, mu_cache.data_ptr(), _stream_ptr(k_cache.device))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_decode_means")
+    return mu_cache
+
+
+def moba_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, mu_cache: torch.Tensor,
+                    cache_lens: torch.Tensor, block_size: int, topk: int, out: Optional[torch.Tensor] = None,
+                    sel_idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    return_sel: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One MoBA decode step.  q [b, Hq, D]; k_cache / v_cache [b, max_len,
+    Hkv, D]; mu_cache fp32 [b, Hkv, max_len / block_size, D] (moba_decode_means,
+    kept current by this call); cache_lens int32 [b] (the new token included).
+    Returns (out [b, Hq, D], sel_idx [b, Hq, topk] int32 or None)."""
+    _check_dev(q, k_cache, v_cache, mu_cache, cache_lens)
+    b, Hq, D = q.shape
+    _, Lmax, Hkv, _ = k_cache.shape
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or k_cache.shape != v_cache.shape:
+        raise ValueError("q and the caches must share dtype; k_cache and v_cache must share shape")
+    if cache_lens.dtype != torch.int32 or cache_lens.numel() != b:
+        raise ValueError("cache_lens must be int32 [batch]")
+    if mu_cache.dtype != torch.float32 or tuple(mu_cache.shape) != (b, Hkv, Lmax // max(block_size, 1), D):
+        raise ValueError("mu_cache must be fp32 [batch, Hkv, max_len / block_size, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    if sel_idx is None and return_sel:
+        sel_idx = torch.empty((b, Hq, topk), dtype=torch.int32, device=q.device)
+    nbytes = decode_workspace_bytes(b, Lmax, Hq, Hkv, D, dt, block_size, topk)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check_dev(out, workspace)
+    st = lib.moba_decode_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), mu_cache.data_ptr(),
+                             cache_lens.data_ptr(), b, Lmax, Hq, Hkv, D, dt, block_size, topk, out.data_ptr(),
+                             sel_idx.data_ptr() if sel_idx is not None else None, workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_decode_fwd")
+    return out, sel_idx

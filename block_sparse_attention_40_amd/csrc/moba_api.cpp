@@ -51,7 +51,7 @@ struct StageScope {
     if (g_prof.on) {
       std::lock_guard<std::mutex> lk(g_prof.mu);
       a = g_prof.get();
-      if (a) hipEventRecord(a, s);
+      if (a) (void)hipEventRecord(a, s);
     }
   }
   ~StageScope() {
@@ -59,7 +59,7 @@ struct StageScope {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     hipEvent_t b = g_prof.get();
     if (!b) return;
-    hipEventRecord(b, s);
+    (void)hipEventRecord(b, s);
     g_prof.recs.push_back(ProfRec{stage, a, b, work});
   }
 };
@@ -71,6 +71,51 @@ double past_blocks_sum(const Plan& p, int64_t t0, int64_t cnt) {
   for (int64_t jb = t0 / B; jb < (t0 + cnt) / B; ++jb)
     tot += (double)B * (double)(p.s.causal ? (jb < p.kp ? jb : p.kp) : p.kp);
   return tot;
+}
+
+// Decode: sizes, limits and the workspace carve-up.
+struct DecodePlan {
+  int64_t nmax;
+  int32_t g, U, nchunk;
+  size_t off_sc, off_uni, off_uslot, off_ucount, off_sel, off_po, off_pml, off_ksum, total;
+};
+
+int make_decode_plan(int64_t batch, int64_t lmax, int32_t hq, int32_t hkv, int32_t d, int32_t dtype, int32_t block,
+                     int32_t topk, DecodePlan* p) {
+  if (dtype != MOBA_DTYPE_F32 && dtype != MOBA_DTYPE_BF16) return MOBA_ERR_DTYPE;
+  if (batch < 1 || lmax < 1 || hq < 1 || hkv < 1 || block < 1 || d < 1) return MOBA_ERR_SHAPE;
+  if (dtype == MOBA_DTYPE_BF16 && d != 128) return MOBA_ERR_HEAD_DIM;
+  if (dtype == MOBA_DTYPE_F32 && d != 64 && d != 128) return MOBA_ERR_HEAD_DIM;
+  if (hq % hkv != 0 || hq / hkv > kDecodeMaxGroup) return MOBA_ERR_GQA;
+  if (topk < 1 || topk > kDecodeMaxTopk) return MOBA_ERR_TOPK;
+  if (lmax % block != 0) return MOBA_ERR_SEQ_NOT_DIVISIBLE;
+  DecodePlan q{};
+  q.nmax = lmax / block;
+  q.g = hq / hkv;
+  q.U = q.g * topk;
+  q.nchunk = (block + kDecodeChunk - 1) / kDecodeChunk;
+  // grid limits: (batch * hkv, nchunk, U), (hkv, batch), (hq, batch)
+  if (q.nmax > kDecodeMaxBlocks || batch > 65535 || q.nchunk > 65535 || batch * hkv > (int64_t(1) << 31) - 1 ||
+      lmax > (int64_t(1) << 31) - 1)
+    return MOBA_ERR_SHAPE;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  const size_t rows = (size_t)batch * hq;
+  q.off_sc = take(rows * q.nmax * sizeof(float));
+  q.off_uni = take((size_t)batch * hkv * q.U * sizeof(int32_t));
+  q.off_uslot = take((size_t)batch * hkv * q.U * q.g * sizeof(int32_t));
+  q.off_ucount = take((size_t)batch * hkv * sizeof(int32_t));
+  q.off_sel = take(rows * topk * sizeof(int32_t));
+  q.off_po = take(rows * topk * q.nchunk * (size_t)d * sizeof(float));
+  q.off_pml = take(rows * topk * q.nchunk * 2 * sizeof(float));
+  q.off_ksum = take((size_t)batch * hkv * q.nchunk * (size_t)d * sizeof(float));
+  q.total = off;
+  *p = q;
+  return MOBA_OK;
 }
 
 float scale_log2_for(int d) {
@@ -344,6 +389,81 @@ int moba_gate(const void* q, const float* mu, int64_t batch, int64_t seqlen, int
     ga.causal = causal ? 1 : 0; ga.g = p.g; ga.gate_t = p.gate_t; ga.bb = (int32_t)bb;
     if (launch_gate(ga, dtype, head_dim, reinterpret_cast<hipStream_t>(stream))) return MOBA_ERR_HIP;
   }
+  return MOBA_OK;
+}
+
+int moba_decode_workspace_bytes(int64_t batch, int64_t max_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t dtype, int32_t block_size, int32_t topk, size_t* bytes) {
+  if (!bytes) return MOBA_ERR_NULL;
+  DecodePlan p;
+  const int st = make_decode_plan(batch, max_len, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk, &p);
+  if (st != MOBA_OK) return st;
+  *bytes = p.total;
+  return MOBA_OK;
+}
+
+int moba_decode_fwd(const void* q, const void* k_cache, const void* v_cache, float* mu_cache,
+                    const int32_t* cache_lens, int64_t batch, int64_t max_len, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype, int32_t block_size, int32_t topk,
+                    void* out, int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan p;
+  const int st = make_decode_plan(batch, max_len, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk, &p);
+  if (st != MOBA_OK) return st;
+  if (!q || !k_cache || !v_cache || !mu_cache || !cache_lens || !out) return MOBA_ERR_NULL;
+  if (!workspace || workspace_bytes < p.total) return MOBA_ERR_WORKSPACE;
+  if (misaligned(q) || misaligned(k_cache) || misaligned(v_cache) || misaligned(mu_cache) || misaligned(out) ||
+      misaligned(workspace) || (reinterpret_cast<uintptr_t>(cache_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(sel_idx) & 3u))
+    return MOBA_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  DecodeArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.mu = mu_cache; a.lens = cache_lens;
+  a.sel = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(ws + p.off_sel);
+  a.sc = reinterpret_cast<float*>(ws + p.off_sc);
+  a.uni = reinterpret_cast<int32_t*>(ws + p.off_uni);
+  a.uslot = reinterpret_cast<int32_t*>(ws + p.off_uslot);
+  a.ucount = reinterpret_cast<int32_t*>(ws + p.off_ucount);
+  a.po = reinterpret_cast<float*>(ws + p.off_po);
+  a.pml = reinterpret_cast<float*>(ws + p.off_pml);
+  a.ksum = reinterpret_cast<float*>(ws + p.off_ksum);
+  a.out = out;
+  a.batch = batch; a.lmax = max_len; a.nmax = p.nmax;
+  a.hq = num_q_heads; a.hkv = num_kv_heads; a.g = p.g; a.d = head_dim; a.block = block_size; a.topk = topk;
+  a.U = p.U; a.nchunk = p.nchunk;
+  a.scale_log2 = scale_log2_for(head_dim);
+  // the bytes each stage reads depend on the cache lengths, which are device
+  // data: the stages record no work figure
+  // the mean of a block this token completes is formed by the attention and
+  // merge kernels (for the next call's gate; this call's gate reads the
+  // blocks before it)
+  {
+    StageScope sc(MOBA_STAGE_DECODE_GATE, s, 0.0);
+    if (launch_decode_stage(a, dtype, 0, s)) return MOBA_ERR_HIP;
+  }
+  {
+    StageScope sc(MOBA_STAGE_DECODE_ATTN, s, 0.0);
+    if (launch_decode_stage(a, dtype, 1, s)) return MOBA_ERR_HIP;
+  }
+  {
+    StageScope sc(MOBA_STAGE_DECODE_MERGE, s, 0.0);
+    if (launch_decode_stage(a, dtype, 2, s)) return MOBA_ERR_HIP;
+  }
+  return MOBA_OK;
+}
+
+int moba_decode_means(const void* k_cache, const int32_t* cache_lens, int64_t batch, int64_t max_len,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t dtype, int32_t block_size, float* mu_cache,
+                      void* stream) {
+  DecodePlan p;
+  const int st = make_decode_plan(batch, max_len, num_kv_heads, num_kv_heads, head_dim, dtype, block_size, 1, &p);
+  if (st != MOBA_OK) return st;
+  if (!k_cache || !cache_lens || !mu_cache) return MOBA_ERR_NULL;
+  if (misaligned(k_cache) || misaligned(mu_cache) || (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
+    return MOBA_ERR_ALIGN;
+  if (launch_decode_means(k_cache, cache_lens, mu_cache, dtype, batch, max_len, p.nmax, num_kv_heads, head_dim,
+                          block_size, reinterpret_cast<hipStream_t>(stream)))
+    return MOBA_ERR_HIP;
   return MOBA_OK;
 }
 

@@ -83,6 +83,37 @@ struct F32Args {
   float scale_log2;
 };
 
+// Decode (one new query per sequence against its cache).
+constexpr int kDecodeMaxGroup = 16;     // query heads per KV head
+constexpr int kDecodeMaxTopk = 64;
+constexpr int kDecodeMaxBlocks = 16384;  // cache capacity in blocks
+constexpr int kDecodeChunk = 512;        // keys per attention work-group (8 steps of 64)
+struct DecodeArgs {
+  const void* q;           // [batch, hq, d]
+  const void* k;           // [batch, lmax, hkv, d]
+  const void* v;
+  float* mu;               // [batch, hkv, nmax, d] means of the complete blocks (the merge
+                           // writes the mean of an own block the new token completes)
+  const int32_t* lens;     // [batch] cached positions, the new token included
+  int32_t* sel;            // [batch, hq, topk]
+  float* sc;               // [batch, hq, nmax] gate scores
+  int32_t* uni;            // [batch * hkv, U] the group's chosen blocks, ascending
+  int32_t* uslot;          // [batch * hkv, U, g] slot of a union entry in each head's row, or -1
+  int32_t* ucount;         // [batch * hkv] union sizes
+  float* po;               // [batch, hq, topk, nchunk, d] unnormalised partial outputs
+  float* pml;              // [batch, hq, topk, nchunk, 2] partial max (base 2) and sum
+  float* ksum;             // [batch * hkv, nchunk, d] key column sums of a completed own block
+  void* out;               // [batch, hq, d]
+  int64_t batch, lmax, nmax;
+  int32_t hq, hkv, g, d, block, topk, U, nchunk;
+  float scale_log2;
+};
+// stage 0: gate + top-k + union; 1: chunk attention; 2: merge
+int launch_decode_stage(const DecodeArgs& a, int dtype, int stage, hipStream_t stream);
+// Block means of every complete block of the cache.
+int launch_decode_means(const void* k, const int32_t* lens, float* mu, int dtype, int64_t batch, int64_t lmax,
+                        int64_t nmax, int hkv, int d, int block, hipStream_t stream);
+
 // K and V^T images of all 64-key slices (bf16 path, seqlen % 64 == 0).
 int launch_kv_image(const void* k, const void* v, int64_t batch, int64_t seqlen, int hkv, uint16_t* kimg,
                     uint16_t* vimg, hipStream_t stream);

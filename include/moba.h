@@ -165,6 +165,64 @@ int moba_gate(const void* q, const float* mu, int64_t batch, int64_t seqlen,
               int32_t* sel_idx, void* stream);
 
 /*
+ * Decode-time MoBA: one new query per sequence against its key/value cache.
+ * The pages evaluate generation with full attention and name sparse decode
+ * as future work (report §4.4, §6.3); here the new token of sequence b, at
+ * position t = L_b - 1 of a cache of L_b positions (its own key and value
+ * already appended), is routed and attended exactly as prefill row t
+ * (report §2.2, §2.3): own block j = t / B, cut at t; the best min(k-1, j)
+ * complete past blocks 0..j-1 by <q, mean key>, ties to the lower index;
+ * softmax over the union.
+ *
+ * Layouts (row-major, 16-byte aligned, dtype and head_dim as for
+ * moba_attn_fwd):
+ *   q          [batch, Hq, D]       the new tokens' queries
+ *   k_cache,   [batch, max_len, Hkv, D]  positions 0 .. L_b - 1 are read;
+ *   v_cache                         later positions are never touched
+ *   mu_cache   fp32 [batch, Hkv, max_len / B, D]  mean key of each complete
+ *              block (moba_decode_means fills it; see below)
+ *   cache_lens int32 [batch] on the device: L_b, the new token included
+ *   out        [batch, Hq, D]
+ *   sel_idx    int32 [batch, Hq, topk] or NULL: the chosen past blocks
+ *              ascending, then the own block j, then -1
+ * max_len must be a multiple of block_size with max_len / block_size <=
+ * 16384; Hq / Hkv <= 16; 1 <= topk <= 64.  A sequence whose L_b lies
+ * outside [1, max_len] gets a zero output row and a sel row of -1 (no
+ * memory is read for it).
+ */
+
+/* moba_decode_workspace_bytes: the device workspace moba_decode_fwd needs. */
+int moba_decode_workspace_bytes(int64_t batch, int64_t max_len, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                int32_t block_size, int32_t topk, size_t* bytes);
+
+/*
+ * moba_decode_fwd: one decode step for every sequence of the batch.  Reads
+ * mu_cache entries 0 .. j-1 of each sequence and, when L_b % block_size == 0
+ * (the new token completes block j), writes entry j: the cache of means stays
+ * current for the next step of a caller that appends one token per step.
+ * Stream-ordered on `stream`; no allocation, no host synchronisation.
+ * Errors as moba_attn_fwd (MOBA_ERR_SEQ_NOT_DIVISIBLE: max_len % block_size
+ * != 0); nothing is launched on an error.
+ */
+int moba_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
+                    float* mu_cache, const int32_t* cache_lens,
+                    int64_t batch, int64_t max_len, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                    int32_t block_size, int32_t topk, void* out, int32_t* sel_idx,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moba_decode_means: mu_cache[b, hk, i, :] = mean of block i's keys (fp32
+ * sum) for every complete block i < L_b / block_size of every sequence; other
+ * entries are left as they are.  Use it once after filling a cache (after a
+ * prefill, for instance); moba_decode_fwd keeps it current from then on.
+ */
+int moba_decode_means(const void* k_cache, const int32_t* cache_lens, int64_t batch,
+                      int64_t max_len, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t dtype, int32_t block_size, float* mu_cache, void* stream);
+
+/*
  * Measurement support (for benchmarks; not thread-safe).  While enabled, every
  * kernel launch made by the calls above is bracketed by two HIP events
  * recorded on the caller's stream, and the host adds the launch's
@@ -184,7 +242,10 @@ enum moba_stage {
   MOBA_STAGE_OWN = 4,       /* own block + merge: FLOPs */
   MOBA_STAGE_F32 = 5,       /* fp32 attention path: FLOPs */
   MOBA_STAGE_KVLAYOUT = 6,  /* K and V re-laid out as per-slice LDS images: bytes */
-  MOBA_NUM_STAGES = 7
+  MOBA_STAGE_DECODE_GATE = 7,   /* decode gate, top-k and union (work 0: */
+  MOBA_STAGE_DECODE_ATTN = 8,   /*   the bytes read depend on the device-side cache */
+  MOBA_STAGE_DECODE_MERGE = 9,  /*   lengths and are left to the caller) */
+  MOBA_NUM_STAGES = 10
 };
 int moba_profile_enable(int on);
 int moba_profile_read(double* ms, int64_t* launches, double* work, int32_t n);

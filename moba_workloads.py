@@ -151,3 +151,58 @@ def describe(w: Workload) -> dict:
         "block_size": w.block_size, "topk": w.topk, "causal": w.causal,
         "needle_blocks": w.needles,
     }
+
+
+# ---------------------------------------------------------------------------
+# Decode: one new query per sequence against a cache of L_b positions
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    dtype: str  # "bf16" | "f32"
+    num_q_heads: int
+    num_kv_heads: int
+    max_len: int
+    head_dim: int
+    block_size: int
+    topk: int
+    lens: tuple  # cached positions per sequence (the new token included)
+    seed: int = 0
+
+    @property
+    def batch(self) -> int:
+        return len(self.lens)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+def _ragged_1m_lens():
+    # eight sequences a little below 1M positions, at different points of
+    # their last block (one exactly at a block boundary, one just past one)
+    M = 1 << 20
+    return (M, M - 1, M - 4095, M - 4096, M - 4097, M - 70001, M - 123457, M - 262143)
+
+
+DECODE_WORKLOADS = {
+    # the prefill 1M layout (32/8 heads, D 128, block 4096, top-12) at decode
+    "decode_gqa32x8_1m_b8": DecodeWorkload("decode_gqa32x8_1m_b8", "bf16", 32, 8, 1 << 20, 128, 4096, 12,
+                                           _ragged_1m_lens(), seed=2001),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, device: str = "cpu", seed: Optional[int] = None):
+    """Return (q [b, Hq, D], k_cache, v_cache [b, max_len, Hkv, D], lens int32
+    [b]): seeded N(0, 1) noise rounded to the storage dtype.  Cache entries at
+    positions >= L_b hold noise too (a decode must never read them)."""
+    seed = w.seed if seed is None else seed
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    dt = w.torch_dtype
+    b, Hq, Hkv, D, Lm = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_len
+    q = _randn_chunked((b, Hq, D), gen, device, dt)
+    k = _randn_chunked((b, Lm, Hkv, D), gen, device, dt)
+    v = _randn_chunked((b, Lm, Hkv, D), gen, device, dt)
+    lens = torch.tensor(list(w.lens), dtype=torch.int32, device=device)
+    return q, k, v, lens

@@ -238,7 +238,9 @@ def moba_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_size: int,
 # Decode: one new query per sequence against a cache of its keys and values
 # ----------------------------------------------------------------------------
 def decode_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, lens: Sequence[int],
-                block_size: int, topk: int, keep_scores: bool = False) -> "RowResult":
+                block_size: int, topk: int, keep_scores: bool = False,
+                rows: Optional[Sequence[Tuple[int, int]]] = None,
+                given_sel: Optional[Sequence[Sequence[int]]] = None) -> "RowResult":
     """Decode-time MoBA: for sequence b with L = lens[b] cached positions (the
     new token's own key and value included), the new query q[b, h] sits at
     position t = L - 1 and is routed exactly as prefill row t would be
@@ -249,40 +251,51 @@ def decode_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, lens: S
     decode as future work (report §6.3) without fixing its rule; this is the
     prefill rule applied to the last row.
 
-    q: [batch, Hq, D]; k_cache, v_cache: [batch, Lmax, Hkv, D]; rows are
-    returned in (b, h) order, b-major."""
+    q: [batch, Hq, D]; k_cache, v_cache: [batch, Lmax, Hkv, D].  `rows`
+    lists the (b, h) pairs to evaluate (default: all, b-major); `given_sel`,
+    if set, replaces the gate's choice per row (checking an output under
+    another valid top-k set after a near tie)."""
     b, Hq, D = q.shape
     Hkv = k_cache.shape[2]
     g = Hq // Hkv
     B = block_size
     scale = 1.0 / math.sqrt(D)
-    res = RowResult(b * Hq, D, topk)
-    for bb in range(b):
+    if rows is None:
+        rows = [(bb, h) for bb in range(b) for h in range(Hq)]
+    rows = list(rows)
+    res = RowResult(len(rows), D, topk)
+    order = sorted(range(len(rows)), key=lambda r: (rows[r][0], rows[r][1] // g, r))
+    cur = None
+    for r in order:
+        bb, h = rows[r]
         L = int(lens[bb])
         if not 1 <= L <= k_cache.shape[1]:
             raise ValueError(f"cache length {L} outside [1, {k_cache.shape[1]}]")
         t = L - 1
         j = t // B
-        for hk in range(Hkv):
+        hk = h // g
+        if cur != (bb, hk):
+            cur = (bb, hk)
             k_head = np.asarray(k_cache[bb, :L, hk, :], dtype=np.float64)
             v_head = np.asarray(v_cache[bb, :L, hk, :], dtype=np.float64)
             mu = k_head[:j * B].reshape(j, B, D).mean(axis=1)  # the complete past blocks
-            for h in range(hk * g, (hk + 1) * g):
-                r = bb * Hq + h
-                q64 = np.asarray(q[bb, h], dtype=np.float64)
-                scores = mu @ q64
-                sel = select_blocks(np.concatenate([scores, [0.0]]), j, topk, True)
-                res.out[r] = _attend_blocks(q64, k_head, v_head, sel, t, B, True, scale)
-                res.sel[r, :len(sel)] = sel
-                if keep_scores:
-                    res.scores[r] = scores
-                m = min(topk - 1, j)
-                if 0 < m < j:
-                    ranked = sorted(range(j), key=lambda i: (-float(scores[i]), i))
-                    res.gap[r] = float(scores[ranked[m - 1]] - scores[ranked[m]])
-                    res.boundary[r] = (scores[ranked[m - 1]], scores[ranked[m]])
-                absk = np.abs(k_head[:j * B]).reshape(j, B, D).mean(axis=1)
-                res.score_eps[r] = score_error_bound(q64, mu, absk, B) if j else 0.0
+            absk = np.abs(k_head[:j * B]).reshape(j, B, D).mean(axis=1)
+        q64 = np.asarray(q[bb, h], dtype=np.float64)
+        scores = mu @ q64
+        if given_sel is None:
+            sel = select_blocks(np.concatenate([scores, [0.0]]), j, topk, True)
+        else:
+            sel = sorted(int(i) for i in given_sel[r] if i >= 0)
+        res.out[r] = _attend_blocks(q64, k_head, v_head, sel, t, B, True, scale)
+        res.sel[r, :len(sel)] = sel
+        if keep_scores:
+            res.scores[r] = scores
+        m = min(topk - 1, j)
+        if 0 < m < j:
+            ranked = sorted(range(j), key=lambda i: (-float(scores[i]), i))
+            res.gap[r] = float(scores[ranked[m - 1]] - scores[ranked[m]])
+            res.boundary[r] = (scores[ranked[m - 1]], scores[ranked[m]])
+        res.score_eps[r] = score_error_bound(q64, mu, absk, B) if j else 0.0
     return res
 
 

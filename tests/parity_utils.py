@@ -107,3 +107,59 @@ def compare(q_dev, k_dev, v_dev, out_dev, sel_dev, block_size: int, topk: int, c
         raise AssertionError(f"max |out - oracle| = {err[worst]:.3e} > {tol} at row {rows[worst]} "
                              f"(sel gpu {gsel[worst].tolist()} oracle {res.sel[worst].tolist()})")
     return ParityReport(len(rows), int(ties.sum()), len(redo), float(err[worst]), rows[worst], secs)
+
+
+def compare_decode(q_dev, kc_dev, vc_dev, lens, out_dev, sel_dev, block_size: int, topk: int,
+                   rows: Optional[Sequence[Tuple[int, int]]] = None, tol: float = 2e-2) -> ParityReport:
+    """Decode parity, with the same selection protocol as `compare`: rows
+    (b, h) (all if None) must choose the oracle's blocks unless the oracle's
+    gap is a near tie; their outputs are compared with the oracle evaluated
+    on the GPU's selection then."""
+    qh = q_dev.detach().cpu()
+    b, Hq, D = qh.shape
+    lens = [int(x) for x in lens]
+    if rows is None:
+        rows = [(bb, h) for bb in range(b) for h in range(Hq)]
+    rows = list(rows)
+    # the caches stay in their storage dtype on the host; the oracle converts
+    # one (sequence, KV head) prefix at a time
+    k32 = RowSource(kc_dev.detach().cpu())
+    v32 = RowSource(vc_dev.detach().cpu())
+    q32 = to_np32(qh)
+    outh = out_dev.detach().cpu().to(torch.float32)
+    selh = sel_dev.detach().cpu()
+    t0 = time.perf_counter()
+    res = O.decode_rows(q32, k32, v32, lens, block_size, topk, keep_scores=True, rows=rows)
+    ties = O.near_tie_rows(res)
+    gsel = np.stack([selh[bb, h].numpy() for (bb, h) in rows])
+    redo: List[int] = []
+    for r in range(len(rows)):
+        if np.array_equal(gsel[r], res.sel[r]):
+            continue
+        bb, h = rows[r]
+        if not ties[r]:
+            raise AssertionError(f"row {rows[r]}: GPU chose {gsel[r].tolist()}, oracle {res.sel[r].tolist()}, "
+                                 f"gap {res.gap[r]:.3e} is not a near tie (eps {res.score_eps[r]:.3e})")
+        j = (lens[bb] - 1) // block_size
+        past = [int(i) for i in gsel[r] if 0 <= i != j]
+        if j not in gsel[r].tolist():
+            raise AssertionError(f"row {rows[r]}: own block missing from GPU selection {gsel[r].tolist()}")
+        if not O.valid_topk_set(res.scores[r], past, j, min(topk - 1, j), res.score_eps[r]):
+            raise AssertionError(f"row {rows[r]}: GPU selection {gsel[r].tolist()} is not a valid top-k")
+        redo.append(r)
+    ref_out = res.out.copy()
+    if redo:
+        sub = O.decode_rows(q32, k32, v32, lens, block_size, topk, rows=[rows[r] for r in redo],
+                            given_sel=[gsel[r] for r in redo])
+        for x, r in enumerate(redo):
+            ref_out[r] = sub.out[x]
+    secs = time.perf_counter() - t0
+    gout = np.stack([outh[bb, h].numpy() for (bb, h) in rows]).astype(np.float64)
+    if not np.all(np.isfinite(gout)):
+        raise AssertionError("non-finite GPU decode output")
+    err = np.abs(gout - ref_out).max(axis=1)
+    worst = int(np.argmax(err))
+    if err[worst] > tol:
+        raise AssertionError(f"max |out - oracle| = {err[worst]:.3e} > {tol} at row {rows[worst]} "
+                             f"(sel gpu {gsel[worst].tolist()} oracle {res.sel[worst].tolist()})")
+    return ParityReport(len(rows), int(ties.sum()), len(redo), float(err[worst]), rows[worst], secs)

@@ -149,3 +149,50 @@ def test_gate_kind_entry_point_rejects_bad_arguments():
 def test_python_binding_rejects_unknown_gate():
     with pytest.raises(ValueError):
         M.moba_attn_fwd(torch.zeros(1), torch.zeros(1), torch.zeros(1), 128, 3, gate="max")
+
+
+def dws(b=2, L=4096, Hq=8, Hkv=2, D=128, dt=BF16, B=128, k=4):
+    out = ctypes.c_size_t(0)
+    st = _lib.lib.moba_decode_workspace_bytes(b, L, Hq, Hkv, D, dt, B, k, ctypes.byref(out))
+    return st, out.value
+
+
+def test_decode_workspace_validation():
+    st, n = dws()
+    assert st == OK and n > 0
+    assert dws(dt=7)[0] == DTYPE
+    assert dws(D=64)[0] == HEAD_DIM
+    assert dws(dt=0, D=64)[0] == OK
+    assert dws(Hq=6, Hkv=4)[0] == GQA
+    assert dws(Hq=34, Hkv=2)[0] == GQA  # group of 17 > 16
+    assert dws(k=0)[0] == TOPK and dws(k=65)[0] == TOPK and dws(k=64)[0] == OK
+    assert dws(L=4000)[0] == SEQ
+    assert dws(L=16385 * 64, B=64)[0] == SHAPE  # more than 16384 blocks
+    # partials grow with topk and the block size; scores with the capacity
+    assert dws(k=12)[1] > dws(k=4)[1]
+    assert dws(L=1 << 20, B=4096, k=12)[1] < 64 << 20
+
+
+def test_decode_entry_points_reject_bad_arguments():
+    L = _lib.lib
+    st, n = dws()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4096, 8, 2, 128, BF16, 128, 4, FAKE, None, FAKE, n, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.moba_decode_fwd(*a)
+
+    assert call(a0=None) == NULL
+    assert call(a3=None) == NULL  # mu_cache
+    assert call(a4=None) == NULL  # cache_lens
+    assert call(a15=None) == WS
+    assert call(a16=n - 1) == WS
+    assert call(a1=FAKE + 8) == ALIGN
+    assert call(a4=FAKE + 2) == ALIGN
+    assert call(a12=0) == TOPK
+    assert call(a6=4000) == SEQ
+    assert L.moba_decode_means(None, FAKE, 2, 4096, 2, 128, BF16, 128, FAKE, None) == NULL
+    assert L.moba_decode_means(FAKE, FAKE, 2, 4000, 2, 128, BF16, 128, FAKE, None) == SEQ
+    assert L.moba_decode_means(FAKE, FAKE, 2, 4096, 2, 128, BF16, 128, FAKE + 4, None) == ALIGN
