@@ -235,6 +235,63 @@ def moba_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_size: int,
 
 
 # ----------------------------------------------------------------------------
+# Backward: gradients of the forward with the gate's choice held fixed
+# ----------------------------------------------------------------------------
+def moba_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, block_size: int,
+                  topk: int, causal: bool = True,
+                  sel_idx: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """dq, dk, dv of sum(dout * out) and the row log-sum-exp, fp64, small inputs.
+
+    The gate is a hard top-k with no parameters (report §2.2): it only picks
+    which keys each row attends, and no gradient flows through the choice.
+    With the chosen key set K_t of row t fixed, the row is plain softmax
+    attention, so (the report trains models with MoBA, §3.3 and §3.4, but
+    prints no backward; the plainest reading is the gradient of the attention
+    over K_t):
+      p_s = exp(scale q.k_s - lse),  lse = log sum_{s in K_t} exp(scale q.k_s)
+      dv_s += p_s dout,   dp_s = dout . v_s,   delta = dout . out
+      ds_s = p_s (dp_s - delta)
+      dq = scale sum_s ds_s k_s,   dk_s += scale ds_s q.
+    sel_idx (as moba_forward returns it) fixes the choice; by default the
+    oracle's own gate makes it.  Returns dq [b, S, Hq, D], dk, dv [b, S,
+    Hkv, D] and lse [b, Hq, S] (natural log)."""
+    b, S, Hq, Hkv, D = _check_shapes(q, k, v, block_size, topk)
+    g = Hq // Hkv
+    B = block_size
+    scale = 1.0 / math.sqrt(D)
+    if sel_idx is None:
+        _, sel_idx = moba_forward(q, k, v, B, topk, causal)
+    q64 = np.asarray(q, dtype=np.float64)
+    k64 = np.asarray(k, dtype=np.float64)
+    v64 = np.asarray(v, dtype=np.float64)
+    do64 = np.asarray(dout, dtype=np.float64)
+    dq = np.zeros_like(q64)
+    dk = np.zeros_like(k64)
+    dv = np.zeros_like(v64)
+    lse = np.zeros((b, Hq, S))
+    for bb in range(b):
+        for h in range(Hq):
+            hk = h // g
+            for t in range(S):
+                sel = [int(i) for i in sel_idx[bb, h, t] if i >= 0]
+                keys = key_positions(sel, t, B, causal)
+                kk = k64[bb, keys, hk]
+                vv = v64[bb, keys, hk]
+                logits = (kk @ q64[bb, t, h]) * scale
+                m = logits.max()
+                z = np.exp(logits - m).sum()
+                lse[bb, h, t] = m + math.log(z)
+                p = np.exp(logits - lse[bb, h, t])
+                o = p @ vv
+                dp = vv @ do64[bb, t, h]
+                ds = p * (dp - do64[bb, t, h] @ o)
+                dq[bb, t, h] = scale * (ds @ kk)
+                dk[bb, keys, hk] += scale * np.outer(ds, q64[bb, t, h])
+                dv[bb, keys, hk] += np.outer(p, do64[bb, t, h])
+    return dq, dk, dv, lse
+
+
+# ----------------------------------------------------------------------------
 # Decode: one new query per sequence against a cache of its keys and values
 # ----------------------------------------------------------------------------
 def decode_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, lens: Sequence[int],

@@ -669,3 +669,124 @@ def test_decode_rejects_bad_lengths():
     for L in (0, 33):
         with pytest.raises(ValueError):
             O.decode_rows(q, kc, vc, [L], 8, 2)
+
+
+# ----------------------------------------------------------------------------
+# backward: gradients with the gate's choice held fixed
+# ----------------------------------------------------------------------------
+def _autograd_masked(q, k, v, dout, mask):
+    """torch fp64 autograd of softmax(q k^T / sqrt(D) + log mask) v, with the
+    KV heads expanded (query head h reads KV head h // g)."""
+    Hq, Hkv = q.shape[2], k.shape[2]
+    g = Hq // Hkv
+    qt = torch.from_numpy(q).requires_grad_(True)
+    kt = torch.from_numpy(k).requires_grad_(True)
+    vt = torch.from_numpy(v).requires_grad_(True)
+    qh = qt.permute(0, 2, 1, 3)
+    kh = kt.permute(0, 2, 1, 3).repeat_interleave(g, dim=1)
+    vh = vt.permute(0, 2, 1, 3).repeat_interleave(g, dim=1)
+    logits = (qh @ kh.transpose(-1, -2)) / math.sqrt(q.shape[3])
+    logits = logits.masked_fill(~torch.from_numpy(mask), float("-inf"))
+    o = torch.softmax(logits, dim=-1) @ vh
+    (o.permute(0, 2, 1, 3) * torch.from_numpy(dout)).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def _mask_from_sel(sel, S, B, causal):
+    """[b, Hq, S, S] boolean mask of the keys each row attends, element by
+    element from the chosen blocks (own block cut at the row itself)."""
+    b, Hq = sel.shape[0], sel.shape[1]
+    mask = np.zeros((b, Hq, S, S), dtype=bool)
+    for bb in range(b):
+        for h in range(Hq):
+            for t in range(S):
+                for i in sel[bb, h, t]:
+                    if i < 0:
+                        continue
+                    for s in range(i * B, (i + 1) * B):
+                        if not causal or s <= t:
+                            mask[bb, h, t, s] = True
+    return mask
+
+
+@pytest.mark.parametrize("S,B,topk,Hq,Hkv,causal", [
+    (64, 16, 2, 2, 1, True), (96, 16, 3, 4, 2, True), (48, 8, 4, 2, 2, True), (64, 16, 2, 2, 1, False),
+])
+def test_backward_equals_autograd_of_masked_attention(S, B, topk, Hq, Hkv, causal):
+    rng = np.random.default_rng(S + B + topk)
+    D = 8
+    q, k, v = rand_qkv(rng, 1, S, Hq, Hkv, D)
+    dout = rng.standard_normal(q.shape)
+    _, sel = O.moba_forward(q, k, v, B, topk, causal)
+    dq, dk, dv, lse = O.moba_backward(q, k, v, dout, B, topk, causal)
+    mask = _mask_from_sel(sel, S, B, causal)
+    rq, rk, rv = _autograd_masked(q, k, v, dout, mask)
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-10)
+    # lse: log-sum-exp of the row's scaled logits over the same mask
+    logits = np.einsum("bthd,bshd->bhts", q, np.repeat(k, Hq // Hkv, axis=2)) / math.sqrt(D)
+    ref_lse = np.log(np.where(mask, np.exp(logits), 0.0).sum(-1))
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+def test_backward_dense_equals_sdpa_autograd():
+    """Every block chosen: the gradients of dense causal attention (torch fp64
+    SDPA autograd)."""
+    rng = np.random.default_rng(77)
+    b, S, Hq, Hkv, D, B = 2, 48, 4, 2, 8, 16
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    dout = rng.standard_normal(q.shape)
+    dq, dk, dv, _ = O.moba_backward(q, k, v, dout, B, 3, True)
+    qt = torch.from_numpy(q).requires_grad_(True)
+    kt = torch.from_numpy(k).requires_grad_(True)
+    vt = torch.from_numpy(v).requires_grad_(True)
+    o = F.scaled_dot_product_attention(qt.permute(0, 2, 1, 3), kt.permute(0, 2, 1, 3).repeat_interleave(2, 1),
+                                       vt.permute(0, 2, 1, 3).repeat_interleave(2, 1), is_causal=True)
+    (o.permute(0, 2, 1, 3) * torch.from_numpy(dout)).sum().backward()
+    for got, ref in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-10)
+
+
+def test_backward_matches_finite_differences():
+    """Central differences of sum(dout * out) along random directions, with
+    the selection held fixed (it is piecewise constant: checked unchanged)."""
+    rng = np.random.default_rng(5)
+    b, S, Hq, Hkv, D, B, topk = 1, 48, 2, 1, 8, 8, 3
+    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
+    dout = rng.standard_normal(q.shape)
+    out0, sel0 = O.moba_forward(q, k, v, B, topk, True)
+    dq, dk, dv, _ = O.moba_backward(q, k, v, dout, B, topk, True)
+    eps = 1e-6
+    for which in range(3):
+        dirn = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)]
+        dirn[which] = rng.standard_normal(dirn[which].shape)
+        plus = [x + eps * d for x, d in zip((q, k, v), dirn)]
+        minus = [x - eps * d for x, d in zip((q, k, v), dirn)]
+        op, sp = O.moba_forward(*plus, B, topk, True)
+        om, sm = O.moba_forward(*minus, B, topk, True)
+        assert np.array_equal(sp, sel0) and np.array_equal(sm, sel0)
+        fd = ((op - om) * dout).sum() / (2 * eps)
+        an = (dq * dirn[0]).sum() + (dk * dirn[1]).sum() + (dv * dirn[2]).sum()
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (which, fd, an)
+
+
+def test_planted_backward_mistakes_are_caught(monkeypatch):
+    """A backward without the delta term, or with the own block uncut, must
+    fail the masked-autograd pin."""
+    rng = np.random.default_rng(8)
+    S, B, topk, D = 48, 16, 2, 8
+    q, k, v = rand_qkv(rng, 1, S, 2, 1, D)
+    dout = rng.standard_normal(q.shape)
+    _, sel = O.moba_forward(q, k, v, B, topk, True)
+    rq, rk, rv = _autograd_masked(q, k, v, dout, _mask_from_sel(sel, S, B, True))
+    real = O.key_positions
+
+    def own_uncut(sel_, t, B_, causal):
+        return real(sel_, (t // B_) * B_ + B_ - 1, B_, causal) if causal else real(sel_, t, B_, causal)
+
+    monkeypatch.setattr(O, "key_positions", own_uncut)
+    dq, dk, dv, _ = O.moba_backward(q, k, v, dout, B, topk, True, sel_idx=sel)
+    assert not np.allclose(dv, rv, atol=1e-6)
+    monkeypatch.setattr(O, "key_positions", real)
+    dq, dk, dv, _ = O.moba_backward(q, k, v, dout, B, topk, True, sel_idx=sel)
+    np.testing.assert_allclose(dv, rv, rtol=0, atol=1e-10)
