@@ -16,7 +16,10 @@ from ._lib import (  # noqa: F401
     decode_workspace_bytes,
     moba_decode_fwd,
     moba_decode_means,
+    bwd_workspace_bytes,
+    moba_attn_bwd,
     moba_attn_fwd,
+    moba_attn_fwd_train,
     moba_gate,
     moba_meanpool,
     moba_minmaxpool,

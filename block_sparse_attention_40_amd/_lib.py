@@ -41,6 +41,12 @@ SIGNATURES = {
     "moba_decode_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                        _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "moba_decode_means": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p]),
+    "moba_attn_fwd_train": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "moba_bwd_workspace_bytes": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                _c_i32, ctypes.POINTER(_c_sz)]),
+    "moba_attn_bwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32,
+                                     _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "moba_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "moba_profile_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_i64),
                                          ctypes.POINTER(ctypes.c_double), _c_i32]),
@@ -50,7 +56,7 @@ SIGNATURES = {
 GATE_KINDS = {"mean": 0, "minmax": 1}
 
 STAGES = ("meanpool", "gate", "dispatch", "attn_past", "attn_own", "attn_f32", "kv_layout",
-          "decode_gate", "decode_attn", "decode_merge")
+          "decode_gate", "decode_attn", "decode_merge", "bwd_prep", "bwd_dkdv", "bwd_dq")
 
 
 class MobaError(RuntimeError):
@@ -282,3 +288,61 @@ def moba_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     if st != MOBA_OK:
         raise MobaError(st, "moba_decode_fwd")
     return out, sel_idx
+
+
+def moba_attn_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int, topk: int,
+                        causal: bool = True, workspace: Optional[torch.Tensor] = None
+                        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Forward for training: (out, sel_idx [b, Hq, S, topk] int32, lse [b, Hq,
+    S] fp32, natural log of the row's sum of exp of the scaled logits)."""
+    _check_dev(q, k, v)
+    b, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    dt = _dtype_code(q)
+    out = torch.empty_like(q)
+    sel = torch.empty((b, Hq, S, topk), dtype=torch.int32, device=q.device)
+    lse = torch.empty((b, Hq, S), dtype=torch.float32, device=q.device)
+    nbytes = workspace_bytes(b, S, Hq, Hkv, D, dt, block_size, topk, causal)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = lib.moba_attn_fwd_train(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, S, Hq, Hkv, D, dt, block_size, topk,
+                                 int(bool(causal)), out.data_ptr(), sel.data_ptr(), lse.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 _stream_ptr(q.device))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_attn_fwd_train")
+    return out, sel, lse
+
+
+def bwd_workspace_bytes(batch: int, seqlen: int, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int,
+                        block_size: int, topk: int, causal: bool = True) -> int:
+    out = _c_sz(0)
+    st = lib.moba_bwd_workspace_bytes(batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
+                                      int(bool(causal)), ctypes.byref(out))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_bwd_workspace_bytes")
+    return int(out.value)
+
+
+def moba_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                  lse: torch.Tensor, sel_idx: torch.Tensor, block_size: int, topk: int, causal: bool = True,
+                  workspace: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward with the forward's selection held fixed: (dq, dk, dv)."""
+    _check_dev(q, k, v, out, dout, lse, sel_idx)
+    b, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    dt = _dtype_code(q)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    nbytes = bwd_workspace_bytes(b, S, Hq, Hkv, D, dt, block_size, topk, causal)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = lib.moba_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                           lse.data_ptr(), sel_idx.data_ptr(), b, S, Hq, Hkv, D, dt, block_size, topk,
+                           int(bool(causal)), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_attn_bwd")
+    return dq, dk, dv

@@ -812,6 +812,8 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
   if (valid) {
     const float inv = 1.f / Lsum;
     const int64_t t = j * a.block + pos;
+    // the row's log-sum-exp of the scaled logits, natural log (for the backward)
+    if (a.lse && lg == 0) a.lse[((int64_t)a.bb * a.hq + h) * a.seqlen + t] = (M + fast_log2(Lsum)) * 0.6931471805599453f;
     bf16raw* dst = reinterpret_cast<bf16raw*>(a.out) + ((a.bb * a.seqlen + t) * a.hq + h) * HD;
 #pragma unroll
     for (int b = 0; b < 4; ++b)

@@ -88,6 +88,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Args a) {
   }
   float* orow = a.out + ((a.bb * a.seqlen + t) * a.hq + h) * D;
   const float inv = 1.f / l;
+  // the row's log-sum-exp of the scaled logits, natural log (for the backward)
+  if (a.lse && lane == 0) a.lse[((int64_t)a.bb * a.hq + h) * a.seqlen + t] = (m + fast_log2(l)) * 0.6931471805599453f;
 #pragma unroll
   for (int xo = 0; xo < NPL; ++xo) orow[lane + 64 * xo] = o[xo] * inv;
 }

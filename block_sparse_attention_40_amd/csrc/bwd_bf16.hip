@@ -1,0 +1,498 @@
+// Backward of the MoBA attention on bf16 MFMA (gfx950), head dim 128.
+//
+// The gate is a hard top-k with no parameters (deep-dive report on MoBA,
+// §2.2): it only decides which keys a row attends, and no gradient flows
+// through that decision.  With each row's chosen keys fixed, the row is plain
+// softmax attention, so with the forward's row log-sum-exp (lse) and
+// delta = dout . out:
+//   p = exp(scale q.k - lse),  dp = dout . v,  ds = p (dp - delta),
+//   dq = scale sum_keys ds k,  dk += scale ds q,  dv += p dout.
+// The report trains with this attention (§3.3) but prints no backward; this
+// is the gradient of the forward as computed.
+//
+// Work split, reusing the forward's block-major dispatch (report §3.2):
+//   bwd_dq_kernel    query-stationary, like the forward's past-block kernel:
+//                    one work-group per tile of up to 256 (row, slot) entries
+//                    of one list (KV head, block), the block's keys streamed
+//                    through LDS from three slice images (K and V in the K
+//                    layout, K in the V^T layout); per 32-key half:
+//                    S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+//                    Own-block tiles (causal) mask keys after the row.  Each
+//                    (row, slot) writes its dq contribution (fp32); a merge
+//                    adds a row's contributions.
+//   bwd_dkdv_kernel  key-stationary: one work-group per 128 keys of one block
+//                    (4 waves x 32 keys, the keys' K and V rows held in
+//                    registers); it walks every row that attends the block
+//                    (the block's whole-sequence list, then, causal, the
+//                    block's own rows at or after the slice) in steps of 32
+//                    rows staged in LDS, and accumulates
+//                    dV += P^T dO and dK += dS^T Q on the MFMAs.  The row
+//                    operands of those two products run along the
+//                    contraction, so they are read with the transposing LDS
+//                    load (ds_read_b64_tr_b16) from the row-major staging.
+#include "moba_device.h"
+#include "moba_kernels.h"
+#include "moba_plan.h"
+
+namespace moba {
+
+namespace {
+
+constexpr int BD = 128;              // head dim
+constexpr int BKT = 64;              // keys per image slice
+constexpr int BIMG = BKT * BD * 2;   // bytes of one slice image (16 KiB)
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float wsum64(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Slice-relative key held in accumulator element e of 32-key half kb (the
+// C layout of v_mfma_f32_32x32x16: element e of lane l is row 8(e/4) +
+// 4(l/32) + e%4 of the 32-row block).
+__device__ __forceinline__ int acc_row(int e, int lg) { return 8 * (e >> 2) + 4 * lg + (e & 3); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// delta and base-2 lse per row.  One wave per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16raw* __restrict__ out, const bf16raw* __restrict__ dout,
+                                                       const float* __restrict__ lse, float* __restrict__ lse2,
+                                                       float* __restrict__ delta, int64_t rows, int64_t seqlen,
+                                                       int hq) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const uint32_t o = *reinterpret_cast<const uint32_t*>(out + row * BD + 2 * lane);
+  const uint32_t d = *reinterpret_cast<const uint32_t*>(dout + row * BD + 2 * lane);
+  const float x = wsum64(bf16lo(o) * bf16lo(d) + bf16hi(o) * bf16hi(d));
+  if (lane == 0) {
+    const int64_t per_b = seqlen * hq;
+    const int64_t bb = row / per_b, rem = row % per_b;
+    const int64_t t = rem / hq;
+    const int h = (int)(rem % hq);
+    delta[row] = x;
+    lse2[row] = lse[(bb * hq + h) * seqlen + t] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq.  256 rows per work-group (8 waves x 32 rows); kOwn: the rows are
+// 256 / g positions x g heads of one own block (grid (tiles, hkv)).
+// ---------------------------------------------------------------------------
+template <bool kOwn>
+__global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * 3 * BIMG];  // two buffers x three images
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 5;
+  int hk, cnt;
+  int64_t blk, own_p0 = 0;
+  int32_t start = 0;
+  if constexpr (!kOwn) {
+    const int32_t total = a.tiles[0];
+    const int32_t tile = (int32_t)blockIdx.x;
+    if (tile >= total) return;
+    const int32_t L = a.tiles[8 + 2 * tile];
+    start = a.tiles[9 + 2 * tile];
+    const int32_t end = a.listoff[L] + a.count[L];
+    cnt = (end - start) < 256 ? (end - start) : 256;
+    hk = (int)(L / a.n);
+    blk = L % a.n;
+  } else {
+    const int ppt = 256 / a.g;  // positions per tile
+    const int64_t tpb = (a.block + ppt - 1) / ppt;
+    hk = (int)blockIdx.y;
+    blk = a.t0 / a.block + blockIdx.x / tpb;
+    own_p0 = (int64_t)(blockIdx.x % tpb) * ppt;
+    const int64_t np = (a.block - own_p0) < ppt ? (a.block - own_p0) : ppt;
+    cnt = (int)np * a.g;
+  }
+  const int r = wave * 32 + (lane & 31);
+  const bool valid = r < cnt;
+  const int rr = valid ? r : 0;
+  int64_t t, pidx;
+  int h;
+  if constexpr (!kOwn) {
+    const int32_t entry = a.entries[start + rr];
+    const int64_t local_row = entry / a.kp;
+    t = a.t0 + local_row / a.hq;
+    h = (int)(local_row % a.hq);
+    pidx = local_row * a.kps + entry % a.kp;
+  } else {
+    h = hk * a.g + rr % a.g;
+    t = blk * a.block + own_p0 + rr / a.g;
+    pidx = ((t - a.t0) * a.hq + h) * a.kps + a.kp;  // the own slot
+  }
+  const int64_t grow = ((int64_t)a.bb * a.seqlen + t) * a.hq + h;
+  bf16x8 qb[8], db[8];
+  {
+    const bf16raw* qr = reinterpret_cast<const bf16raw*>(a.q) + grow * BD + lg * 8;
+    const bf16raw* dr = reinterpret_cast<const bf16raw*>(a.dout) + grow * BD + lg * 8;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qb[s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s);
+      db[s] = *reinterpret_cast<const bf16x8*>(dr + 16 * s);
+    }
+  }
+  const float lse2 = valid ? a.lse2[grow] : __builtin_inff();  // invalid rows: p = 0
+  const float dl = a.delta[grow];
+  f32x16 o[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[b][e] = 0.f;
+
+  const int nsl_blk = a.block / BKT;
+  int nsl = nsl_blk;
+  if constexpr (kOwn) {
+    // slices up to the tile's last position
+    const int64_t last = own_p0 + (cnt + a.g - 1) / a.g - 1;
+    nsl = (int)(last / BKT) + 1;
+  }
+  const int64_t img0 = (((int64_t)a.bb * a.hkv + hk) * (a.seqlen / BKT) + blk * nsl_blk) * (BKT * BD);
+  const uint16_t* im[3] = {a.kimg + img0, a.vkimg + img0, a.kvimg + img0};
+  // staging: 3 images x 1024 units of 16 bytes = 6 units per thread
+  u32x4 stg[6];
+  auto load = [&](int sl) {
+    const int64_t so = (int64_t)(sl < nsl ? sl : nsl - 1) * (BKT * BD);
+#pragma unroll
+    for (int x = 0; x < 6; ++x) {
+      const int u = tid + 512 * x;  // 0 .. 3071
+      stg[x] = *reinterpret_cast<const u32x4*>(im[u >> 10] + so + (u & 1023) * 8);
+    }
+  };
+  auto store = [&](char* buf) {
+#pragma unroll
+    for (int x = 0; x < 6; ++x) {
+      const int u = tid + 512 * x;
+      *reinterpret_cast<u32x4*>(buf + (u >> 10) * BIMG + (u & 1023) * 16) = stg[x];
+    }
+  };
+  const int kofs = lg * 1024 + (lane & 31) * 16;  // K-layout operand base (unit-major images)
+  const int vofs = lg * 2048 + (lane & 31) * 16;  // V^T-layout operand base
+  const float c = a.scale_log2;
+
+  load(0);
+  store(smem);
+  __syncthreads();
+  for (int sl = 0; sl < nsl; ++sl) {
+    const char* buf = smem + (sl & 1) * 3 * BIMG;
+    if (sl + 1 < nsl) load(sl + 1);
+    const int64_t key_base = blk * a.block + (int64_t)sl * BKT;  // absolute position of key 0 of the slice
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(buf + kofs + st * 2048 + kb * 512);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(buf + BIMG + kofs + st * 2048 + kb * 512);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[st], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, db[st], dp, 0, 0, 0);
+      }
+      // dS^T, packed as the B operand of dQ^T (same order as the forward's P^T)
+      uint32_t pk[8];
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        float p0 = fast_exp2(__builtin_fmaf(s[e], c, -lse2));
+        float p1 = fast_exp2(__builtin_fmaf(s[e + 1], c, -lse2));
+        if constexpr (kOwn) {
+          const int64_t k0 = key_base + kb * 32 + acc_row(e, lg);
+          if (k0 > t) p0 = 0.f;
+          if (k0 + 1 > t) p1 = 0.f;
+        }
+        pk[e >> 1] = pack_bf16x2(p0 * (dp[e] - dl), p1 * (dp[e + 1] - dl));
+      }
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[4 * hs], pk[4 * hs + 1], pk[4 * hs + 2], pk[4 * hs + 3]});
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(buf + 2 * BIMG + vofs + (4 * kb + 2 * hs) * 2048 + b * 512);
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, pb, o[b], 0, 0, 0);
+        }
+      }
+    }
+    if (sl + 1 < nsl) store(smem + ((sl + 1) & 1) * 3 * BIMG);
+    __syncthreads();
+  }
+
+  if (valid) {
+    // lane holds d = 32 b + 8 q + 4 lg + i (i = 0..3) of its row
+    float* dst = a.dq_part + pidx * BD;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(dst + 32 * b + 8 * q4 + 4 * lg) =
+            f32x4{o[b][4 * q4] * a.scale, o[b][4 * q4 + 1] * a.scale, o[b][4 * q4 + 2] * a.scale,
+                  o[b][4 * q4 + 3] * a.scale};
+  }
+}
+
+// dq of the chunk's rows: the sum of the row's slot contributions, bf16.  One
+// wave per row (two dims per lane).
+__global__ __launch_bounds__(256) void bwd_dq_merge_kernel(BwdArgs a) {
+  const int64_t lr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // chunk-local row
+  const int lane = threadIdx.x & 63;
+  if (lr >= a.cnt * a.hq) return;
+  const int64_t t = a.t0 + lr / a.hq;
+  const int h = (int)(lr % a.hq);
+  const int64_t j = t / a.block;
+  const int npast = a.causal ? (int)(j < a.kp ? j : a.kp) : a.kp;
+  const float* src = a.dq_part + lr * a.kps * BD + 2 * lane;
+  float x0 = 0.f, x1 = 0.f;
+  for (int s = 0; s < npast; ++s) {
+    const float2 v = *reinterpret_cast<const float2*>(src + s * BD);
+    x0 += v.x;
+    x1 += v.y;
+  }
+  if (a.causal) {
+    const float2 v = *reinterpret_cast<const float2*>(src + a.kp * BD);
+    x0 += v.x;
+    x1 += v.y;
+  }
+  bf16raw* dst = reinterpret_cast<bf16raw*>(a.dq) + (((int64_t)a.bb * a.seqlen + t) * a.hq + h) * BD + 2 * lane;
+  *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(x0, x1);
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv.  grid (n * ceil(block / 128), hkv): 128 keys of one block per
+// work-group, 4 waves x 32 keys.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int RSTEP = 32;        // rows per step
+constexpr int RROW = BD * 2;     // bytes per staged row (16 units of 16 bytes)
+constexpr int RTILE = RSTEP * RROW;  // one staged tensor (8 KiB)
+constexpr int kKvWaves = 4;          // waves (32 keys each) per work-group
+constexpr int kKvKeys = 32 * kKvWaves;
+constexpr int kKvThreads = 64 * kKvWaves;
+
+// Position of 16-byte unit u of staged row r: a rotation per row that keeps
+// both the row-wise 16-byte operand reads (16 rows, one unit) and the
+// transposing 8-byte reads (4 rows x 4 units per 16 lanes) free of bank
+// conflicts.
+__device__ __forceinline__ int unit_pos(int r, int u) { return (u + 4 * (r & 3) + ((r >> 2) & 3)) & 15; }
+__device__ __forceinline__ int row_off(int r, int u) { return r * RROW + unit_pos(r, u) * 16; }
+}  // namespace
+
+__global__ __launch_bounds__(kKvWaves * 64) void bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char rs[2][2 * RTILE];  // [buffer][Q rows | dO rows]
+  __shared__ __attribute__((aligned(16))) float rl[2][RSTEP];
+  __shared__ __attribute__((aligned(16))) float rd[2][RSTEP];
+  __shared__ __attribute__((aligned(16))) int32_t rt[2][RSTEP];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 5;
+  const int hk = (int)blockIdx.y;
+  const int spb = (a.block + kKvKeys - 1) / kKvKeys;  // work-groups per block
+  const int64_t i = blockIdx.x / spb;
+  const int64_t key0 = i * a.block + (int64_t)(blockIdx.x % spb) * kKvKeys;  // first key of the work-group
+  const int64_t wkey = key0 + wave * 32;                                  // first key of this wave
+  // a block of 64 or 128 keys leaves waves without keys (wave-uniform)
+  const bool wact = wkey < (i + 1) * a.block;
+  const int64_t rowstride = (int64_t)a.hkv * BD;
+  const int64_t bS = (int64_t)a.bb * a.seqlen;
+
+  // the wave's keys and values as B operands of S = Q K^T and dP = dO V^T:
+  // lane = key (l % 32), 8 dims at 8 lg + 16 s
+  bf16x8 kbv[8], vbv[8];
+  if (wact) {
+    const int64_t key = wkey + (lane & 31);
+    const bf16raw* kr = reinterpret_cast<const bf16raw*>(a.k) + (bS + key) * rowstride + hk * BD + lg * 8;
+    const bf16raw* vr = reinterpret_cast<const bf16raw*>(a.v) + (bS + key) * rowstride + hk * BD + lg * 8;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kbv[s] = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
+      vbv[s] = *reinterpret_cast<const bf16x8*>(vr + 16 * s);
+    }
+  }
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { dk[b][e] = 0.f; dv[b][e] = 0.f; }
+
+  // rows: the block's list, then (causal) its own rows at or after key0
+  const int64_t L = (int64_t)hk * a.n + i;
+  // (no past slots, kp = 0: the lists were not built)
+  const int32_t lbeg = a.kp > 0 ? a.listoff_f[L] : 0;
+  const int64_t npast = a.kp > 0 ? a.count_f[L] : 0;
+  const int64_t own_pos0 = key0;                    // positions before key0 see none of these keys
+  const int64_t nown = a.causal ? ((i + 1) * a.block - own_pos0) * a.g : 0;
+  const int64_t nrows = npast + nown;
+  const int64_t nsteps = (nrows + RSTEP - 1) / RSTEP;
+
+  // staging: 32 rows x 16 units x 2 tensors = 1024 units
+  constexpr int SU = 512 / kKvThreads;  // units per thread and tensor
+  u32x4 sq[SU], sd[SU];
+  int64_t sgrow[SU];
+  int32_t st_pos[SU];
+  bool sval[SU];
+  auto row_of = [&](int64_t rix, int64_t& grow, int32_t& pos) {
+    if (rix < npast) {
+      const int32_t entry = a.entries_f[lbeg + rix];
+      const int64_t lr = entry / a.kp;  // whole-sequence list: row = position * hq + head
+      grow = bS * a.hq + lr;
+      pos = (int32_t)(lr / a.hq);
+    } else {
+      const int64_t o = rix - npast;
+      const int64_t p = own_pos0 + o / a.g;
+      grow = (bS + p) * a.hq + hk * a.g + (int)(o % a.g);
+      pos = (int32_t)p;
+    }
+  };
+  // thread unit x: row (tid + kKvThreads x) / 16, unit tid % 16
+  auto load_step = [&](int64_t step) {
+#pragma unroll
+    for (int x = 0; x < SU; ++x) {
+      const int row = (tid + kKvThreads * x) >> 4, u = tid & 15;
+      const int64_t rix = step * RSTEP + row;
+      sval[x] = rix < nrows;
+      row_of(sval[x] ? rix : nrows - 1, sgrow[x], st_pos[x]);
+      sq[x] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16raw*>(a.q) + sgrow[x] * BD + u * 8);
+      sd[x] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16raw*>(a.dout) + sgrow[x] * BD + u * 8);
+    }
+  };
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < SU; ++x) {
+      const int row = (tid + kKvThreads * x) >> 4, u = tid & 15;
+      *reinterpret_cast<u32x4*>(rs[buf] + row_off(row, u)) = sq[x];
+      *reinterpret_cast<u32x4*>(rs[buf] + RTILE + row_off(row, u)) = sd[x];
+      if (u == 0) {
+        rl[buf][row] = sval[x] ? a.lse2[sgrow[x]] : __builtin_inff();  // padding rows: p = 0
+        rd[buf][row] = a.delta[sgrow[x]];
+        rt[buf][row] = st_pos[x];
+      }
+    }
+  };
+
+  const float c = a.scale_log2;
+  // transposing reads: lane l supplies row 4 (l / 32) + (l % 16) / 4 (+ 8) of
+  // a 16-row step and dims 32 dt + 16 ((l / 16) & 1) + 4 (l % 4) .. + 3
+  const int tr_r = 4 * lg + ((lane & 15) >> 2);
+  const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // element offset inside a 32-dim tile
+
+  if (nsteps > 0) {
+    load_step(0);
+    store_step(0);
+  }
+  __syncthreads();
+  for (int64_t step = 0; step < nsteps; ++step) {
+    const int buf = (int)(step & 1);
+    if (step + 1 < nsteps) load_step(step + 1);
+    if (!wact) {
+      if (step + 1 < nsteps) store_step(buf ^ 1);
+      __syncthreads();
+      continue;
+    }
+    const char* qs = rs[buf];
+    const char* ds = rs[buf] + RTILE;
+    // S = Q K^T and dP = dO V^T: M = row (lane % 32 reads its row), N = key
+    f32x16 s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+    const int ar = lane & 31;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + row_off(ar, lg + 2 * st));
+      const bf16x8 da = *reinterpret_cast<const bf16x8*>(ds + row_off(ar, lg + 2 * st));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kbv[st], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vbv[st], dp, 0, 0, 0);
+    }
+    // lane = key wkey + lane % 32; element e = row acc_row(e, lg)
+    const int32_t mykey = (int32_t)(wkey + (lane & 31));  // position of this lane's key
+    uint32_t pa[8], sa[8];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // rows 8 q4 + 4 lg + 0..3 are consecutive: one 16-byte read per array
+      const int r0 = 8 * q4 + 4 * lg;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&rl[buf][r0]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&rd[buf][r0]);
+      const u32x4 t4 = *reinterpret_cast<const u32x4*>(&rt[buf][r0]);
+      float p[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        p[x] = fast_exp2(__builtin_fmaf(s[4 * q4 + x], c, -l4[x]));
+        if (a.causal && mykey > (int32_t)t4[x]) p[x] = 0.f;
+      }
+      pa[2 * q4] = pack_bf16x2(p[0], p[1]);
+      pa[2 * q4 + 1] = pack_bf16x2(p[2], p[3]);
+      sa[2 * q4] = pack_bf16x2(p[0] * (dp[4 * q4] - d4[0]), p[1] * (dp[4 * q4 + 1] - d4[1]));
+      sa[2 * q4 + 1] = pack_bf16x2(p[2] * (dp[4 * q4 + 2] - d4[2]), p[3] * (dp[4 * q4 + 3] - d4[3]));
+    }
+    // dV += P^T dO and dK += dS^T Q: M = key, N = dim, K = row; the A
+    // operand of step st is elements 8 st .. 8 st + 7 (rows 16 st + 8 (j/4) +
+    // 4 lg + j % 4), the B operand the same rows of dO / Q read transposed
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8 pA = __builtin_bit_cast(bf16x8, u32x4{pa[4 * st], pa[4 * st + 1], pa[4 * st + 2], pa[4 * st + 3]});
+      const bf16x8 sA = __builtin_bit_cast(bf16x8, u32x4{sa[4 * st], sa[4 * st + 1], sa[4 * st + 2], sa[4 * st + 3]});
+      const int ra = 16 * st + tr_r, rb = ra + 8;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int col = 32 * dt + tr_c;  // element; unit col / 8, half (col / 4) & 1
+        const int oa = row_off(ra, col >> 3) + ((col >> 2) & 1) * 8;
+        const int ob = row_off(rb, col >> 3) + ((col >> 2) & 1) * 8;
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const s16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ds + oa));
+        const s16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ds + ob));
+        const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qs + oa));
+        const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qs + ob));
+        const bf16x8 dB = __builtin_bit_cast(bf16x8, __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 qB = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pA, dB, dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sA, qB, dk[dt], 0, 0, 0);
+      }
+    }
+    if (step + 1 < nsteps) store_step(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!wact) return;
+  // C layout of dK, dV: lane = dim 32 dt + lane % 32, element e = key acc_row(e, lg)
+  bf16raw* dkp = reinterpret_cast<bf16raw*>(a.dk) + (bS + wkey) * rowstride + hk * BD + (lane & 31);
+  bf16raw* dvp = reinterpret_cast<bf16raw*>(a.dv) + (bS + wkey) * rowstride + hk * BD + (lane & 31);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t off = (int64_t)acc_row(e, lg) * rowstride + 32 * dt;
+      dkp[off] = (bf16raw)(pack_bf16x2(dk[dt][e] * a.scale, 0.f) & 0xffffu);
+      dvp[off] = (bf16raw)(pack_bf16x2(dv[dt][e], 0.f) & 0xffffu);
+    }
+}
+
+int launch_bwd_prep(const void* out, const void* dout, const float* lse, float* lse2, float* delta, int64_t batch,
+                    int64_t seqlen, int hq, hipStream_t st) {
+  const int64_t rows = batch * seqlen * hq;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                     reinterpret_cast<const bf16raw*>(out), reinterpret_cast<const bf16raw*>(dout), lse, lse2, delta,
+                     rows, seqlen, hq);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_bwd_dq(const BwdArgs& a, int64_t max_tiles, hipStream_t st) {
+  if (max_tiles > 0) hipLaunchKernelGGL((bwd_dq_kernel<false>), dim3((unsigned)max_tiles), dim3(512), 0, st, a);
+  if (a.causal) {
+    const int ppt = 256 / a.g;
+    const int64_t tpb = (a.block + ppt - 1) / ppt;
+    const int64_t nblk = a.cnt / a.block;
+    hipLaunchKernelGGL((bwd_dq_kernel<true>), dim3((unsigned)(tpb * nblk), (unsigned)a.hkv), dim3(512), 0, st, a);
+  }
+  const int64_t rows = a.cnt * a.hq;
+  hipLaunchKernelGGL(bwd_dq_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_bwd_dkdv(const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(a.n * ((a.block + kKvKeys - 1) / kKvKeys)), (unsigned)a.hkv),
+                     dim3(kKvThreads), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace moba

@@ -116,6 +116,45 @@ __global__ __launch_bounds__(256) void scatter_kernel(DispatchArgs a) {
   }
 }
 
+// Counts per (list, gate work-group) from the selection alone: the same rows
+// per work-group as the gate and the scatter, written contiguous per list.
+__global__ __launch_bounds__(256) void hist_kernel(DispatchArgs a) {
+  extern __shared__ int32_t lcnt[];  // [n]
+  const int tid = threadIdx.x;
+  const int64_t w = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int64_t n = a.n;
+  for (int64_t i = tid; i < n; i += 256) lcnt[i] = 0;
+  __syncthreads();
+  const int g = a.g;
+  const int64_t pic = w * a.gate_t + tid / g;
+  const int h = hk * g + tid % g;
+  const bool valid = tid < a.gate_t * g && pic < a.cnt;
+  if (valid) {
+    const int64_t t = a.t0 + pic;
+    const int64_t j = t / a.block;
+    const int32_t* row = a.sel + (int64_t)h * a.sel_stride_h + (t - a.sel_pos_base) * a.topk;
+    int slot = 0;
+    for (int c = 0; c < a.topk && slot < a.kp; ++c) {
+      const int32_t i = row[c];
+      if (i < 0) break;
+      if (a.causal && i == j) continue;
+      atomicAdd(&lcnt[i], 1);
+      ++slot;
+    }
+  }
+  __syncthreads();
+  int32_t* dst = a.hist + (int64_t)hk * n * a.gate_wg + w;
+  for (int64_t i = tid; i < n; i += 256) dst[i * a.gate_wg] = lcnt[i];
+}
+
+int launch_dispatch_from_sel(const DispatchArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)a.gate_wg, (unsigned)a.hkv), dim3(256), (size_t)a.n * sizeof(int32_t),
+                     st, a);
+  if (hipGetLastError() != hipSuccess) return -1;
+  return launch_dispatch(a, st);
+}
+
 int launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   const int64_t lists = (int64_t)a.hkv * a.n;
   hipLaunchKernelGGL(list_scan_kernel, dim3((unsigned)lists), dim3(1024), 0, st, a.hist, a.count, a.gate_wg);

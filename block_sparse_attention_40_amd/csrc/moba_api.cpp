@@ -118,6 +118,66 @@ int make_decode_plan(int64_t batch, int64_t lmax, int32_t hq, int32_t hkv, int32
   return MOBA_OK;
 }
 
+// Backward: sizes and the workspace carve-up (bf16, head dim 128).
+constexpr uint64_t kBwdPartialCapBytes = 2ull << 30;  // per-chunk dq contributions
+struct BwdPlan {
+  Plan p;
+  int32_t kps;              // dq slots per row: kp past + 1 own (causal)
+  int64_t gate_wg_f;        // rows-per-work-group units of the whole sequence
+  int64_t max_tiles_f;
+  int64_t chunk;            // query positions per dq chunk (whole blocks)
+  int64_t gate_wg_c, max_tiles_c;
+  size_t off_lse2, off_delta, off_kimg, off_vtmp, off_vkimg, off_kvimg;
+  size_t off_hist_f, off_count_f, off_listoff_f, off_tiles_f, off_entries_f;
+  size_t off_hist_c, off_count_c, off_listoff_c, off_tiles_c, off_entries_c, off_dqp, total;
+};
+
+int make_bwd_plan(const Shape& s, BwdPlan* out) {
+  BwdPlan b{};
+  const int st = make_plan(s, &b.p);
+  if (st != MOBA_OK) return st;
+  if (s.dtype != MOBA_DTYPE_BF16) return MOBA_ERR_DTYPE;  // the backward runs on bf16 MFMA
+  if (s.block % 64 != 0) return MOBA_ERR_SHAPE;            // whole 64-key slices
+  const Plan& p = b.p;
+  b.kps = p.kp + (s.causal ? 1 : 0);
+  const int64_t S = s.seqlen, rows = s.batch * S * s.hq, lists = (int64_t)s.hkv * p.n;
+  b.gate_wg_f = (S + p.gate_t - 1) / p.gate_t;
+  b.max_tiles_f = ((S * s.hq * (int64_t)std::max(p.kp, 0) + 255) / 256 + lists + 7) / 8 * 8;
+  const uint64_t per_block = (uint64_t)s.block * s.hq * b.kps * 128 * 4;
+  int64_t cb = (int64_t)std::max<uint64_t>(1, kBwdPartialCapBytes / per_block);
+  cb = std::min<int64_t>(cb, p.n);
+  b.chunk = cb * s.block;
+  b.gate_wg_c = (b.chunk + p.gate_t - 1) / p.gate_t;
+  b.max_tiles_c = ((b.chunk * s.hq * (int64_t)std::max(p.kp, 0) + 255) / 256 + lists + 7) / 8 * 8;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  const size_t img = (size_t)s.batch * S * s.hkv * 128 * 2;
+  b.off_lse2 = take(rows * 4);
+  b.off_delta = take(rows * 4);
+  b.off_kimg = take(img);
+  b.off_vtmp = take(img);
+  b.off_vkimg = take(img);
+  b.off_kvimg = take(img);
+  b.off_hist_f = take((size_t)lists * b.gate_wg_f * 4);
+  b.off_count_f = take((size_t)lists * 4);
+  b.off_listoff_f = take((size_t)(lists + 1) * 4);
+  b.off_tiles_f = take((size_t)(8 + 2 * b.max_tiles_f) * 4);
+  b.off_entries_f = take((size_t)S * s.hq * std::max(p.kp, 1) * 4);
+  b.off_hist_c = take((size_t)lists * b.gate_wg_c * 4);
+  b.off_count_c = take((size_t)lists * 4);
+  b.off_listoff_c = take((size_t)(lists + 1) * 4);
+  b.off_tiles_c = take((size_t)(8 + 2 * b.max_tiles_c) * 4);
+  b.off_entries_c = take((size_t)b.chunk * s.hq * std::max(p.kp, 1) * 4);
+  b.off_dqp = take((size_t)b.chunk * s.hq * b.kps * 128 * 4);
+  b.total = off;
+  *out = b;
+  return MOBA_OK;
+}
+
 float scale_log2_for(int d) {
   // log2(e) / sqrt(D): the softmax scale 1/sqrt(D) folded into base-2 exponentials
   return (float)(1.4426950408889634 / std::sqrt((double)d));
@@ -187,18 +247,15 @@ int moba_workspace_bytes(int64_t batch, int64_t seqlen, int32_t num_q_heads, int
   return MOBA_OK;
 }
 
-int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, int64_t seqlen,
-                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
-                  int32_t block_size, int32_t topk, int32_t causal, void* out, int32_t* sel_idx,
-                  void* workspace, size_t workspace_bytes, void* stream) {
-  return moba_attn_fwd_gate(q, k, v, batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
-                            causal, MOBA_GATE_MEAN, out, sel_idx, workspace, workspace_bytes, stream);
-}
+}  // extern "C"
 
-int moba_attn_fwd_gate(const void* q, const void* k, const void* v, int64_t batch, int64_t seqlen,
-                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
-                       int32_t block_size, int32_t topk, int32_t causal, int32_t gate_kind, void* out,
-                       int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// The forward behind moba_attn_fwd, moba_attn_fwd_gate and moba_attn_fwd_train.
+int fwd_impl(const void* q, const void* k, const void* v, int64_t batch, int64_t seqlen, int32_t num_q_heads,
+             int32_t num_kv_heads, int32_t head_dim, int32_t dtype, int32_t block_size, int32_t topk, int32_t causal,
+             int32_t gate_kind, void* out, int32_t* sel_idx, float* lse, void* workspace, size_t workspace_bytes,
+             void* stream) {
   if (gate_kind != MOBA_GATE_MEAN && gate_kind != MOBA_GATE_MINMAX) return MOBA_ERR_SHAPE;
   const bool minmax = gate_kind == MOBA_GATE_MINMAX;
   Plan p;
@@ -300,7 +357,7 @@ int moba_attn_fwd_gate(const void* q, const void* k, const void* v, int64_t batc
         fa.sel = sel_base; fa.sel_stride_h = sel_stride_h; fa.sel_pos_base = sel_pos_base;
         fa.seqlen = seqlen; fa.t0 = t0; fa.cnt = cnt; fa.hq = num_q_heads; fa.hkv = num_kv_heads;
         fa.d = head_dim; fa.block = block_size; fa.topk = topk; fa.causal = causal ? 1 : 0; fa.g = p.g;
-        fa.bb = (int32_t)bb; fa.scale_log2 = sl2;
+        fa.bb = (int32_t)bb; fa.scale_log2 = sl2; fa.lse = lse;
         StageScope sc(MOBA_STAGE_F32, s, 4.0 * D * (past_rows * block_size + own_keys));
         if (launch_attn_f32(fa, s)) return MOBA_ERR_HIP;
         continue;
@@ -334,7 +391,7 @@ int moba_attn_fwd_gate(const void* q, const void* k, const void* v, int64_t batc
       oa.q = q; oa.k = k; oa.v = v; oa.out = out; oa.part_o = part_o; oa.part_lse = part_lse;
       oa.seqlen = seqlen; oa.n = p.n; oa.t0 = t0; oa.cnt = cnt; oa.hq = num_q_heads; oa.hkv = num_kv_heads;
       oa.block = block_size; oa.kp = p.kp; oa.g = p.g; oa.own_t = p.own_t; oa.bb = (int32_t)bb;
-      oa.causal = causal ? 1 : 0; oa.scale_log2 = sl2; oa.kimg = kimg; oa.vimg = vimg;
+      oa.causal = causal ? 1 : 0; oa.scale_log2 = sl2; oa.kimg = kimg; oa.vimg = vimg; oa.lse = lse;
       {
         StageScope sc(MOBA_STAGE_OWN, s, 4.0 * D * own_keys);
         if (launch_attn_own(oa, s)) return MOBA_ERR_HIP;
@@ -342,6 +399,36 @@ int moba_attn_fwd_gate(const void* q, const void* k, const void* v, int64_t batc
     }
   }
   return MOBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, int64_t seqlen,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                  int32_t block_size, int32_t topk, int32_t causal, void* out, int32_t* sel_idx,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk, causal,
+                  MOBA_GATE_MEAN, out, sel_idx, nullptr, workspace, workspace_bytes, stream);
+}
+
+int moba_attn_fwd_gate(const void* q, const void* k, const void* v, int64_t batch, int64_t seqlen,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                       int32_t block_size, int32_t topk, int32_t causal, int32_t gate_kind, void* out,
+                       int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk, causal,
+                  gate_kind, out, sel_idx, nullptr, workspace, workspace_bytes, stream);
+}
+
+int moba_attn_fwd_train(const void* q, const void* k, const void* v, int64_t batch, int64_t seqlen,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                        int32_t block_size, int32_t topk, int32_t causal, void* out, int32_t* sel_idx, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!sel_idx || !lse) return MOBA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return MOBA_ERR_ALIGN;
+  return fwd_impl(q, k, v, batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk, causal,
+                  MOBA_GATE_MEAN, out, sel_idx, lse, workspace, workspace_bytes, stream);
 }
 
 int moba_meanpool(const void* k, int64_t batch, int64_t seqlen, int32_t num_kv_heads, int32_t head_dim,
@@ -464,6 +551,116 @@ int moba_decode_means(const void* k_cache, const int32_t* cache_lens, int64_t ba
   if (launch_decode_means(k_cache, cache_lens, mu_cache, dtype, batch, max_len, p.nmax, num_kv_heads, head_dim,
                           block_size, reinterpret_cast<hipStream_t>(stream)))
     return MOBA_ERR_HIP;
+  return MOBA_OK;
+}
+
+int moba_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t dtype, int32_t block_size, int32_t topk, int32_t causal,
+                             size_t* bytes) {
+  if (!bytes) return MOBA_ERR_NULL;
+  BwdPlan b;
+  const int st = make_bwd_plan(Shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
+                                     causal ? 1 : 0},
+                               &b);
+  if (st != MOBA_OK) return st;
+  *bytes = b.total;
+  return MOBA_OK;
+}
+
+int moba_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                  const int32_t* sel_idx, int64_t batch, int64_t seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t dtype, int32_t block_size, int32_t topk, int32_t causal, void* dq,
+                  void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  BwdPlan b;
+  const int st = make_bwd_plan(Shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
+                                     causal ? 1 : 0},
+                               &b);
+  if (st != MOBA_OK) return st;
+  const Plan& p = b.p;
+  if (!q || !k || !v || !out || !dout || !lse || !sel_idx || !dq || !dk || !dv) return MOBA_ERR_NULL;
+  if (!workspace || workspace_bytes < b.total) return MOBA_ERR_WORKSPACE;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(dout) || misaligned(dq) ||
+      misaligned(dk) || misaligned(dv) || misaligned(workspace) || (reinterpret_cast<uintptr_t>(lse) & 3u) ||
+      (reinterpret_cast<uintptr_t>(sel_idx) & 3u))
+    return MOBA_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  const int64_t S = seqlen, D = head_dim;
+  float* lse2 = reinterpret_cast<float*>(ws + b.off_lse2);
+  float* delta = reinterpret_cast<float*>(ws + b.off_delta);
+  uint16_t* kimg = reinterpret_cast<uint16_t*>(ws + b.off_kimg);
+  uint16_t* vtmp = reinterpret_cast<uint16_t*>(ws + b.off_vtmp);
+  uint16_t* vkimg = reinterpret_cast<uint16_t*>(ws + b.off_vkimg);
+  uint16_t* kvimg = reinterpret_cast<uint16_t*>(ws + b.off_kvimg);
+  {
+    StageScope sc(MOBA_STAGE_BWD_PREP, s, (double)batch * S * num_q_heads * D * 2.0 * 2.0 +
+                                              4.0 * batch * S * num_kv_heads * D * 2.0 * 2.0);
+    if (launch_bwd_prep(out, dout, lse, lse2, delta, batch, S, num_q_heads, s)) return MOBA_ERR_HIP;
+    // K and V in both operand layouts: (K layout of K, V^T layout of V) and (K layout of V, V^T layout of K)
+    if (launch_kv_image(k, v, batch, S, num_kv_heads, kimg, vtmp, s)) return MOBA_ERR_HIP;
+    if (launch_kv_image(v, k, batch, S, num_kv_heads, vkimg, kvimg, s)) return MOBA_ERR_HIP;
+  }
+  BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse2 = lse2; a.delta = delta;
+  a.kimg = kimg; a.vkimg = vkimg; a.kvimg = kvimg;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dq_part = reinterpret_cast<float*>(ws + b.off_dqp);
+  a.seqlen = S; a.n = p.n; a.hq = num_q_heads; a.hkv = num_kv_heads; a.block = block_size; a.kp = p.kp;
+  a.kps = b.kps; a.g = p.g; a.causal = causal ? 1 : 0;
+  a.scale_log2 = scale_log2_for(head_dim);
+  a.scale = (float)(1.0 / std::sqrt((double)head_dim));
+  const double own_pairs_per_block = causal ? (double)num_q_heads * block_size * (block_size + 1) / 2.0 : 0.0;
+  for (int64_t bb = 0; bb < batch; ++bb) {
+    a.bb = (int32_t)bb;
+    const int32_t* sel_b = sel_idx + bb * (int64_t)num_q_heads * S * topk;
+    DispatchArgs da{};
+    da.sel = sel_b; da.sel_stride_h = S * (int64_t)topk; da.sel_pos_base = 0;
+    da.n = p.n; da.hq = num_q_heads; da.hkv = num_kv_heads; da.block = block_size; da.topk = topk; da.kp = p.kp;
+    da.causal = causal ? 1 : 0; da.g = p.g; da.gate_t = p.gate_t; da.tile_rows = 256;
+    // whole-sequence lists for dk / dv
+    a.count_f = reinterpret_cast<int32_t*>(ws + b.off_count_f);
+    a.listoff_f = reinterpret_cast<int32_t*>(ws + b.off_listoff_f);
+    a.entries_f = reinterpret_cast<int32_t*>(ws + b.off_entries_f);
+    if (p.kp > 0) {
+      StageScope sc(MOBA_STAGE_DISPATCH, s, (double)S * num_q_heads * topk * 4.0 * 3.0);
+      DispatchArgs df = da;
+      df.hist = reinterpret_cast<int32_t*>(ws + b.off_hist_f);
+      df.count = const_cast<int32_t*>(a.count_f);
+      df.listoff = const_cast<int32_t*>(a.listoff_f);
+      df.tiles = reinterpret_cast<int32_t*>(ws + b.off_tiles_f);
+      df.entries = const_cast<int32_t*>(a.entries_f);
+      df.t0 = 0; df.cnt = S; df.gate_wg = b.gate_wg_f;
+      if (launch_dispatch_from_sel(df, s)) return MOBA_ERR_HIP;
+    }
+    {
+      const double pairs = past_blocks_sum(p, 0, S) * num_q_heads * block_size + own_pairs_per_block * p.n;
+      StageScope sc(MOBA_STAGE_BWD_DKDV, s, 8.0 * D * pairs);
+      if (launch_bwd_dkdv(a, s)) return MOBA_ERR_HIP;
+    }
+    for (int64_t t0 = 0; t0 < S; t0 += b.chunk) {
+      const int64_t cnt = std::min<int64_t>(b.chunk, S - t0);
+      a.t0 = t0; a.cnt = cnt;
+      a.tiles = reinterpret_cast<int32_t*>(ws + b.off_tiles_c);
+      a.count = reinterpret_cast<int32_t*>(ws + b.off_count_c);
+      a.listoff = reinterpret_cast<int32_t*>(ws + b.off_listoff_c);
+      a.entries = reinterpret_cast<int32_t*>(ws + b.off_entries_c);
+      if (p.kp > 0) {
+        StageScope sc(MOBA_STAGE_DISPATCH, s, (double)cnt * num_q_heads * topk * 4.0 * 3.0);
+        DispatchArgs dc = da;
+        dc.hist = reinterpret_cast<int32_t*>(ws + b.off_hist_c);
+        dc.count = const_cast<int32_t*>(a.count);
+        dc.listoff = const_cast<int32_t*>(a.listoff);
+        dc.tiles = const_cast<int32_t*>(a.tiles);
+        dc.entries = const_cast<int32_t*>(a.entries);
+        dc.t0 = t0; dc.cnt = cnt; dc.gate_wg = (cnt + p.gate_t - 1) / p.gate_t;
+        if (launch_dispatch_from_sel(dc, s)) return MOBA_ERR_HIP;
+      }
+      const double pairs = past_blocks_sum(p, t0, cnt) * num_q_heads * block_size +
+                           own_pairs_per_block * (double)(cnt / block_size);
+      StageScope sc(MOBA_STAGE_BWD_DQ, s, 6.0 * D * pairs);
+      if (launch_bwd_dq(a, p.kp > 0 ? b.max_tiles_c : 0, s)) return MOBA_ERR_HIP;
+    }
+  }
   return MOBA_OK;
 }
 

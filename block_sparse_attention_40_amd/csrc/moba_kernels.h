@@ -64,6 +64,7 @@ struct OwnArgs {
   const float* part_lse;
   const uint16_t* kimg;    // K / V^T slice images, or null
   const uint16_t* vimg;
+  float* lse;              // [batch, hq, seqlen] row log-sum-exp (natural log), or null
   int64_t seqlen, n, t0, cnt;
   int32_t hq, hkv, block, kp, g, own_t, bb, causal;
   float scale_log2;
@@ -79,6 +80,7 @@ struct F32Args {
   int64_t sel_stride_h;
   int64_t sel_pos_base;
   int64_t seqlen, t0, cnt;
+  float* lse;            // [batch, hq, seqlen] row log-sum-exp (natural log), or null
   int32_t hq, hkv, d, block, topk, causal, g, bb;
   float scale_log2;
 };
@@ -113,6 +115,48 @@ int launch_decode_stage(const DecodeArgs& a, int dtype, int stage, hipStream_t s
 // Block means of every complete block of the cache.
 int launch_decode_means(const void* k, const int32_t* lens, float* mu, int dtype, int64_t batch, int64_t lmax,
                         int64_t nmax, int hkv, int d, int block, hipStream_t stream);
+
+// Backward (bf16, head dim 128).  Rows are (batch, position, query head),
+// row index (b * seqlen + t) * hq + h.
+struct BwdArgs {
+  const void* q;           // [batch, seqlen, hq, 128] bf16
+  const void* k;           // [batch, seqlen, hkv, 128]
+  const void* v;
+  const void* dout;        // like q
+  const float* lse2;       // [rows] row log-sum-exp of the scaled logits, base 2
+  const float* delta;      // [rows] dout . out
+  // query-chunk dispatch (dq): as DispatchArgs, 256-row tiles
+  const int32_t* tiles;
+  const int32_t* count;
+  const int32_t* listoff;
+  const int32_t* entries;
+  // whole-sequence lists (dk, dv)
+  const int32_t* count_f;
+  const int32_t* listoff_f;
+  const int32_t* entries_f;
+  const uint16_t* kimg;    // K in the K slice-image layout
+  const uint16_t* vkimg;   // V in the K slice-image layout
+  const uint16_t* kvimg;   // K in the V^T slice-image layout
+  float* dq_part;          // [chunk rows, kps, 128] per (row, slot) dq contributions
+  void* dq;                // [batch, seqlen, hq, 128] bf16
+  void* dk;                // [batch, seqlen, hkv, 128] bf16
+  void* dv;
+  int64_t seqlen, n, t0, cnt;
+  int32_t hq, hkv, block, kp, kps, g, bb, causal;
+  float scale_log2;        // log2(e) / sqrt(D)
+  float scale;             // 1 / sqrt(D)
+};
+// delta = rowsum(dout * out) and lse2 = lse * log2(e), all rows.
+int launch_bwd_prep(const void* out, const void* dout, const float* lse, float* lse2, float* delta, int64_t batch,
+                    int64_t seqlen, int hq, hipStream_t stream);
+// dq contributions of one query chunk: the chunk's list tiles (max_tiles
+// work-groups) and, causal, its own blocks; then their sum into dq.
+int launch_bwd_dq(const BwdArgs& a, int64_t max_tiles, hipStream_t stream);
+// dk and dv of all keys of batch entry a.bb.
+int launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+// Per gate-work-group list counts from a given selection (the gate's side
+// output when the gate has not run), then the dispatch.
+int launch_dispatch_from_sel(const DispatchArgs& a, hipStream_t stream);
 
 // K and V^T images of all 64-key slices (bf16 path, seqlen % 64 == 0).
 int launch_kv_image(const void* k, const void* v, int64_t batch, int64_t seqlen, int hkv, uint16_t* kimg,

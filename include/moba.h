@@ -165,6 +165,50 @@ int moba_gate(const void* q, const float* mu, int64_t batch, int64_t seqlen,
               int32_t* sel_idx, void* stream);
 
 /*
+ * moba_attn_fwd_train: moba_attn_fwd (mean gate) that also writes, for the
+ * backward, lse[b, h, t] = log sum_{attended keys s} exp(q.k_s / sqrt(D))
+ * (natural log), fp32 [batch, Hq, seqlen].  sel_idx and lse are required.
+ */
+int moba_attn_fwd_train(const void* q, const void* k, const void* v,
+                        int64_t batch, int64_t seqlen, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                        int32_t block_size, int32_t topk, int32_t causal,
+                        void* out, int32_t* sel_idx, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward.  The gate is a hard top-k with no parameters (report §2.2): it
+ * only picks each row's keys, and no gradient flows through the choice.  With
+ * the forward's choice (sel_idx) held fixed each row is softmax attention over
+ * its keys, and the gradients of sum(dout * out) are (p = exp(q.k_s / sqrt(D)
+ * - lse), delta = dout . out):
+ *   dv_s += p_s dout,  ds_s = p_s (dout . v_s - delta),
+ *   dq = sum_s ds_s k_s / sqrt(D),  dk_s += ds_s q / sqrt(D).
+ * The pages train with MoBA (report §3.3) but print no backward; this is the
+ * gradient of the forward as computed.
+ *
+ * Inputs: q, k, v, out, dout as for moba_attn_fwd (out and dout like q); lse
+ * and sel_idx as written by moba_attn_fwd_train with the same shapes.
+ * Outputs: dq like q, dk and dv like k, written in full (every key gets its
+ * gradient, zero for a key no row attends).  bf16 only (MOBA_ERR_DTYPE for
+ * fp32), head_dim 128, block_size a multiple of 64 (MOBA_ERR_SHAPE).
+ * dk and dv are summed over rows in an order that can vary between runs
+ * (fp32 accumulation, then one bf16 rounding).  Workspace: at least
+ * moba_bwd_workspace_bytes(); nothing is allocated.  Stream-ordered.
+ */
+int moba_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                             int32_t block_size, int32_t topk, int32_t causal,
+                             size_t* bytes);
+int moba_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                  const void* dout, const float* lse, const int32_t* sel_idx,
+                  int64_t batch, int64_t seqlen, int32_t num_q_heads,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                  int32_t block_size, int32_t topk, int32_t causal,
+                  void* dq, void* dk, void* dv,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode-time MoBA: one new query per sequence against its key/value cache.
  * The pages evaluate generation with full attention and name sparse decode
  * as future work (report §4.4, §6.3); here the new token of sequence b, at
@@ -245,7 +289,10 @@ enum moba_stage {
   MOBA_STAGE_DECODE_GATE = 7,   /* decode gate, top-k and union (work 0: */
   MOBA_STAGE_DECODE_ATTN = 8,   /*   the bytes read depend on the device-side cache */
   MOBA_STAGE_DECODE_MERGE = 9,  /*   lengths and are left to the caller) */
-  MOBA_NUM_STAGES = 10
+  MOBA_STAGE_BWD_PREP = 10,     /* backward: delta, base-2 lse, K/V images: bytes */
+  MOBA_STAGE_BWD_DKDV = 11,     /* backward dk, dv: FLOPs (8 D per attended key) */
+  MOBA_STAGE_BWD_DQ = 12,       /* backward dq: FLOPs (6 D per attended key) */
+  MOBA_NUM_STAGES = 13
 };
 int moba_profile_enable(int on);
 int moba_profile_read(double* ms, int64_t* launches, double* work, int32_t n);

@@ -1,0 +1,82 @@
+"""GPU parity of the MoBA backward (moba_attn_fwd_train + moba_attn_bwd,
+through the C ABI) against the fp64 oracle's moba_backward, run with the
+GPU's own selection (selection parity is the forward's test).
+
+Tolerance, per gradient tensor: max |gpu - oracle| <= 0.02 max|oracle| + 0.01.
+The bf16 path rounds P and dS to bf16 for the MFMAs (relative 2^-9 each),
+accumulates in fp32 and rounds each gradient to bf16 once (2^-9 relative)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_40_amd as M
+import moba_workloads as W
+import oracle.moba_oracle as O
+from parity_utils import to_np32
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small(name, b, S, Hq, Hkv, B, topk, causal=True, seed=17):
+    return W.Workload(name, "bf16", b, Hq, Hkv, S, 128, B, topk, causal=causal, seed=seed)
+
+
+def dout_for(w, device):
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed + 1000)
+    return torch.randn((w.batch, w.seqlen, w.num_q_heads, w.head_dim), generator=gen).to(torch.bfloat16).to(device)
+
+
+def check(name, got, ref):
+    err = float(np.abs(got.astype(np.float64) - ref).max())
+    scale = float(np.abs(ref).max())
+    say(f"[grad] {name}: max err {err:.3e}, max |ref| {scale:.3e}")
+    assert err <= 0.02 * scale + 0.01, (name, err, scale)
+
+
+def run(w):
+    say(f"[case] backward {w}")
+    q, k, v, _ = W.make_inputs(w, device="cpu")
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    do = dout_for(w, DEV)
+    out, sel, lse = M.moba_attn_fwd_train(q, k, v, w.block_size, w.topk, w.causal)
+    dq, dk, dv = M.moba_attn_bwd(q, k, v, out, do, lse, sel, w.block_size, w.topk, w.causal)
+    torch.cuda.synchronize()
+    rq, rk, rv, rl = O.moba_backward(to_np32(q), to_np32(k), to_np32(v), to_np32(do), w.block_size, w.topk,
+                                     w.causal, sel_idx=sel.cpu().numpy())
+    lerr = float(np.abs(lse.cpu().numpy().astype(np.float64) - rl).max())
+    say(f"[lse] max err {lerr:.3e}")
+    # the forward sums the bf16-rounded weights it multiplies V with (each
+    # within 2^-9 relative), so its log-sum-exp is within log(1 + 2^-9) of the
+    # exact one, plus fp32 rounding
+    assert lerr < 2.5e-3
+    check("dq", to_np32(dq), rq)
+    check("dk", to_np32(dk), rk)
+    check("dv", to_np32(dv), rv)
+
+
+CASES = [
+    small("gqa_b128_k3", 1, 1024, 4, 2, 128, 3),
+    small("mha_b64_k5", 1, 1024, 2, 2, 64, 5),
+    small("b256_k2", 1, 2048, 4, 1, 256, 2),
+    small("b192_k3", 1, 1536, 2, 1, 192, 3),
+    small("batch2", 2, 512, 2, 2, 128, 3),
+    small("topk1_own_only", 1, 512, 4, 2, 128, 1),
+    small("dense_topk_ge_n", 1, 512, 2, 1, 64, 9),
+    small("noncausal", 1, 512, 2, 2, 128, 3, causal=False),
+    small("g8", 1, 1024, 8, 1, 128, 4),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_backward_small(w):
+    run(w)
