@@ -504,6 +504,75 @@ def measure_decode(M, W, w, steps, warmup, log, cpu_seconds=0.0, dense=True):
     return line
 
 
+def measure_backward(M, W, w, steps, warmup, log):
+    """Training step of the attention: moba_attn_fwd_train, then
+    moba_attn_bwd with the forward's selection (dout seeded N(0,1)).  Useful
+    FLOPs: the forward's 4 D per attended key, the backward's 10 D (five
+    products: S and dP recomputed once, dV, dK, dQ)."""
+    import torch
+    t0 = time.perf_counter()
+    q, k, v, _ = W.make_inputs(w, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 1000)
+    dout = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(q.dtype)
+    dt = M.DTYPE_BF16
+    wsf = torch.empty(M.workspace_bytes(w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, dt,
+                                        w.block_size, w.topk, w.causal), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(M.bwd_workspace_bytes(w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, dt,
+                                            w.block_size, w.topk, w.causal), dtype=torch.uint8, device="cuda")
+    log(f"[bwd] {w.name}: inputs in {time.perf_counter() - t0:.1f}s, workspaces {wsf.numel() / 2**30:.2f} + "
+        f"{wsb.numel() / 2**30:.2f} GiB")
+    fwd = lambda: M.moba_attn_fwd_train(q, k, v, w.block_size, w.topk, w.causal, workspace=wsf)
+    out, sel, lse = fwd()
+    bwd = lambda: M.moba_attn_bwd(q, k, v, out, dout, lse, sel, w.block_size, w.topk, w.causal, workspace=wsb)
+    for _ in range(warmup):
+        bwd()
+    torch.cuda.synchronize()
+    res = {"workload": w.name}
+    for tag, fn in (("forward_train", fwd), ("backward", bwd)):
+        M.profile_read()
+        M.profile_enable(True)
+        torch.cuda.synchronize()
+        ts = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - ts) / steps * 1e3
+        M.profile_enable(False)
+        st = M.profile_read()
+        res[tag] = {"ms": ms, "stages": {n: {"ms": x["ms"] / steps, "launches": x["launches"] / steps,
+                                             "tflops": x["work"] / (x["ms"] * 1e-3) / 1e12
+                                             if x["ms"] > 0 and n.startswith(("attn", "bwd_d")) else None}
+                                         for n, x in st.items() if x["launches"]}}
+        if tag == "backward":
+            res["dkdv"] = st["bwd_dkdv"]
+            res["dq"] = st["bwd_dq"]
+        log(f"[bwd] {w.name} {tag}: {ms:.2f} ms")
+    fl = useful_flops(w)
+    bw = res["backward"]["ms"]
+    dkdv = res.pop("dkdv")
+    dq = res.pop("dq")
+    dk_ms = dkdv["ms"] / steps / max(dkdv["launches"] / steps, 1)
+    line = {
+        "metric": "MoBA attention backward useful TFLOP/s (10 D per attended key)",
+        "value": 2.5 * fl / (bw * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": bw, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), bf16-rounded; no dataset)",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "topk": w.topk, "causal": w.causal},
+        "forward_train_ms": res["forward_train"]["ms"],
+        "train_step_ms": res["forward_train"]["ms"] + bw,
+        "train_step_useful_tflops": 3.5 * fl / ((res["forward_train"]["ms"] + bw) * 1e-3) / 1e12,
+        "stages": res["backward"]["stages"],
+        "roofline": {"bound": "mfma", "kernel": "moba::bwd_dkdv_kernel", "achieved": dkdv["work"] / steps /
+                     (dkdv["ms"] / steps * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "avg_launch_ms": dk_ms, "traffic": None},
+    }
+    line["roofline"]["frac"] = line["roofline"]["achieved"] / PEAK_BF16_TFLOPS
+    return line
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -519,6 +588,8 @@ def main():
                     help="block gate: block means (the method's) or element-wise key min / max")
     ap.add_argument("--decode", nargs="?", const="decode_gqa32x8_1m_b8", default=None, metavar="WORKLOAD",
                     help="measure decode-time MoBA on a decode workload instead, then exit")
+    ap.add_argument("--backward", nargs="?", const="gqa32x8_128k", default=None, metavar="WORKLOAD",
+                    help="measure the attention training step (forward with lse, backward) instead, then exit")
     ap.add_argument("--decode-skip-dense", action="store_true",
                     help="with --decode: skip the dense-decode comparison")
     ap.add_argument("--summarize-decode-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
@@ -560,6 +631,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.backward:
+        print(json.dumps(measure_backward(M, W, W.WORKLOADS[args.backward], args.steps, args.warmup, log)),
+              flush=True)
+        return
     if args.decode:
         print(json.dumps(measure_decode(M, W, W.DECODE_WORKLOADS[args.decode], args.steps, args.warmup, log,
                                         0.0 if args.no_cpu_baseline else min(args.cpu_seconds, 10.0),

@@ -326,47 +326,65 @@ __global__ __launch_bounds__(kKvWaves * 64) void bwd_dkdv_kernel(BwdArgs a) {
   const int64_t nrows = npast + nown;
   const int64_t nsteps = (nrows + RSTEP - 1) / RSTEP;
 
-  // staging: 32 rows x 16 units x 2 tensors = 1024 units
+  // Staging: 32 rows x 16 units x 2 tensors = 1024 units per step.  The
+  // loads of step s + 2 are issued during step s (two steps to arrive), the
+  // list entries that locate them during step s - 1.
   constexpr int SU = 512 / kKvThreads;  // units per thread and tensor
-  u32x4 sq[SU], sd[SU];
-  int64_t sgrow[SU];
-  int32_t st_pos[SU];
-  bool sval[SU];
-  auto row_of = [&](int64_t rix, int64_t& grow, int32_t& pos) {
-    if (rix < npast) {
-      const int32_t entry = a.entries_f[lbeg + rix];
-      const int64_t lr = entry / a.kp;  // whole-sequence list: row = position * hq + head
-      grow = bS * a.hq + lr;
-      pos = (int32_t)(lr / a.hq);
-    } else {
-      const int64_t o = rix - npast;
-      const int64_t p = own_pos0 + o / a.g;
-      grow = (bS + p) * a.hq + hk * a.g + (int)(o % a.g);
-      pos = (int32_t)p;
+  struct Desc {
+    int32_t raw[SU];   // list entry (past rows) or own-row index
+    bool past[SU];
+    bool val[SU];
+  };
+  struct Stage {
+    u32x4 q[SU], d[SU];
+    float l[SU], dl[SU];
+    int32_t pos[SU];
+  };
+  // only loads here: the entries are decoded a step later, when they have
+  // arrived (a decode right after the load would wait for it)
+  auto desc_of = [&](int64_t step, Desc& D) {
+#pragma unroll
+    for (int x = 0; x < SU; ++x) {
+      const int row = (tid + kKvThreads * x) >> 4;
+      int64_t rix = step * RSTEP + row;
+      D.val[x] = rix < nrows;
+      if (!D.val[x]) rix = nrows - 1;  // padding rows repeat the last row (weight 0)
+      D.past[x] = rix < npast;
+      D.raw[x] = D.past[x] ? a.entries_f[lbeg + rix] : (int32_t)(rix - npast);
     }
   };
-  // thread unit x: row (tid + kKvThreads x) / 16, unit tid % 16
-  auto load_step = [&](int64_t step) {
+  auto load_stage = [&](const Desc& D, Stage& St) {
+#pragma unroll
+    for (int x = 0; x < SU; ++x) {
+      int64_t grow;
+      int32_t pos;
+      if (D.past[x]) {
+        const int32_t lr = D.raw[x] / a.kp;  // whole-sequence list: row = position * hq + head
+        pos = lr / a.hq;
+        grow = bS * a.hq + lr;
+      } else {
+        const int32_t p = (int32_t)own_pos0 + D.raw[x] / a.g;
+        pos = p;
+        grow = (bS + p) * a.hq + hk * a.g + D.raw[x] % a.g;
+      }
+      const int u = tid & 15;
+      St.q[x] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16raw*>(a.q) + grow * BD + u * 8);
+      St.d[x] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16raw*>(a.dout) + grow * BD + u * 8);
+      St.l[x] = D.val[x] ? a.lse2[grow] : __builtin_inff();  // padding rows: p = 0
+      St.dl[x] = a.delta[grow];
+      St.pos[x] = pos;
+    }
+  };
+  auto store_stage = [&](const Stage& St, int buf) {
 #pragma unroll
     for (int x = 0; x < SU; ++x) {
       const int row = (tid + kKvThreads * x) >> 4, u = tid & 15;
-      const int64_t rix = step * RSTEP + row;
-      sval[x] = rix < nrows;
-      row_of(sval[x] ? rix : nrows - 1, sgrow[x], st_pos[x]);
-      sq[x] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16raw*>(a.q) + sgrow[x] * BD + u * 8);
-      sd[x] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16raw*>(a.dout) + sgrow[x] * BD + u * 8);
-    }
-  };
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int x = 0; x < SU; ++x) {
-      const int row = (tid + kKvThreads * x) >> 4, u = tid & 15;
-      *reinterpret_cast<u32x4*>(rs[buf] + row_off(row, u)) = sq[x];
-      *reinterpret_cast<u32x4*>(rs[buf] + RTILE + row_off(row, u)) = sd[x];
+      *reinterpret_cast<u32x4*>(rs[buf] + row_off(row, u)) = St.q[x];
+      *reinterpret_cast<u32x4*>(rs[buf] + RTILE + row_off(row, u)) = St.d[x];
       if (u == 0) {
-        rl[buf][row] = sval[x] ? a.lse2[sgrow[x]] : __builtin_inff();  // padding rows: p = 0
-        rd[buf][row] = a.delta[sgrow[x]];
-        rt[buf][row] = st_pos[x];
+        rl[buf][row] = St.l[x];
+        rd[buf][row] = St.dl[x];
+        rt[buf][row] = St.pos[x];
       }
     }
   };
@@ -377,19 +395,7 @@ __global__ __launch_bounds__(kKvWaves * 64) void bwd_dkdv_kernel(BwdArgs a) {
   const int tr_r = 4 * lg + ((lane & 15) >> 2);
   const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // element offset inside a 32-dim tile
 
-  if (nsteps > 0) {
-    load_step(0);
-    store_step(0);
-  }
-  __syncthreads();
-  for (int64_t step = 0; step < nsteps; ++step) {
-    const int buf = (int)(step & 1);
-    if (step + 1 < nsteps) load_step(step + 1);
-    if (!wact) {
-      if (step + 1 < nsteps) store_step(buf ^ 1);
-      __syncthreads();
-      continue;
-    }
+  auto compute = [&](int buf) {
     const char* qs = rs[buf];
     const char* ds = rs[buf] + RTILE;
     // S = Q K^T and dP = dO V^T: M = row (lane % 32 reads its row), N = key
@@ -449,8 +455,33 @@ __global__ __launch_bounds__(kKvWaves * 64) void bwd_dkdv_kernel(BwdArgs a) {
         dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sA, qB, dk[dt], 0, 0, 0);
       }
     }
-    if (step + 1 < nsteps) store_step(buf ^ 1);
+  };
+
+  Desc D;
+  Stage SA, SB;
+  if (nsteps > 0) {
+    desc_of(0, D);
+    load_stage(D, SA);
+    store_stage(SA, 0);
+    if (nsteps > 1) {
+      desc_of(1, D);
+      load_stage(D, SA);  // step 1, stored at the end of step 0
+    }
+    if (nsteps > 2) desc_of(2, D);
+  }
+  __syncthreads();
+  // step s: X holds step s + 1, Y is free; D locates step s + 2
+  auto iter = [&](int64_t s, Stage& X, Stage& Y) {
+    if (s + 2 < nsteps) load_stage(D, Y);
+    if (s + 3 < nsteps) desc_of(s + 3, D);
+    if (wact) compute((int)(s & 1));
+    if (s + 1 < nsteps) store_stage(X, (int)((s + 1) & 1));
     __syncthreads();
+  };
+  for (int64_t s = 0; s < nsteps; s += 2) {
+    iter(s, SA, SB);
+    if (s + 1 >= nsteps) break;
+    iter(s + 1, SB, SA);
   }
 
   if (!wact) return;
