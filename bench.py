@@ -334,31 +334,41 @@ def summarize_trace(trace_dir, bench_json, out_path):
         fh.write("\n".join(out) + "\n")
 
 
-def curve(M, W, lengths, log, budget_s=4.0):
+def curve(M, W, lengths, log, budget_s=4.0, moba_only=False):
     """Speedup of MoBA over dense causal attention, both from this library
     (report §4.5: the attention layer forward only, MoBA with the block count
     and top-k fixed, n = 256 blocks and top-12, so the block size grows with
     the sequence; dense = block_size = seqlen, topk = 1: one causal block).
-    One JSON line per length; steps adapt to about budget_s of GPU time."""
+    One JSON line per length; steps adapt to about budget_s of GPU time.
+    moba_only: skip the dense side (10M positions: about 13 minutes of dense
+    attention), and when one call exceeds the budget, time a single call
+    after one untimed call."""
     import torch
     out_lines = []
     for S in lengths:
         res = {"seqlen": S}
-        for tag, w in (("moba", W.Workload(f"gqa32x8_{S}_moba", "bf16", 1, 32, 8, S, 128, S // 256, 12, seed=1100)),
-                       ("dense", W.Workload(f"gqa32x8_{S}_dense", "bf16", 1, 32, 8, S, 128, S, 1, seed=1100))):
+        sides = (("moba", W.Workload(f"gqa32x8_{S}_moba", "bf16", 1, 32, 8, S, 128, S // 256, 12, seed=1100)),
+                 ("dense", W.Workload(f"gqa32x8_{S}_dense", "bf16", 1, 32, 8, S, 128, S, 1, seed=1100)))
+        for tag, w in sides[:1 if moba_only else 2]:
+            t_in = time.perf_counter()
             q, k, v, _ = W.make_inputs(w, device="cuda")
+            log(f"[curve] S={S} {tag}: inputs in {time.perf_counter() - t_in:.1f}s")
             out = torch.empty_like(q)
             nbytes = M.workspace_bytes(1, S, 32, 8, 128, M.DTYPE_BF16, w.block_size, w.topk, True)
             ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
             call = lambda: M.moba_attn_fwd(q, k, v, w.block_size, w.topk, True, out=out, workspace=ws,
                                            return_sel=False)
-            call()
-            torch.cuda.synchronize()
             t0 = time.perf_counter()
             call()
             torch.cuda.synchronize()
-            one = time.perf_counter() - t0
-            steps = max(1, min(20, int(budget_s / max(one, 1e-6))))
+            log(f"[curve] S={S} {tag}: untimed call {time.perf_counter() - t0:.1f}s")
+            one = 0.0
+            if not moba_only:
+                t0 = time.perf_counter()
+                call()
+                torch.cuda.synchronize()
+                one = time.perf_counter() - t0
+            steps = max(1, min(20, int(budget_s / max(one, 1e-6)))) if one > 0 else 1
             M.profile_read()
             M.profile_enable(True)
             t0 = time.perf_counter()
@@ -375,7 +385,8 @@ def curve(M, W, lengths, log, budget_s=4.0):
             log(f"[curve] S={S} {tag}: {ms:.3f} ms ({steps} steps)")
             del q, k, v, out, ws
             torch.cuda.empty_cache()
-        res["speedup"] = res["dense"]["ms"] / res["moba"]["ms"]
+        if not moba_only:
+            res["speedup"] = res["dense"]["ms"] / res["moba"]["ms"]
         print(json.dumps(res), flush=True)
         out_lines.append(res)
     return out_lines
@@ -596,6 +607,8 @@ def main():
                     help="write the decode kernel-trace summary from a rocprofv3 --stats run, then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain copy of MIB MiB first (reference dispatch for HBM byte counters)")
+    ap.add_argument("--curve-moba-only", action="store_true",
+                    help="with --curve: MoBA side only (for lengths where dense attention takes minutes)")
     ap.add_argument("--curve", nargs="*", type=int, metavar="SEQLEN",
                     help="MoBA (256 blocks, top-12) vs dense causal attention at these lengths, one JSON line each")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -642,7 +655,8 @@ def main():
               flush=True)
         return
     if args.curve is not None:
-        curve(M, W, args.curve or [32768, 65536, 131072, 262144, 524288, 1048576], log)
+        curve(M, W, args.curve or [32768, 65536, 131072, 262144, 524288, 1048576], log,
+              moba_only=args.curve_moba_only)
         return
     w = W.WORKLOADS[args.workload]
     if args.copy_calibration:
