@@ -20,9 +20,12 @@
 //                    Own-block tiles (causal) mask keys after the row.  Each
 //                    (row, slot) writes its dq contribution (fp32); a merge
 //                    adds a row's contributions.
-//   bwd_dkdv_kernel  key-stationary: one work-group per 128 keys of one block
-//                    (4 waves x 32 keys, the keys' K and V rows held in
-//                    registers); it walks every row that attends the block
+//   bwd_dkdv_kernel  key-stationary: one work-group per 128 keys of one block,
+//                    two waves per 32-key group: one computes S = Q K^T, P
+//                    and dV, the other dP = dO V^T, dS (with P handed over
+//                    through LDS) and dK, so each wave holds one operand and
+//                    one accumulator set (two waves per SIMD); it walks every
+//                    row that attends the block
 //                    (the block's whole-sequence list, then, causal, the
 //                    block's own rows at or after the slice) in steps of 32
 //                    rows staged in LDS, and accumulates
@@ -269,9 +272,9 @@ namespace {
 constexpr int RSTEP = 32;        // rows per step
 constexpr int RROW = BD * 2;     // bytes per staged row (16 units of 16 bytes)
 constexpr int RTILE = RSTEP * RROW;  // one staged tensor (8 KiB)
-constexpr int kKvWaves = 4;          // waves (32 keys each) per work-group
-constexpr int kKvKeys = 32 * kKvWaves;
-constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKvGroups = 4;         // key groups (32 keys each) per work-group
+constexpr int kKvKeys = 32 * kKvGroups;
+constexpr int kKvThreads = 2 * 64 * kKvGroups;  // two waves per key group
 
 // Position of 16-byte unit u of staged row r: a rotation per row that keeps
 // both the row-wise 16-byte operand reads (16 rows, one unit) and the
@@ -281,40 +284,43 @@ __device__ __forceinline__ int unit_pos(int r, int u) { return (u + 4 * (r & 3) 
 __device__ __forceinline__ int row_off(int r, int u) { return r * RROW + unit_pos(r, u) * 16; }
 }  // namespace
 
-__global__ __launch_bounds__(kKvWaves * 64) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char rs[2][2 * RTILE];  // [buffer][Q rows | dO rows]
   __shared__ __attribute__((aligned(16))) float rl[2][RSTEP];
   __shared__ __attribute__((aligned(16))) float rd[2][RSTEP];
   __shared__ __attribute__((aligned(16))) int32_t rt[2][RSTEP];
+  __shared__ __attribute__((aligned(16))) uint32_t pex[kKvGroups][64 * 8];  // P handed from P-wave to dS-wave
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 5;
+  const int kg = wave % kKvGroups;   // key group (32 keys)
+  const bool pw = wave < kKvGroups;  // P-wave (S, P, dV) or dS-wave (dP, dS, dK)
   const int hk = (int)blockIdx.y;
   const int spb = (a.block + kKvKeys - 1) / kKvKeys;  // work-groups per block
   const int64_t i = blockIdx.x / spb;
+  // (consecutive work-groups, one block's slices, go to different XCDs and
+  // read the block's rows at about the same time; measured slower: an order
+  // keeping a block on one XCD (2.4x: the early blocks' long lists then load
+  // a few XCDs) and one with the KV head fastest (4 %))
   const int64_t key0 = i * a.block + (int64_t)(blockIdx.x % spb) * kKvKeys;  // first key of the work-group
-  const int64_t wkey = key0 + wave * 32;                                  // first key of this wave
-  // a block of 64 or 128 keys leaves waves without keys (wave-uniform)
+  const int64_t wkey = key0 + kg * 32;                                    // first key of this wave's group
+  // a block of 64 keys leaves key groups without keys (wave-uniform)
   const bool wact = wkey < (i + 1) * a.block;
   const int64_t rowstride = (int64_t)a.hkv * BD;
   const int64_t bS = (int64_t)a.bb * a.seqlen;
 
-  // the wave's keys and values as B operands of S = Q K^T and dP = dO V^T:
-  // lane = key (l % 32), 8 dims at 8 lg + 16 s
-  bf16x8 kbv[8], vbv[8];
+  // the group's keys (P-wave) or values (dS-wave) as the B operand of
+  // S = Q K^T or dP = dO V^T: lane = key (l % 32), 8 dims at 8 lg + 16 s
+  bf16x8 kv[8];
   if (wact) {
     const int64_t key = wkey + (lane & 31);
-    const bf16raw* kr = reinterpret_cast<const bf16raw*>(a.k) + (bS + key) * rowstride + hk * BD + lg * 8;
-    const bf16raw* vr = reinterpret_cast<const bf16raw*>(a.v) + (bS + key) * rowstride + hk * BD + lg * 8;
+    const bf16raw* src = reinterpret_cast<const bf16raw*>(pw ? a.k : a.v) + (bS + key) * rowstride + hk * BD + lg * 8;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      kbv[s] = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
-      vbv[s] = *reinterpret_cast<const bf16x8*>(vr + 16 * s);
-    }
+    for (int s = 0; s < 8; ++s) kv[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
   }
-  f32x16 dk[4], dv[4];
+  f32x16 acc[4];  // dV (P-wave) or dK (dS-wave): M = key, N = dim
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { dk[b][e] = 0.f; dv[b][e] = 0.f; }
+    for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
 
   // rows: the block's list, then (causal) its own rows at or after key0
   const int64_t L = (int64_t)hk * a.n + i;
@@ -394,50 +400,68 @@ __global__ __launch_bounds__(kKvWaves * 64) void bwd_dkdv_kernel(BwdArgs a) {
   // a 16-row step and dims 32 dt + 16 ((l / 16) & 1) + 4 (l % 4) .. + 3
   const int tr_r = 4 * lg + ((lane & 15) >> 2);
   const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // element offset inside a 32-dim tile
+  const int32_t mykey = (int32_t)(wkey + (lane & 31));       // position of this lane's key
+  uint32_t* myex = pex[kg] + lane * 8;
 
-  auto compute = [&](int buf) {
-    const char* qs = rs[buf];
-    const char* ds = rs[buf] + RTILE;
-    // S = Q K^T and dP = dO V^T: M = row (lane % 32 reads its row), N = key
-    f32x16 s, dp;
+  // phase 1: S (P-wave) or dP (dS-wave) = rows x this group's keys; the
+  // P-wave turns S into P and hands it over through LDS
+  auto phase1 = [&](int buf, f32x16& x) {
+    const char* rowsrc = rs[buf] + (pw ? 0 : RTILE);  // Q rows or dO rows
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+    for (int e = 0; e < 16; ++e) x[e] = 0.f;
     const int ar = lane & 31;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + row_off(ar, lg + 2 * st));
-      const bf16x8 da = *reinterpret_cast<const bf16x8*>(ds + row_off(ar, lg + 2 * st));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kbv[st], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vbv[st], dp, 0, 0, 0);
+      const bf16x8 ra = *reinterpret_cast<const bf16x8*>(rowsrc + row_off(ar, lg + 2 * st));
+      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra, kv[st], x, 0, 0, 0);
     }
-    // lane = key wkey + lane % 32; element e = row acc_row(e, lg)
-    const int32_t mykey = (int32_t)(wkey + (lane & 31));  // position of this lane's key
-    uint32_t pa[8], sa[8];
+    if (pw) {
+      uint32_t pk[8];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      // rows 8 q4 + 4 lg + 0..3 are consecutive: one 16-byte read per array
-      const int r0 = 8 * q4 + 4 * lg;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&rl[buf][r0]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&rd[buf][r0]);
-      const u32x4 t4 = *reinterpret_cast<const u32x4*>(&rt[buf][r0]);
-      float p[4];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // rows 8 q4 + 4 lg + 0..3 are consecutive: one 16-byte read per array
+        const int r0 = 8 * q4 + 4 * lg;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&rl[buf][r0]);
+        const u32x4 t4 = *reinterpret_cast<const u32x4*>(&rt[buf][r0]);
+        float p[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        p[x] = fast_exp2(__builtin_fmaf(s[4 * q4 + x], c, -l4[x]));
-        if (a.causal && mykey > (int32_t)t4[x]) p[x] = 0.f;
+        for (int y = 0; y < 4; ++y) {
+          p[y] = fast_exp2(__builtin_fmaf(x[4 * q4 + y], c, -l4[y]));
+          if (a.causal && mykey > (int32_t)t4[y]) p[y] = 0.f;
+        }
+        pk[2 * q4] = pack_bf16x2(p[0], p[1]);
+        pk[2 * q4 + 1] = pack_bf16x2(p[2], p[3]);
       }
-      pa[2 * q4] = pack_bf16x2(p[0], p[1]);
-      pa[2 * q4 + 1] = pack_bf16x2(p[2], p[3]);
-      sa[2 * q4] = pack_bf16x2(p[0] * (dp[4 * q4] - d4[0]), p[1] * (dp[4 * q4 + 1] - d4[1]));
-      sa[2 * q4 + 1] = pack_bf16x2(p[2] * (dp[4 * q4 + 2] - d4[2]), p[3] * (dp[4 * q4 + 3] - d4[3]));
+      *reinterpret_cast<u32x4*>(myex) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      *reinterpret_cast<u32x4*>(myex + 4) = u32x4{pk[4], pk[5], pk[6], pk[7]};
     }
-    // dV += P^T dO and dK += dS^T Q: M = key, N = dim, K = row; the A
-    // operand of step st is elements 8 st .. 8 st + 7 (rows 16 st + 8 (j/4) +
-    // 4 lg + j % 4), the B operand the same rows of dO / Q read transposed
+  };
+  // phase 2: dV += P^T dO (P-wave) or dK += dS^T Q with dS = P (dP - delta)
+  // (dS-wave); M = key, N = dim, K = row, the row operand read transposed
+  auto phase2 = [&](int buf, const f32x16& x) {
+    uint32_t av[8];
+    {
+      const u32x4 p0 = *reinterpret_cast<const u32x4*>(myex);
+      const u32x4 p1 = *reinterpret_cast<const u32x4*>(myex + 4);
+      const uint32_t pk[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      if (pw) {
+#pragma unroll
+        for (int y = 0; y < 8; ++y) av[y] = pk[y];
+      } else {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int r0 = 8 * q4 + 4 * lg;
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&rd[buf][r0]);
+          av[2 * q4] = pack_bf16x2(bf16lo(pk[2 * q4]) * (x[4 * q4] - d4[0]), bf16hi(pk[2 * q4]) * (x[4 * q4 + 1] - d4[1]));
+          av[2 * q4 + 1] = pack_bf16x2(bf16lo(pk[2 * q4 + 1]) * (x[4 * q4 + 2] - d4[2]),
+                                       bf16hi(pk[2 * q4 + 1]) * (x[4 * q4 + 3] - d4[3]));
+        }
+      }
+    }
+    const char* tsrc = rs[buf] + (pw ? RTILE : 0);  // dO rows (for dV) or Q rows (for dK)
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const bf16x8 pA = __builtin_bit_cast(bf16x8, u32x4{pa[4 * st], pa[4 * st + 1], pa[4 * st + 2], pa[4 * st + 3]});
-      const bf16x8 sA = __builtin_bit_cast(bf16x8, u32x4{sa[4 * st], sa[4 * st + 1], sa[4 * st + 2], sa[4 * st + 3]});
+      const bf16x8 A = __builtin_bit_cast(bf16x8, u32x4{av[4 * st], av[4 * st + 1], av[4 * st + 2], av[4 * st + 3]});
       const int ra = 16 * st + tr_r, rb = ra + 8;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -445,14 +469,10 @@ __global__ __launch_bounds__(kKvWaves * 64) void bwd_dkdv_kernel(BwdArgs a) {
         const int oa = row_off(ra, col >> 3) + ((col >> 2) & 1) * 8;
         const int ob = row_off(rb, col >> 3) + ((col >> 2) & 1) * 8;
         typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        const s16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ds + oa));
-        const s16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ds + ob));
-        const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qs + oa));
-        const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qs + ob));
-        const bf16x8 dB = __builtin_bit_cast(bf16x8, __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7));
-        const bf16x8 qB = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
-        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pA, dB, dv[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sA, qB, dk[dt], 0, 0, 0);
+        const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tsrc + oa));
+        const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tsrc + ob));
+        const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[dt], 0, 0, 0);
       }
     }
   };
@@ -470,11 +490,16 @@ __global__ __launch_bounds__(kKvWaves * 64) void bwd_dkdv_kernel(BwdArgs a) {
     if (nsteps > 2) desc_of(2, D);
   }
   __syncthreads();
-  // step s: X holds step s + 1, Y is free; D locates step s + 2
+  // step s: X holds step s + 1, Y is free; D locates step s + 2.  Two
+  // barriers per step: after phase 1 (P handed over) and after phase 2.
   auto iter = [&](int64_t s, Stage& X, Stage& Y) {
+    const int buf = (int)(s & 1);
     if (s + 2 < nsteps) load_stage(D, Y);
     if (s + 3 < nsteps) desc_of(s + 3, D);
-    if (wact) compute((int)(s & 1));
+    f32x16 x;
+    if (wact) phase1(buf, x);
+    __syncthreads();
+    if (wact) phase2(buf, x);
     if (s + 1 < nsteps) store_stage(X, (int)((s + 1) & 1));
     __syncthreads();
   };
@@ -485,17 +510,14 @@ __global__ __launch_bounds__(kKvWaves * 64) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   if (!wact) return;
-  // C layout of dK, dV: lane = dim 32 dt + lane % 32, element e = key acc_row(e, lg)
-  bf16raw* dkp = reinterpret_cast<bf16raw*>(a.dk) + (bS + wkey) * rowstride + hk * BD + (lane & 31);
-  bf16raw* dvp = reinterpret_cast<bf16raw*>(a.dv) + (bS + wkey) * rowstride + hk * BD + (lane & 31);
+  // C layout of the accumulator: lane = dim 32 dt + lane % 32, element e = key acc_row(e, lg)
+  bf16raw* dst = reinterpret_cast<bf16raw*>(pw ? a.dv : a.dk) + (bS + wkey) * rowstride + hk * BD + (lane & 31);
+  const float f = pw ? 1.f : a.scale;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t off = (int64_t)acc_row(e, lg) * rowstride + 32 * dt;
-      dkp[off] = (bf16raw)(pack_bf16x2(dk[dt][e] * a.scale, 0.f) & 0xffffu);
-      dvp[off] = (bf16raw)(pack_bf16x2(dv[dt][e], 0.f) & 0xffffu);
-    }
+    for (int e = 0; e < 16; ++e)
+      dst[(int64_t)acc_row(e, lg) * rowstride + 32 * dt] = (bf16raw)(pack_bf16x2(acc[dt][e] * f, 0.f) & 0xffffu);
 }
 
 int launch_bwd_prep(const void* out, const void* dout, const float* lse, float* lse2, float* delta, int64_t batch,
