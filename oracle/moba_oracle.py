@@ -291,6 +291,41 @@ def moba_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
     return dq, dk, dv, lse
 
 
+def backward_dq_rows(q, k, v, dout, block_size: int, causal: bool,
+                     rows: Sequence[Tuple[int, int, int]],
+                     sels: Sequence[Sequence[int]]) -> Tuple[np.ndarray, np.ndarray]:
+    """dq and lse of single rows (b, t, h) with their chosen blocks given:
+    the same per-row formulas as moba_backward, for checking sampled rows of
+    large inputs (dq of a row depends on that row alone).  Arrays may be any
+    type with numpy indexing (a KV head is converted per row)."""
+    D = q.shape[3]
+    g = q.shape[2] // k.shape[2]
+    scale = 1.0 / math.sqrt(D)
+    dq = np.zeros((len(rows), D))
+    lse = np.zeros(len(rows))
+    order = sorted(range(len(rows)), key=lambda r: (rows[r][0], rows[r][2] // g, r))
+    cur = None
+    for r in order:
+        (bb, t, h), sel = rows[r], sels[r]
+        hk = h // g
+        if cur != (bb, hk):  # each (batch, KV head) converted once
+            cur = (bb, hk)
+            k_head = np.asarray(k[bb, :, hk, :], dtype=np.float64)
+            v_head = np.asarray(v[bb, :, hk, :], dtype=np.float64)
+        keys = key_positions([int(i) for i in sel if i >= 0], t, block_size, causal)
+        kk = k_head[keys]
+        vv = v_head[keys]
+        q64 = np.asarray(q[bb, t, h], dtype=np.float64)
+        do64 = np.asarray(dout[bb, t, h], dtype=np.float64)
+        logits = (kk @ q64) * scale
+        m = logits.max()
+        lse[r] = m + math.log(np.exp(logits - m).sum())
+        p = np.exp(logits - lse[r])
+        ds = p * (vv @ do64 - do64 @ (p @ vv))
+        dq[r] = scale * (ds @ kk)
+    return dq, lse
+
+
 # ----------------------------------------------------------------------------
 # Decode: one new query per sequence against a cache of its keys and values
 # ----------------------------------------------------------------------------

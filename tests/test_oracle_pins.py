@@ -790,3 +790,19 @@ def test_planted_backward_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(O, "key_positions", real)
     dq, dk, dv, _ = O.moba_backward(q, k, v, dout, B, topk, True, sel_idx=sel)
     np.testing.assert_allclose(dv, rv, rtol=0, atol=1e-10)
+
+
+def test_backward_dq_rows_equal_the_full_backward():
+    """The per-row dq (for sampled checks at large sizes) is the full
+    backward's dq, row by row, bit for bit up to summation order."""
+    rng = np.random.default_rng(31)
+    S, B, topk, D = 64, 16, 3, 8
+    q, k, v = rand_qkv(rng, 2, S, 4, 2, D)
+    dout = rng.standard_normal(q.shape)
+    _, sel = O.moba_forward(q, k, v, B, topk, True)
+    dq, _, _, lse = O.moba_backward(q, k, v, dout, B, topk, True, sel_idx=sel)
+    rows = [(bb, t, h) for bb in range(2) for t in (0, 15, 16, 40, 63) for h in range(4)]
+    got, gl = O.backward_dq_rows(q, k, v, dout, B, True, rows, [sel[bb, h, t] for (bb, t, h) in rows])
+    for x, (bb, t, h) in enumerate(rows):
+        np.testing.assert_allclose(got[x], dq[bb, t, h], rtol=0, atol=1e-12)
+        assert abs(gl[x] - lse[bb, h, t]) < 1e-12
