@@ -392,6 +392,75 @@ def curve(M, W, lengths, log, budget_s=4.0, moba_only=False):
     return out_lines
 
 
+def granularity(M, W, log, budget_s=2.0):
+    """Kernel speed across the block granularities of the report's ablation
+    (§4.2, Figure 4): 32K positions at 75 % sparsity, n blocks choosing n / 4
+    (8/2, 16/4, 32/8, 64/16, 128/32), on the 32K scaling-law layout (32 query
+    heads = KV heads, D = 128, bf16).  One JSON line per shape.  The report
+    compares model loss here; only speed is measured."""
+    import torch
+    S = 32768
+    lines = []
+    for n in (8, 16, 32, 64, 128):
+        w = W.Workload(f"mha32_32k_n{n}_k{n // 4}", "bf16", 1, 32, 32, S, 128, S // n, n // 4, seed=1200 + n)
+        q, k, v, _ = W.make_inputs(w, device="cuda")
+        out = torch.empty_like(q)
+        ws = torch.empty(M.workspace_bytes(1, S, 32, 32, 128, M.DTYPE_BF16, w.block_size, w.topk, True),
+                         dtype=torch.uint8, device="cuda")
+        call = lambda: M.moba_attn_fwd(q, k, v, w.block_size, w.topk, True, out=out, workspace=ws,
+                                       return_sel=False)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        call()
+        torch.cuda.synchronize()
+        steps = max(3, min(200, int(budget_s / max(time.perf_counter() - t0, 1e-6))))
+        M.profile_read()
+        M.profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        M.profile_enable(False)
+        st = M.profile_read()
+        fl = useful_flops(w)
+        res = {"seqlen": S, "blocks": n, "topk": n // 4, "block_size": w.block_size, "ms": ms, "steps": steps,
+               "useful_tflops": fl / (ms * 1e-3) / 1e12, "tokens_per_s": S / (ms * 1e-3),
+               "stages_ms": {k_: x["ms"] / steps for k_, x in st.items() if x["launches"]}}
+        log(f"[granularity] {n}/{n // 4}: {ms:.3f} ms")
+        print(json.dumps(res), flush=True)
+        lines.append(res)
+        del q, k, v, out, ws
+        torch.cuda.empty_cache()
+    return lines
+
+
+def gemm_peak(log):
+    """The attainable dense bf16 rate on this GPU: torch.matmul (hipBLASLt)
+    on square bf16 products, best of a few sizes."""
+    import torch
+    best = {}
+    for n in (4096, 8192, 16384):
+        a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+        b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        reps = max(3, int(2e14 / (2.0 * n ** 3)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        tf = 2.0 * n ** 3 * reps / (time.perf_counter() - t0) / 1e12
+        best[str(n)] = round(tf, 1)
+        log(f"[gemm] {n}^3 bf16: {tf:.1f} TFLOP/s")
+        del a, b
+    print(json.dumps({"gemm_bf16_tflops": best, "peak_datasheet": PEAK_BF16_TFLOPS}), flush=True)
+    return best
+
+
 def decode_bytes(w, sel, lens, chunk):
     """Algorithmic HBM bytes of one decode step, from the step's own selection:
     per (sequence, KV head) the union of the group's chosen blocks is read once
@@ -607,6 +676,10 @@ def main():
                     help="write the decode kernel-trace summary from a rocprofv3 --stats run, then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain copy of MIB MiB first (reference dispatch for HBM byte counters)")
+    ap.add_argument("--granularity", action="store_true",
+                    help="time the 32K forward at the report's five block granularities (75 %% sparsity), then exit")
+    ap.add_argument("--gemm-peak", action="store_true",
+                    help="measure the attainable dense bf16 GEMM rate (torch.matmul), then exit")
     ap.add_argument("--curve-moba-only", action="store_true",
                     help="with --curve: MoBA side only (for lengths where dense attention takes minutes)")
     ap.add_argument("--curve", nargs="*", type=int, metavar="SEQLEN",
@@ -644,6 +717,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.granularity:
+        granularity(M, W, log)
+        return
+    if args.gemm_peak:
+        gemm_peak(log)
+        return
     if args.backward:
         print(json.dumps(measure_backward(M, W, W.WORKLOADS[args.backward], args.steps, args.warmup, log)),
               flush=True)

@@ -268,3 +268,15 @@ def test_workload_gqa32x8_128k_sampled():
 def test_workload_gqa32x8_1m_sampled():
     w = W.WORKLOADS["gqa32x8_1m"]
     run(w, rows=W.sample_rows(w, 8, seed=24), device_inputs=True)
+
+
+@pytest.mark.parametrize("n", [8, 128])
+def test_forward_granularity_extremes_32k_sampled(n):
+    """The coarsest and the finest of the report's block granularities at 32K
+    and 75 % sparsity (8 blocks choosing 2; 128 blocks choosing 32), 32 MHA
+    heads, sampled rows per head."""
+    w = small(f"gran_n{n}", "bf16", 1, 32768, 32, 32, 128, 32768 // n, n // 4, seed=1200 + n)
+    rng = np.random.default_rng(n)
+    rows = [(0, int(t), h) for h in range(32) for t in rng.integers(0, 32768, 12)] + \
+           [(0, t, 0) for t in (0, 32768 // n - 1, 32768 // n, 32767)]
+    run(w, rows=rows, device_inputs=True)
