@@ -437,12 +437,12 @@ def granularity(M, W, log, budget_s=2.0):
     return lines
 
 
-def gemm_peak(log):
+def gemm_peak(log, sizes=(4096, 8192, 16384), emit=True):
     """The attainable dense bf16 rate on this GPU: torch.matmul (hipBLASLt)
-    on square bf16 products, best of a few sizes."""
+    on square bf16 products."""
     import torch
     best = {}
-    for n in (4096, 8192, 16384):
+    for n in sizes:
         a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
         b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
         for _ in range(3):
@@ -457,7 +457,8 @@ def gemm_peak(log):
         best[str(n)] = round(tf, 1)
         log(f"[gemm] {n}^3 bf16: {tf:.1f} TFLOP/s")
         del a, b
-    print(json.dumps({"gemm_bf16_tflops": best, "peak_datasheet": PEAK_BF16_TFLOPS}), flush=True)
+    if emit:
+        print(json.dumps({"gemm_bf16_tflops": best, "peak_datasheet": PEAK_BF16_TFLOPS}), flush=True)
     return best
 
 
@@ -663,6 +664,8 @@ def main():
     ap.add_argument("--secondary-steps", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the bf16 GEMM reference rate measured after the run")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--gate", choices=("mean", "minmax"), default="mean",
                     help="block gate: block means (the method's) or element-wise key min / max")
@@ -770,6 +773,13 @@ def main():
         line["secondary"] = res2
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W, w, inputs, args.cpu_seconds, log, gate=args.gate)
+    if not args.no_gemm_reference and line["roofline"]:
+        # context for the roofline: what a library GEMM attains on this GPU now
+        del inputs
+        torch.cuda.empty_cache()
+        g = gemm_peak(log, sizes=(8192,), emit=False)
+        line["gemm_reference"] = {"kernel": "torch.matmul bf16 8192^3 (hipBLASLt)", "tflops": g["8192"],
+                                  "past_kernel_frac_of_gemm": line["roofline"]["achieved"] / g["8192"]}
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

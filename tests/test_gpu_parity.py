@@ -280,3 +280,14 @@ def test_forward_granularity_extremes_32k_sampled(n):
     rows = [(0, int(t), h) for h in range(32) for t in rng.integers(0, 32768, 12)] + \
            [(0, t, 0) for t in (0, 32768 // n - 1, 32768 // n, 32767)]
     run(w, rows=rows, device_inputs=True)
+
+
+def test_forward_max_blocks_sampled():
+    """The largest block count the plan accepts (8192 blocks of 16 keys,
+    128K positions): the gate's per-block counters fill 32 KiB of LDS and the
+    top list ranks up to 8191 candidates."""
+    w = small("n8192", "bf16", 1, 131072, 2, 2, 128, 16, 4, seed=77)
+    rng = np.random.default_rng(3)
+    rows = [(0, int(t), h) for h in range(2) for t in rng.integers(0, 131072, 24)] + \
+           [(0, t, 1) for t in (0, 15, 16, 131071)]
+    run(w, rows=rows, device_inputs=True)
