@@ -709,7 +709,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         if int(os.environ.get("RANK", "0")) == 0:
-            print("bench.py measures one GPU only: this build has no multi-GPU path "
+            print("bench.py measures one GPU only: there is no multi-GPU path "
                   "(run with --gpus 1)", file=sys.stderr, flush=True)
         sys.exit(2)
 
