@@ -13,8 +13,9 @@
 //       normalised partial o (bf16) and its log2-domain log-sum-exp (fp32).
 //   attn_own_kernel: one work-group per 256 query rows of one own block (all
 //       query heads of a KV-head group together): causal attention over the
-//       own block up to each query, then the merge of that row's partials,
-//       then the bf16 output.
+//       own block up to each query, with the row's partials folded into the
+//       same online softmax as further groups of keys (their loads overlap
+//       the slice loop), then the bf16 output.
 //
 // Work split inside a work-group: every wave owns 32 query rows; 4 or 8
 // waves share each K/V slice staged in LDS, and two waves per SIMD let one
@@ -191,13 +192,27 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
 }
 
-// A partial o (one (row, past block) pair, 128 bf16) is stored in the order
-// the O^T accumulators hold it: lane half lg owns d = 32 b + 8 q4 + 4 lg + i
-// (b, q4, i = 0..3) at position 64 lg + 16 b + 4 q4 + i, so each lane writes
-// and reads 128 contiguous bytes.  The layout is private to the two
-// attention kernels.
-__device__ __forceinline__ void store_partial(bf16raw* dst, const f32x16* o, float inv, int lg) {
-  u32x4* p = reinterpret_cast<u32x4*>(dst + 64 * lg);
+// Partial results of one chunk, private to the two attention kernels.
+// Rows are numbered in the own-block kernel's order,
+//   orow = ((jl * hkv + hk) * block + pos) * g + gi
+// for position pos of the chunk's block jl and query head hk * g + gi, so
+// the 32 rows of an own-block wave are consecutive.  Slot s (the row's s-th
+// past block) is a plane of `rows` partials (the chunk's row capacity): the
+// partial o of (orow, s) is 256 contiguous bytes at (s * rows + orow) * 256,
+// so a wave's 32 rows of one slot are one contiguous 8 KiB.  Inside a partial
+// the d values are in the order the O^T accumulators hold them: lane half lg
+// owns the 128 bytes at 128 lg, whose 16-byte unit x = 2 b + h holds
+// d = 32 b + 8 q4 + 4 lg + i for q4 = 2h, 2h + 1 and i = 0..3.  A (row, slot)
+// pair is written whole by one lane pair of the past-block kernel, so its
+// cache lines are complete after one wave's stores.  The log-sum-exp of
+// (orow, s) sits at s * rows + orow.
+__device__ __forceinline__ int64_t partial_row(int64_t pic, int h, int64_t block, int hkv, int g) {
+  const int64_t jl = pic / block;
+  return ((jl * hkv + h / g) * block + (pic - jl * block)) * g + h % g;
+}
+__device__ __forceinline__ void store_partial(bf16raw* part_o, int64_t rows, int64_t orow, int64_t s, const f32x16* o,
+                                              float inv, int lg) {
+  u32x4* p = reinterpret_cast<u32x4*>(part_o) + (s * rows + orow) * 16 + 8 * lg;
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -207,11 +222,13 @@ __device__ __forceinline__ void store_partial(bf16raw* dst, const f32x16* o, flo
                            pack_bf16x2(o[b][e + 4] * inv, o[b][e + 5] * inv), pack_bf16x2(o[b][e + 6] * inv, o[b][e + 7] * inv)};
     }
 }
-__device__ __forceinline__ void add_partial(const bf16raw* src, float w, f32x16* o, int lg) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(src + 64 * lg);
-  u32x4 v[8];
+__device__ __forceinline__ void load_partial(const bf16raw* part_o, int64_t rows, int64_t orow, int64_t s, int lg,
+                                             u32x4* v) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(part_o) + (s * rows + orow) * 16 + 8 * lg;
 #pragma unroll
   for (int x = 0; x < 8; ++x) v[x] = p[x];
+}
+__device__ __forceinline__ void add_partial(const u32x4* v, float w, f32x16* o) {
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -221,6 +238,28 @@ __device__ __forceinline__ void add_partial(const bf16raw* src, float w, f32x16*
         o[b][8 * h + 2 * j] += w * bf16lo(v[2 * b + h][j]);
         o[b][8 * h + 2 * j + 1] += w * bf16hi(v[2 * b + h][j]);
       }
+}
+
+// Fold one partial (normalised o, log2-domain log-sum-exp) into a row's
+// running softmax state as one more group of keys: its weight relative to
+// the running max m is 2^(lse - m), and m is raised by the same lazy rule
+// as for a slice of scores.  The weight enters the row sum once (lane half
+// 0), since the two lanes of a row each hold half of the sum.
+__device__ __forceinline__ void fold_partial(WaveRows& R, const u32x4* v, float lse, int lg) {
+  const bool need = lse > R.m + kLazyRescale;
+  if (__any(need)) {
+    const float mn = need ? lse : R.m;
+    const float alpha = need ? fast_exp2(R.m - mn) : 1.0f;
+    R.m = mn;
+    R.l *= alpha;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) R.o[b][e] *= alpha;
+  }
+  const float w = fast_exp2(lse - R.m);
+  R.l += (lg == 0) ? w : 0.f;
+  add_partial(v, w, R.o);
 }
 
 // Byte offsets of this lane's V^T operand units.  Row d = 32 b + lr holds
@@ -239,8 +278,10 @@ struct VtOffsets {
 };
 __host__ __device__ constexpr int vt_c(int b, int kb, int hs) { return (4 * kb + 2 * hs) ^ (4 * (b & 1)); }
 
-// Slice-relative key index held in accumulator element e of 32-key block kb.
-__device__ __forceinline__ int key_of(int kb, int e, int lg) { return kb * 32 + 8 * (e >> 2) + lg * 4 + (e & 3); }
+// Slice-relative key index held in accumulator element e of 32-key block kb
+// is key_of(kb, e) + 4 * (lane / 32); the masks take the lane term into
+// their limit, so every test compares against a compile-time key.
+__device__ __forceinline__ constexpr int key_of(int kb, int e) { return kb * 32 + 8 * (e >> 2) + (e & 3); }
 
 // S^T for one 64-key slice: two 32-key blocks of 32 keys x 32 queries.
 __device__ __forceinline__ void qk_slice(const bf16raw* buf, const bf16x8* qb, f32x16* s, int lane) {
@@ -262,7 +303,8 @@ __device__ __forceinline__ void qk_slice(const bf16raw* buf, const bf16x8* qb, f
 
 // Online-softmax update with the scores of one slice; returns P^T as packed
 // bf16 pairs (pk[kb][x] holds accumulator elements 2x and 2x+1 of block kb).
-// masked(kr): key kr of the slice is invisible to this lane's query.
+// masked(kc): key kc + 4 * (lane / 32) of the slice is invisible to this
+// lane's query.
 template <bool kMasked, typename Mask>
 __device__ __forceinline__ void softmax_p(f32x16* s, WaveRows& R, float c, int lane, Mask masked, uint32_t (*pk)[8]) {
   const int lg = lane >> 5;
@@ -271,7 +313,7 @@ __device__ __forceinline__ void softmax_p(f32x16* s, WaveRows& R, float c, int l
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      if (kMasked && masked(key_of(kb, e, lg))) s[kb][e] = -__builtin_inff();
+      if (kMasked && masked(key_of(kb, e))) s[kb][e] = -__builtin_inff();
       mx = __builtin_fmaxf(mx, s[kb][e]);
     }
   mx = pair_max(mx);
@@ -349,16 +391,30 @@ __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, co
   softmax_pv<kMasked>(buf, s, R, vo, c, lane, masked);
 }
 
+// Scores of the keys a mask hides become -inf (weight 0 after the softmax).
+template <typename Mask>
+__device__ __forceinline__ void mask_scores(f32x16* s, Mask masked) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (masked(key_of(kb, e))) s[kb][e] = -__builtin_inff();
+}
+
 struct NoMask {
   __device__ __forceinline__ bool operator()(int) const { return false; }
 };
-struct TailMask {  // keys at or beyond `lim` (slice-relative) do not exist
-  int lim;
-  __device__ __forceinline__ bool operator()(int kr) const { return kr >= lim; }
+// Keys at or beyond `avail` (slice-relative) do not exist.
+struct TailMask {
+  int lim;  // avail - 4 * (lane / 32)
+  __device__ __forceinline__ TailMask(int avail, int lane) : lim(avail - 4 * (lane >> 5)) {}
+  __device__ __forceinline__ bool operator()(int kc) const { return kc >= lim; }
 };
-struct CausalMask {  // key kr (slice-relative) is visible iff kr <= qpos
-  int qpos;
-  __device__ __forceinline__ bool operator()(int kr) const { return kr > qpos; }
+// Key kr (slice-relative) is visible iff kr <= qpos.
+struct CausalMask {
+  int lim;  // qpos - 4 * (lane / 32)
+  __device__ __forceinline__ CausalMask(int qpos, int lane) : lim(qpos - 4 * (lane >> 5)) {}
+  __device__ __forceinline__ bool operator()(int kc) const { return kc > lim; }
 };
 
 template <int NW, bool kPipe>
@@ -452,7 +508,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __syncthreads();
     }
     if (nfull < nsl)
-      attend_slice<true>(smem + (nfull & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, TailMask{a.block - nfull * KT});
+      attend_slice<true>(smem + (nfull & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, TailMask(a.block - nfull * KT, lane));
   }
 
   const int lg = lane >> 5;
@@ -460,8 +516,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   if (valid) {
     // the normalised partial is a convex combination of value rows, so bf16
     // keeps it to 2^-9 of the largest |v|
-    store_partial(a.part_o + (int64_t)entry * HD, R.o, 1.f / ltot, lg);
-    if (lg == 0) a.part_lse[entry] = R.m + fast_log2(ltot);
+    const int64_t local_row = entry / a.kp, slot = entry - local_row * a.kp;
+    const int64_t orow = partial_row(local_row / a.hq, (int)(local_row % a.hq), a.block, a.hkv, a.g);
+    store_partial(a.part_o, a.part_rows, orow, slot, R.o, 1.f / ltot, lg);
+    if (lg == 0) a.part_lse[slot * a.part_rows + orow] = R.m + fast_log2(ltot);
   }
 }
 
@@ -671,23 +729,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const float ltot = pair_sum(R.l);
   if (valid) {
-    store_partial(a.part_o + (int64_t)entry * HD, R.o, 1.f / ltot, lg);
-    if (lg == 0) a.part_lse[entry] = R.m + fast_log2(ltot);
+    const int64_t local_row = entry / a.kp, slot = entry - local_row * a.kp;
+    const int64_t orow = partial_row(local_row / a.hq, (int)(local_row % a.hq), a.block, a.hkv, a.g);
+    store_partial(a.part_o, a.part_rows, orow, slot, R.o, 1.f / ltot, lg);
+    if (lg == 0) a.part_lse[slot * a.part_rows + orow] = R.m + fast_log2(ltot);
   }
 }
 
 constexpr int OWN_NW = 8;  // own-block tiles: 8 waves x 32 rows
-
-// One 64-key slice from a K / V^T image slice in LDS.
-template <bool kMasked, typename Mask>
-__device__ __forceinline__ void attend_slice_img(const char* buf, WaveRows& R, float c, int lane, int kofs, int vofs,
-                                                 Mask masked) {
-  f32x16 sc[2];
-  uint32_t pk[2][8];
-  qk_img(buf + kofs, R.qb, sc);
-  softmax_p<kMasked>(sc, R, c, lane, masked, pk);
-  pv_img(buf + IMG_BYTES + vofs, pk, R);
-}
 
 // Own block of each query (causal up to the query itself) plus the merge
 // of the row's partials.  kImg: K and V come from the slice images (block a
@@ -718,6 +767,14 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
   }
   rows_init(R);
 
+  // this row's partials from the past-block kernel (slot s: past block s of
+  // its selection), folded into the softmax state like further keys
+  const int64_t nslot = a.causal ? (j < a.kp ? j : a.kp) : a.kp;
+  const int64_t orow = partial_row(j * a.block + pos - a.t0, h, a.block, a.hkv, G);
+  const bf16raw* po = reinterpret_cast<const bf16raw*>(a.part_o);
+  const int64_t rows = a.part_rows;
+  int64_t nfolded = 0;
+
   if (a.causal) {
     const int64_t last = (p0 + a.own_t < a.block ? p0 + a.own_t : a.block);  // keys [0, last) of the block
     const int nsl = (int)((last + KT - 1) / KT);
@@ -735,24 +792,56 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
       const uint16_t* vimg = a.vimg + img0;
       const int kofs = lg * 1024 + (lane & 31) * 16;
       const int vofs = lg * 2048 + (lane & 31) * 16;
-      ImgStager<OWN_NW> st;
-      auto bufp = [&](int sl) { return smem + (sl & 1) * SLICE_BYTES; };
-      st.load(kimg, vimg);
-      st.store(bufp(0));
-      __syncthreads();
-      for (int sl = 0; sl < nfree; ++sl) {
-        if (sl + 1 < nsl) st.load(kimg + (int64_t)(sl + 1) * (KT * HD), vimg + (int64_t)(sl + 1) * (KT * HD));
-        attend_slice_img<false>(bufp(sl), R, c, lane, kofs, vofs, NoMask{});
-        if (sl + 1 < nsl) st.store(bufp(sl + 1));
-        __syncthreads();
-      }
-      for (int sl = nfree; sl < nsl; ++sl) {
+      // the loads of slice s+2 go out at the start of slice s (two register
+      // sets, LDS double-buffered), as in the past-block kernel; past the
+      // last slice they repeat it
+      ImgStager<OWN_NW> st, st2;
+      auto src = [&](int sl) { return (int64_t)(sl < nsl ? sl : nsl - 1) * (KT * HD); };
+      // one instance of the slice code: the causal mask is a separate step
+      // on the scores of the slices that reach the tile's first query.  The
+      // partial of slot sl is loaded before the slice's K/V prefetch and
+      // folded after its P V, so its loads overlap the slice's MFMAs.
+      auto slice = [&](int sl, const char* buf, bool fold, const u32x4* pv, float pl) {
         const int64_t k0 = (int64_t)sl * KT;
-        if (sl + 1 < nsl) st.load(kimg + (int64_t)(sl + 1) * (KT * HD), vimg + (int64_t)(sl + 1) * (KT * HD));
-        if (k0 <= wmax) attend_slice_img<true>(bufp(sl), R, c, lane, kofs, vofs, CausalMask{(int)(pos - k0)});
-        if (sl + 1 < nsl) st.store(bufp(sl + 1));
+        if (k0 <= wmax) {
+          f32x16 sc[2];
+          uint32_t pk[2][8];
+          qk_img(buf + kofs, R.qb, sc);
+          if (sl >= nfree) mask_scores(sc, CausalMask((int)(pos - k0), lane));
+          softmax_p<false>(sc, R, c, lane, NoMask{}, pk);
+          pv_img(buf + IMG_BYTES + vofs, pk, R);
+        }
+        if (fold) fold_partial(R, pv, pl, lg);
+      };
+      const int64_t nloop = nslot < nsl ? nslot : nsl;  // slots folded inside the slice loop
+      auto slice_with_partial = [&](int sl, const char* buf, auto&& prefetch) {
+        u32x4 pv[8];
+        float pl = 0.f;
+        const bool fold = sl < nloop;
+        if (fold) {
+          load_partial(po, rows, orow, sl, lg, pv);
+          pl = a.part_lse[sl * rows + orow];
+        }
+        prefetch();
+        slice(sl, buf, fold, pv, pl);
+      };
+      st.load(kimg, vimg);
+      st.store(smem);
+      // the query rows and slice 0 must be in before the prefetch loads go out
+      drain_vmem();
+      st2.load(kimg + src(1), vimg + src(1));
+      __syncthreads();
+      for (int sl = 0; sl < nsl; sl += 2) {
+        slice_with_partial(sl, smem, [&] { st.load(kimg + src(sl + 2), vimg + src(sl + 2)); });
+        if (sl + 1 < nsl) st2.store(smem + SLICE_BYTES);
+        __syncthreads();
+        if (sl + 1 >= nsl) break;
+        slice_with_partial(sl + 1, smem + SLICE_BYTES, [&] { st2.load(kimg + src(sl + 3), vimg + src(sl + 3)); });
+        if (sl + 2 < nsl) st.store(smem);
         __syncthreads();
       }
+      drain_vmem();
+      nfolded = nloop;
     } else {
       bf16raw* sb = reinterpret_cast<bf16raw*>(smem);
       VtOffsets vo;
@@ -781,39 +870,27 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
       for (int sl = nfree; sl < nsl; ++sl) {
         const int64_t k0 = (int64_t)sl * KT;
         if (sl + 1 < nsl) fetch(sl + 1);
-        if (k0 <= wmax) attend_slice<true>(sb + (sl & 1) * BUF_ELEMS, R, vo, c, lane, CausalMask{(int)(pos - k0)});
+        if (k0 <= wmax) attend_slice<true>(sb + (sl & 1) * BUF_ELEMS, R, vo, c, lane, CausalMask((int)(pos - k0), lane));
         if (sl + 1 < nsl) st.store(sb + ((sl + 1) & 1) * BUF_ELEMS);
         __syncthreads();
       }
     }
   }
 
-  // merge this row's partials (log-sum-exp rule), normalise, store bf16
-  const int64_t nslot = a.causal ? (j < a.kp ? j : a.kp) : a.kp;
-  const float l_own = pair_sum(R.l);
-  const int64_t local_row = (j * a.block + pos - a.t0) * a.hq + h;
-  const float* lse = a.part_lse + local_row * a.kp;
-  const bf16raw* po = reinterpret_cast<const bf16raw*>(a.part_o) + local_row * a.kp * HD;
-  // an own block with no visible key (non-causal mode) carries no weight
-  const float m_own = (l_own > 0.f) ? R.m : -__builtin_inff();
-  float M = m_own;
-  for (int64_t s = 0; s < nslot; ++s) M = __builtin_fmaxf(M, lse[s]);
-  const float c_own = (l_own > 0.f) ? fast_exp2(m_own - M) : 0.f;
-  float Lsum = l_own * c_own;
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) R.o[b][e] *= c_own;
-  for (int64_t s = 0; s < nslot; ++s) {
-    const float w = fast_exp2(lse[s] - M);
-    Lsum += w;
-    add_partial(po + s * HD, w, R.o, lg);
+  // the partials not folded in the slice loop (all of them in non-causal
+  // mode, where the own block has no visible key and starts with weight 0),
+  // then normalise and store bf16
+  for (int64_t s = nfolded; s < nslot; ++s) {
+    u32x4 pv[8];
+    load_partial(po, rows, orow, s, lg, pv);
+    fold_partial(R, pv, a.part_lse[s * rows + orow], lg);
   }
+  const float Lsum = pair_sum(R.l);
   if (valid) {
     const float inv = 1.f / Lsum;
     const int64_t t = j * a.block + pos;
     // the row's log-sum-exp of the scaled logits, natural log (for the backward)
-    if (a.lse && lg == 0) a.lse[((int64_t)a.bb * a.hq + h) * a.seqlen + t] = (M + fast_log2(Lsum)) * 0.6931471805599453f;
+    if (a.lse && lg == 0) a.lse[((int64_t)a.bb * a.hq + h) * a.seqlen + t] = (R.m + fast_log2(Lsum)) * 0.6931471805599453f;
     bf16raw* dst = reinterpret_cast<bf16raw*>(a.out) + ((a.bb * a.seqlen + t) * a.hq + h) * HD;
 #pragma unroll
     for (int b = 0; b < 4; ++b)

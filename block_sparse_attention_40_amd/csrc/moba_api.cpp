@@ -280,6 +280,8 @@ int fwd_impl(const void* q, const void* k, const void* v, int64_t batch, int64_t
   int32_t* entries = reinterpret_cast<int32_t*>(ws + p.off_entries);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + p.off_part_o);
   float* part_lse = reinterpret_cast<float*>(ws + p.off_part_lse);
+  // one slot plane of the partials holds every row of a chunk
+  const int64_t part_rows = p.kp > 0 ? p.max_pairs / p.kp : 0;
   const bool bf16 = dtype == MOBA_DTYPE_BF16;
   const float sl2 = scale_log2_for(head_dim);
 
@@ -377,7 +379,8 @@ int fwd_impl(const void* q, const void* k, const void* v, int64_t batch, int64_t
 
         PastArgs pa{};
         pa.q = q; pa.k = k; pa.v = v; pa.tiles = tiles; pa.count = count; pa.listoff = listoff;
-        pa.entries = entries; pa.part_o = part_o; pa.part_lse = part_lse; pa.seqlen = seqlen; pa.n = p.n;
+        pa.entries = entries; pa.part_o = part_o; pa.part_lse = part_lse; pa.part_rows = part_rows;
+        pa.seqlen = seqlen; pa.n = p.n;
         pa.t0 = t0; pa.hq = num_q_heads; pa.hkv = num_kv_heads; pa.block = block_size; pa.kp = p.kp;
         pa.g = p.g; pa.bb = (int32_t)bb; pa.max_tiles = (int32_t)p.max_tiles; pa.tile_rows = p.tile_rows;
         pa.scale_log2 = sl2; pa.kimg = kimg; pa.vimg = vimg;
@@ -389,6 +392,7 @@ int fwd_impl(const void* q, const void* k, const void* v, int64_t batch, int64_t
 
       OwnArgs oa{};
       oa.q = q; oa.k = k; oa.v = v; oa.out = out; oa.part_o = part_o; oa.part_lse = part_lse;
+      oa.part_rows = part_rows;
       oa.seqlen = seqlen; oa.n = p.n; oa.t0 = t0; oa.cnt = cnt; oa.hq = num_q_heads; oa.hkv = num_kv_heads;
       oa.block = block_size; oa.kp = p.kp; oa.g = p.g; oa.own_t = p.own_t; oa.bb = (int32_t)bb;
       oa.causal = causal ? 1 : 0; oa.scale_log2 = sl2; oa.kimg = kimg; oa.vimg = vimg; oa.lse = lse;

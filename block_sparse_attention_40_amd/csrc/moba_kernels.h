@@ -45,8 +45,9 @@ struct PastArgs {
   const int32_t* count;
   const int32_t* listoff;
   const int32_t* entries;
-  uint16_t* part_o;      // [pairs, D] normalised partial output, bf16
-  float* part_lse;       // [pairs] log2-domain log-sum-exp of the scaled logits
+  uint16_t* part_o;      // normalised partial outputs, bf16 (layout in attn_bf16.hip)
+  float* part_lse;       // their log2-domain log-sum-exp of the scaled logits
+  int64_t part_rows;     // row capacity of one slot plane (chunk positions x hq)
   const uint16_t* kimg;  // K slice images [batch, hkv, seqlen / 64, 64 x 128], or null
   const uint16_t* vimg;  // V^T slice images, same shape
   int64_t seqlen, n, t0;
@@ -60,8 +61,9 @@ struct OwnArgs {
   const void* k;
   const void* v;
   void* out;
-  const uint16_t* part_o;  // [pairs, D] bf16
+  const uint16_t* part_o;  // partial outputs written by the past-block kernel
   const float* part_lse;
+  int64_t part_rows;
   const uint16_t* kimg;    // K / V^T slice images, or null
   const uint16_t* vimg;
   float* lse;              // [batch, hq, seqlen] row log-sum-exp (natural log), or null
