@@ -417,7 +417,7 @@ struct CausalMask {
   __device__ __forceinline__ bool operator()(int kc) const { return kc > lim; }
 };
 
-template <int NW, bool kPipe>
+template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_past_kernel(PastArgs a) {
   __shared__ __attribute__((aligned(16))) bf16raw smem[2 * BUF_ELEMS];
   constexpr int ROWS = NW * 32;
@@ -454,62 +454,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int rs = a.hkv * HD;
   const bf16raw* kblk = reinterpret_cast<const bf16raw*>(a.k) + ((a.bb * a.seqlen) + blk * a.block) * (int64_t)rs + hk * HD;
   const bf16raw* vblk = reinterpret_cast<const bf16raw*>(a.v) + ((a.bb * a.seqlen) + blk * a.block) * (int64_t)rs + hk * HD;
+  // any block size: double-buffered slices (the loads of slice s+1 in
+  // flight while slice s is computed), a ragged last slice masked
   const int nsl = (a.block + KT - 1) / KT;
+  const int nfull = a.block / KT;
   KVStager<NW> st;
-  if constexpr (kPipe) {
-    // Every slice is full.  Two register sets carry slices from HBM: the
-    // loads of slice s+2 are issued at the start of iteration s and written
-    // to LDS only at the end of iteration s+1, so each load has two slice
-    // iterations to arrive.  LDS stays double-buffered.  The loads are issued
-    // unconditionally (past the end they re-read the last slice) so the
-    // number of loads in flight is the same in every iteration and the wait
-    // before each LDS store leaves the younger loads outstanding.
-    KVStager<NW> st2;
-    auto sptr = [&](int sl) { return (int64_t)(sl < nsl ? sl : nsl - 1) * KT * rs; };
-    st.template load<false>(kblk, vblk, rs, KT);
-    st.store(smem);
-    // Everything loaded so far (the query rows, slice 0) must be complete
-    // before the prefetch loads go out: the loop's MFMAs read the query
-    // registers, and a wait for them inside the loop would also wait for the
-    // younger prefetch loads (the load counter is in-order).
-    drain_vmem();
-    st2.template load<false>(kblk + sptr(1), vblk + sptr(1), rs, KT);
+  auto fetch = [&](int sl) {
+    const int64_t off = (int64_t)sl * KT * rs;
+    if (sl < nfull)
+      st.template load<false>(kblk + off, vblk + off, rs, KT);
+    else
+      st.template load<true>(kblk + off, vblk + off, rs, a.block - sl * KT);
+  };
+  fetch(0);
+  st.store(smem);
+  __syncthreads();
+  for (int sl = 0; sl < nfull; ++sl) {
+    if (sl + 1 < nsl) fetch(sl + 1);
+    attend_slice<false>(smem + (sl & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, NoMask{});
+    if (sl + 1 < nsl) st.store(smem + ((sl + 1) & 1) * BUF_ELEMS);
     __syncthreads();
-    for (int sl = 0; sl < nsl; sl += 2) {
-      // slice sl in buffer 0; slice sl+1 in flight in st2
-      st.template load<false>(kblk + sptr(sl + 2), vblk + sptr(sl + 2), rs, KT);
-      attend_slice<false>(smem, R, vo, a.scale_log2, lane, NoMask{});
-      if (sl + 1 < nsl) st2.store(smem + BUF_ELEMS);
-      __syncthreads();
-      if (sl + 1 >= nsl) break;
-      // slice sl+1 in buffer 1; slice sl+2 in flight in st
-      st2.template load<false>(kblk + sptr(sl + 3), vblk + sptr(sl + 3), rs, KT);
-      attend_slice<false>(smem + BUF_ELEMS, R, vo, a.scale_log2, lane, NoMask{});
-      if (sl + 2 < nsl) st.store(smem);
-      __syncthreads();
-    }
-  } else {
-    // any block size: double-buffered slices, a ragged last slice masked
-    const int nfull = a.block / KT;
-    auto fetch = [&](int sl) {
-      const int64_t off = (int64_t)sl * KT * rs;
-      if (sl < nfull)
-        st.template load<false>(kblk + off, vblk + off, rs, KT);
-      else
-        st.template load<true>(kblk + off, vblk + off, rs, a.block - sl * KT);
-    };
-    fetch(0);
-    st.store(smem);
-    __syncthreads();
-    for (int sl = 0; sl < nfull; ++sl) {
-      if (sl + 1 < nsl) fetch(sl + 1);
-      attend_slice<false>(smem + (sl & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, NoMask{});
-      if (sl + 1 < nsl) st.store(smem + ((sl + 1) & 1) * BUF_ELEMS);
-      __syncthreads();
-    }
-    if (nfull < nsl)
-      attend_slice<true>(smem + (nfull & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, TailMask(a.block - nfull * KT, lane));
   }
+  if (nfull < nsl)
+    attend_slice<true>(smem + (nfull & 1) * BUF_ELEMS, R, vo, a.scale_log2, lane, TailMask(a.block - nfull * KT, lane));
 
   const int lg = lane >> 5;
   const float ltot = pair_sum(R.l);
@@ -906,16 +873,15 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
 int launch_attn_past(const PastArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.max_tiles);
   if (a.tile_rows == 256) {
-    // 8 waves, one work-group per CU: loads two slices ahead when every slice is full
+    // 8 waves, one work-group per CU; from the slice images the loads run two
+    // slices ahead, otherwise one (any block size)
     if (a.block % KT == 0 && a.kimg)
       hipLaunchKernelGGL((attn_past_img_kernel<8>), grid, dim3(512), 0, st, a);
-    else if (a.block % KT == 0)
-      hipLaunchKernelGGL((attn_past_kernel<8, true>), grid, dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL((attn_past_kernel<8, false>), grid, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((attn_past_kernel<8>), grid, dim3(512), 0, st, a);
   } else {
     // 4 waves, two independent work-groups per CU
-    hipLaunchKernelGGL((attn_past_kernel<4, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_past_kernel<4>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

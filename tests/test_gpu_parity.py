@@ -125,6 +125,9 @@ SMALL = [
     small("b16_tiny_blocks", "bf16", 1, 512, 2, 2, 128, 16, 4),
     small("b2048_long", "bf16", 1, 8192, 4, 1, 128, 2048, 2),
     small("single_block", "bf16", 1, 256, 2, 2, 128, 256, 3),
+    # lists of 2304 rows on average: 256-row tiles over blocks that are not a
+    # whole number of 64-key slices (direct K/V staging, masked last slice)
+    small("ragged_b96_long_lists", "bf16", 1, 3840, 8, 1, 128, 96, 4),
     # bf16 gate on MFMA: several 32-block score tiles with a ragged last one,
     # and each top-k list capacity (kept past blocks 8, 11, 15, 19)
     small("gate_n50_k9", "bf16", 1, 2400, 4, 2, 128, 48, 9),
