@@ -8,7 +8,8 @@ inputs resident in HBM.  Prints one JSON line.
 Headline workload: 1M tokens, Llama-3.1-8B-shaped grouped-query attention
 (32 query / 8 KV heads, head dim 128), block 4096, top-12, bf16.  The 32K
 workload (32 heads, block 512, top-3, planted needles) is measured in the same
-run and reported under "secondary".
+run and reported under "secondary", launched eagerly and, under "graph", as
+replays of the same call captured once into a HIP graph.
 """
 from __future__ import annotations
 
@@ -47,7 +48,38 @@ def useful_flops(w) -> float:
     return 4.0 * D * keys * w.batch * w.num_q_heads
 
 
-def measure(M, W, w, steps, warmup, log, gate="mean"):
+def graph_replay(M, w, q, k, v, out, sel, ws, steps, gate, log):
+    """The same forward captured once into a HIP graph (torch.cuda.CUDAGraph)
+    and replayed `steps` times: the step time without the host's per-kernel
+    launch cost.  The first replay's output must equal the eager output bit
+    for bit (the kernels are deterministic)."""
+    import torch
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal, out=out, sel_idx=sel, workspace=ws, gate=gate)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal, out=out, sel_idx=sel, workspace=ws, gate=gate)
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref):
+        raise RuntimeError("graph replay output differs from the eager forward")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    log(f"[bench] {w.name}: {steps} graph replays, {ms:.3f} ms each")
+    del g
+    return ms
+
+
+def measure(M, W, w, steps, warmup, log, gate="mean", graph=False):
     import torch
     dev = "cuda"
     t0 = time.perf_counter()
@@ -98,6 +130,10 @@ def measure(M, W, w, steps, warmup, log, gate="mean"):
     # the library's own work accounting must agree with the closed form
     if abs(attn_fl - fl) > 1e-6 * fl:
         raise RuntimeError(f"useful FLOP accounting mismatch: library {attn_fl:.6e} vs closed form {fl:.6e}")
+    if graph:
+        gms = graph_replay(M, w, q, k, v, out, sel, ws, steps, gate, log)
+        res["graph"] = {"ms_per_step": gms, "useful_tflops": fl / (gms * 1e-3) / 1e12,
+                        "tokens_per_s": w.batch * w.seqlen / (gms * 1e-3)}
     inputs = (q, k, v, out, sel)
     return res, inputs, stages
 
@@ -768,9 +804,11 @@ def main():
     }
     if args.secondary:
         w2 = W.WORKLOADS[args.secondary]
-        res2, inputs2, _ = measure(M, W, w2, args.secondary_steps, max(args.warmup, 3), log, gate=args.gate)
+        res2, inputs2, _ = measure(M, W, w2, args.secondary_steps, max(args.warmup, 3), log, gate=args.gate,
+                                   graph=True)
         del inputs2
         line["secondary"] = res2
+    line["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W, w, inputs, args.cpu_seconds, log, gate=args.gate)
     if not args.no_gemm_reference and line["roofline"]:
@@ -780,8 +818,6 @@ def main():
         g = gemm_peak(log, sizes=(8192,), emit=False)
         line["gemm_reference"] = {"kernel": "torch.matmul bf16 8192^3 (hipBLASLt)", "tflops": g["8192"],
                                   "past_kernel_frac_of_gemm": line["roofline"]["achieved"] / g["8192"]}
-    else:
-        line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
 
 

@@ -140,6 +140,56 @@ SMALL = [
 ]
 
 
+GRAPH_CASES = [
+    small("graph_small_tiles", "bf16", 1, 2048, 4, 2, 128, 256, 3, seed=31),
+    # 256-row tiles: the K/V slice images are built inside the captured call
+    small("graph_images", "bf16", 1, 8192, 4, 1, 128, 2048, 2, seed=32),
+]
+
+
+@pytest.mark.parametrize("w", GRAPH_CASES, ids=[w.name for w in GRAPH_CASES])
+def test_forward_graph_replay_matches_eager(w):
+    """One forward captured into a HIP graph (torch.cuda.CUDAGraph) and
+    replayed three times, with eager forwards on other inputs and host
+    synchronisations between the replays: every replay's output and selection
+    equal the eager ones bit for bit (the library only launches kernels: no
+    allocation, copy, memset or synchronisation inside a call)."""
+    say(f"[case] graph replay {w}")
+    q, k, v, _ = W.make_inputs(w, device=DEV)
+    dt = M.DTYPE_BF16
+    ws = torch.empty(M.workspace_bytes(w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, dt,
+                                       w.block_size, w.topk, w.causal), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(q)
+    sel = torch.empty((w.batch, w.num_q_heads, w.seqlen, w.topk), dtype=torch.int32, device=DEV)
+    M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal, out=out, sel_idx=sel, workspace=ws)
+    torch.cuda.synchronize()
+    out_ref, sel_ref = out.clone(), sel.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal, out=out, sel_idx=sel, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal, out=out, sel_idx=sel, workspace=ws)
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    for i in range(3):
+        # eager work between the replays, on other inputs and buffers
+        q2 = torch.randn(q.shape, generator=gen).to(q.dtype).to(DEV)
+        o2, _ = M.moba_attn_fwd(q2, k, v, w.block_size, w.topk, w.causal)
+        torch.cuda.synchronize()
+        out.zero_()
+        sel.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_ref), f"replay {i}: output differs from the eager forward"
+        assert torch.equal(sel, sel_ref), f"replay {i}: selection differs from the eager forward"
+        del o2
+    del g
+
+
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_forward_small(w):
     run(w)
