@@ -74,6 +74,7 @@ CASES = [
     small("dense_topk_ge_n", 1, 512, 2, 1, 64, 9),
     small("noncausal", 1, 512, 2, 2, 128, 3, causal=False),
     small("g8", 1, 1024, 8, 1, 128, 4),
+    small("g3", 1, 1024, 6, 2, 128, 4),
 ]
 
 

@@ -72,6 +72,8 @@ CASES = [
     wl("b16_small_blocks", "bf16", 4, 2, 1024, 128, 16, 5, [1024, 17, 999]),
     wl("f32_d64", "f32", 4, 2, 1024, 64, 64, 4, [1024, 300, 65]),
     wl("f32_d128", "f32", 4, 1, 2048, 128, 128, 3, [2048, 1500]),
+    # a group of 3 query heads per KV head
+    wl("g3_b128", "bf16", 6, 2, 2048, 128, 128, 4, [2048, 1111, 300]),
 ]
 
 

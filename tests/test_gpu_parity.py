@@ -125,6 +125,10 @@ SMALL = [
     small("b16_tiny_blocks", "bf16", 1, 512, 2, 2, 128, 16, 4),
     small("b2048_long", "bf16", 1, 8192, 4, 1, 128, 2048, 2),
     small("single_block", "bf16", 1, 256, 2, 2, 128, 256, 3),
+    # groups that do not divide the 256-row tiles (g = 3: 85 positions x 3
+    # heads) and a group of 32 (8 positions x 32 heads per tile)
+    small("gqa_g3", "bf16", 1, 2048, 6, 2, 128, 128, 4),
+    small("gqa_g32", "bf16", 1, 1024, 32, 1, 128, 128, 3),
     # lists of 2304 rows on average: 256-row tiles over blocks that are not a
     # whole number of 64-key slices (direct K/V staging, masked last slice)
     small("ragged_b96_long_lists", "bf16", 1, 3840, 8, 1, 128, 96, 4),
