@@ -305,6 +305,138 @@ def summarize_traffic(fetch_dir, write_dir, calib_mib, out_path):
     return res
 
 
+MFMA_CMD = ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+            "-d gpurun_out/pmc_mfma -o run -- python3 -u bench.py --steps 1 --warmup 0 --secondary '' "
+            "--no-cpu-baseline --no-gemm-reference > gpurun_out/pmc_mfma.json")
+HBM_STAGES_FILE = os.path.join(ROOT, "profiles", "hbm_stages_gqa32x8_1m.md")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_busy_gqa32x8_1m.md")
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _agent_info(d):
+    import csv
+    import glob
+    for f in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Name", "").startswith("gfx"):
+                    return r
+    raise RuntimeError(f"no GPU agent in {d}")
+
+
+def _short(name):
+    n = name.replace("void ", "")
+    return n.split("(")[0]
+
+
+def summarize_mfma(pmc_dir, out_path):
+    """MFMA-busy fraction per kernel from SQ_VALU_MFMA_BUSY_CYCLES (summed over
+    every SIMD) against GRBM_GUI_ACTIVE (summed over the XCDs): busy =
+    MFMA cycles / (GPU cycles per XCD x SIMDs); the clock the kernels ran at =
+    GPU cycles per XCD / kernel time."""
+    info = _agent_info(pmc_dir)
+    simds, xcc = int(info["Simd_Count"]), int(info["Num_Xcc"])
+    per = {}
+    for r in _counter_rows(pmc_dir):
+        k = _short(r["Kernel_Name"])
+        if not k.startswith("moba::"):
+            continue
+        d = per.setdefault(k, {"disp": set(), "t": {}})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["disp"].add(r["Dispatch_Id"])
+        d["t"][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    out = ["# MFMA busy: MoBA forward, gqa32x8_1m workload (1M tokens, 32/8 heads, D 128, block 4096, top-12)",
+           "", "Command (run from the repository root on one MI355X):", "", "```", MFMA_CMD, "```", "",
+           f"Counters summed over the dispatches of one forward call; {simds} SIMDs, {xcc} XCDs. "
+           "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs); clock = "
+           "(GRBM_GUI_ACTIVE / XCDs) / kernel time.", "",
+           "| Kernel | Dispatches | Kernel ms (sum) | MFMA busy | Clock GHz |", "|---|---|---|---|---|"]
+    res = {}
+    for k, d in sorted(per.items(), key=lambda x: -sum(x[1]["t"].values())):
+        if d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) <= 0:
+            continue
+        cyc = d["GRBM_GUI_ACTIVE"] / xcc
+        t = sum(d["t"].values())
+        busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * simds)
+        res[k] = {"busy": busy, "clock_ghz": cyc / t / 1e9, "ms": t * 1e3}
+        out.append(f"| {k} | {len(d['disp'])} | {t * 1e3:.2f} | {100 * busy:.1f} % | {cyc / t / 1e9:.2f} |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    return res
+
+
+def summarize_stage_hbm(fetch_dir, write_dir, calib_mib, bench_json, out_path):
+    """HBM bytes per dispatch of every MoBA kernel from FETCH_SIZE and
+    WRITE_SIZE (scaled by the calibration copy, as for the past-block kernel),
+    over the dispatch time in the same counter run, beside the bytes the stage
+    must move (bench.py's own accounting, HIP-event time)."""
+    calib_kib = calib_mib * 1024.0
+    byk = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == counter]
+        cal = [float(r["Counter_Value"]) for r in rows if COPY_KERNEL_TAG in r["Kernel_Name"]]
+        if not cal:
+            raise RuntimeError(f"{counter}: calibration dispatch missing in {d}")
+        factor = calib_kib / (sum(cal) / len(cal))
+        for r in rows:
+            k = _short(r["Kernel_Name"])
+            if not k.startswith("moba::"):
+                continue
+            e = byk.setdefault(k, {"FETCH_SIZE": [], "WRITE_SIZE": [], "t": []})
+            e[counter].append(float(r["Counter_Value"]) * factor * 1024)
+            if counter == "FETCH_SIZE":
+                e["t"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    st = line["stages"]
+    out = ["# HBM traffic per kernel: MoBA forward, gqa32x8_1m workload (1M tokens, 32/8 heads, D 128, block 4096, top-12)",
+           "", "Commands (run from the repository root on one MI355X):", "", "```",
+           PMC_CMD.format(counter="FETCH_SIZE"), PMC_CMD.format(counter="WRITE_SIZE"), "```", "",
+           f"FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what each reads for a {calib_mib} MiB "
+           "elementwise copy in the same run; time = dispatch time in the FETCH_SIZE run. Peak 8000 GB/s.", "",
+           "| Kernel | Dispatches | HBM read GB | HBM write GB | ms | GB/s | % of peak |",
+           "|---|---|---|---|---|---|---|"]
+    res = {}
+    for k, e in sorted(byk.items(), key=lambda x: -sum(x[1]["t"])):
+        n = len(e["t"])
+        rd = sum(e["FETCH_SIZE"]) / max(1, len(e["FETCH_SIZE"]))
+        wr = sum(e["WRITE_SIZE"]) / max(1, len(e["WRITE_SIZE"]))
+        t = sum(e["t"]) / n
+        gbs = (rd + wr) / t / 1e9
+        res[k] = {"read": rd, "write": wr, "ms": t * 1e3, "gbs": gbs}
+        out.append(f"| {k} | {n} | {rd / 1e9:.3f} | {wr / 1e9:.3f} | {t * 1e3:.3f} | {gbs:.0f} | "
+                   f"{100 * gbs / PEAK_HBM_GBS:.1f} % |")
+    # the bytes each stage must move (bench.py's accounting of the same call)
+    # over its kernels' time in this run
+    kernels_of = {"meanpool": ("moba::meanpool_kernel", "moba::mu_split_kernel"),
+                  "gate": ("moba::gate_mfma_kernel",),
+                  "dispatch": ("moba::scatter_kernel", "moba::tile_plan_kernel", "moba::list_scan_kernel"),
+                  "kv_layout": ("moba::kv_image_kernel",)}
+    out += ["", "Per stage, the bytes it must move (bench.py's accounting of the same call) over its kernels' time "
+            "in this run:", "",
+            "| Stage | kernels | algorithmic GB per call | ms per call | GB/s | % of peak |", "|---|---|---|---|---|---|"]
+    for name, ks in kernels_of.items():
+        if name not in st:
+            continue
+        t = sum(sum(e["t"]) for k, e in byk.items() if k.startswith(ks))
+        if t <= 0:
+            continue
+        gb = st[name]["work_per_step"]
+        out.append(f"| {name} | {', '.join(k.split('::')[1] for k in ks)} | {gb / 1e9:.3f} | {t * 1e3:.3f} | "
+                   f"{gb / t / 1e9:.0f} | {100 * gb / t / 1e9 / PEAK_HBM_GBS:.1f} % |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    return res
+
+
 DECODE_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_decode -o run -- "
                     "python3 -u bench.py --decode --decode-skip-dense --steps 20 --warmup 3 --no-cpu-baseline "
                     "> gpurun_out/trace_decode.json")
@@ -727,7 +859,18 @@ def main():
                     help="write the traffic summary from two rocprofv3 --pmc runs, then exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
                     help="write the kernel-trace summary from a rocprofv3 --stats run, then exit")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="write the MFMA-busy summary from a rocprofv3 --pmc run, then exit")
+    ap.add_argument("--summarize-hbm", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
+                    help="write the per-kernel HBM summary from the two traffic runs, then exit")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        print(json.dumps(summarize_mfma(args.summarize_mfma, MFMA_FILE), indent=1))
+        return
+    if args.summarize_hbm:
+        f, w, bj = args.summarize_hbm
+        print(json.dumps(summarize_stage_hbm(f, w, 1024, bj, HBM_STAGES_FILE), indent=1))
+        return
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic, 1024, TRAFFIC_FILE), indent=1))
         return
