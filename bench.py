@@ -308,8 +308,24 @@ def summarize_traffic(fetch_dir, write_dir, calib_mib, out_path):
 MFMA_CMD = ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv "
             "-d gpurun_out/pmc_mfma -o run -- python3 -u bench.py --steps 1 --warmup 0 --secondary '' "
             "--no-cpu-baseline --no-gemm-reference > gpurun_out/pmc_mfma.json")
-HBM_STAGES_FILE = os.path.join(ROOT, "profiles", "hbm_stages_gqa32x8_1m.md")
-MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_busy_gqa32x8_1m.md")
+# the same three counter runs on the 32K workload (two untimed calls first)
+PMC32_CMD = ("rocprofv3 --pmc {counters} --output-format csv -d gpurun_out/pmc32k_{tag} -o run -- "
+             "python3 -u bench.py --workload mha32_32k_needle --steps 1 --warmup 2 --secondary '' "
+             "--no-cpu-baseline --no-gemm-reference --copy-calibration 1024 > gpurun_out/pmc32k_{tag}.json")
+PROFILE_CMDS = {
+    "gqa32x8_1m": {"title": "gqa32x8_1m workload (1M tokens, 32/8 heads, D 128, block 4096, top-12)",
+                   "fetch": PMC_CMD.format(counter="FETCH_SIZE"), "write": PMC_CMD.format(counter="WRITE_SIZE"),
+                   "mfma": MFMA_CMD},
+    "mha32_32k_needle": {"title": "mha32_32k_needle workload (32K tokens, 32 heads, D 128, block 512, top-3)",
+                         "fetch": PMC32_CMD.format(counters="FETCH_SIZE", tag="FETCH_SIZE"),
+                         "write": PMC32_CMD.format(counters="WRITE_SIZE", tag="WRITE_SIZE"),
+                         "mfma": PMC32_CMD.format(counters="SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+                                                  tag="mfma")},
+}
+
+
+def _workload_of(bench_json):
+    return json.loads(open(bench_json).read().strip().splitlines()[-1])["config"]["workload"]
 
 
 def _counter_rows(d):
@@ -338,13 +354,16 @@ def _short(name):
     return n.split("(")[0]
 
 
-def summarize_mfma(pmc_dir, out_path):
+def summarize_mfma(pmc_dir, bench_json):
     """MFMA-busy fraction per kernel from SQ_VALU_MFMA_BUSY_CYCLES (summed over
     every SIMD) against GRBM_GUI_ACTIVE (summed over the XCDs): busy =
     MFMA cycles / (GPU cycles per XCD x SIMDs); the clock the kernels ran at =
     GPU cycles per XCD / kernel time."""
     info = _agent_info(pmc_dir)
     simds, xcc = int(info["Simd_Count"]), int(info["Num_Xcc"])
+    wl = _workload_of(bench_json)
+    cmds = PROFILE_CMDS[wl]
+    out_path = os.path.join(ROOT, "profiles", f"mfma_busy_{wl}.md")
     per = {}
     for r in _counter_rows(pmc_dir):
         k = _short(r["Kernel_Name"])
@@ -354,9 +373,9 @@ def summarize_mfma(pmc_dir, out_path):
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         d["disp"].add(r["Dispatch_Id"])
         d["t"][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
-    out = ["# MFMA busy: MoBA forward, gqa32x8_1m workload (1M tokens, 32/8 heads, D 128, block 4096, top-12)",
-           "", "Command (run from the repository root on one MI355X):", "", "```", MFMA_CMD, "```", "",
-           f"Counters summed over the dispatches of one forward call; {simds} SIMDs, {xcc} XCDs. "
+    out = [f"# MFMA busy: MoBA forward, {cmds['title']}",
+           "", "Command (run from the repository root on one MI355X):", "", "```", cmds["mfma"], "```", "",
+           f"Counters summed over the dispatches of the run's forward calls; {simds} SIMDs, {xcc} XCDs. "
            "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs); clock = "
            "(GRBM_GUI_ACTIVE / XCDs) / kernel time.", "",
            "| Kernel | Dispatches | Kernel ms (sum) | MFMA busy | Clock GHz |", "|---|---|---|---|---|"]
@@ -374,12 +393,15 @@ def summarize_mfma(pmc_dir, out_path):
     return res
 
 
-def summarize_stage_hbm(fetch_dir, write_dir, calib_mib, bench_json, out_path):
+def summarize_stage_hbm(fetch_dir, write_dir, calib_mib, bench_json):
     """HBM bytes per dispatch of every MoBA kernel from FETCH_SIZE and
     WRITE_SIZE (scaled by the calibration copy, as for the past-block kernel),
     over the dispatch time in the same counter run, beside the bytes the stage
     must move (bench.py's own accounting, HIP-event time)."""
     calib_kib = calib_mib * 1024.0
+    wl = _workload_of(bench_json)
+    cmds = PROFILE_CMDS[wl]
+    out_path = os.path.join(ROOT, "profiles", f"hbm_stages_{wl}.md")
     byk = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == counter]
@@ -397,9 +419,9 @@ def summarize_stage_hbm(fetch_dir, write_dir, calib_mib, bench_json, out_path):
                 e["t"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
     line = json.loads(open(bench_json).read().strip().splitlines()[-1])
     st = line["stages"]
-    out = ["# HBM traffic per kernel: MoBA forward, gqa32x8_1m workload (1M tokens, 32/8 heads, D 128, block 4096, top-12)",
+    out = [f"# HBM traffic per kernel: MoBA forward, {cmds['title']}",
            "", "Commands (run from the repository root on one MI355X):", "", "```",
-           PMC_CMD.format(counter="FETCH_SIZE"), PMC_CMD.format(counter="WRITE_SIZE"), "```", "",
+           cmds["fetch"], cmds["write"], "```", "",
            f"FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what each reads for a {calib_mib} MiB "
            "elementwise copy in the same run; time = dispatch time in the FETCH_SIZE run. Peak 8000 GB/s.", "",
            "| Kernel | Dispatches | HBM read GB | HBM write GB | ms | GB/s | % of peak |",
@@ -423,10 +445,12 @@ def summarize_stage_hbm(fetch_dir, write_dir, calib_mib, bench_json, out_path):
     out += ["", "Per stage, the bytes it must move (bench.py's accounting of the same call) over its kernels' time "
             "in this run:", "",
             "| Stage | kernels | algorithmic GB per call | ms per call | GB/s | % of peak |", "|---|---|---|---|---|---|"]
+    line_w = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    calls = line_w["steps"] + line_w["warmup"]
     for name, ks in kernels_of.items():
         if name not in st:
             continue
-        t = sum(sum(e["t"]) for k, e in byk.items() if k.startswith(ks))
+        t = sum(sum(e["t"]) for k, e in byk.items() if k.startswith(ks)) / calls
         if t <= 0:
             continue
         gb = st[name]["work_per_step"]
@@ -859,17 +883,17 @@ def main():
                     help="write the traffic summary from two rocprofv3 --pmc runs, then exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
                     help="write the kernel-trace summary from a rocprofv3 --stats run, then exit")
-    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "BENCH_JSON"),
                     help="write the MFMA-busy summary from a rocprofv3 --pmc run, then exit")
     ap.add_argument("--summarize-hbm", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
                     help="write the per-kernel HBM summary from the two traffic runs, then exit")
     args = ap.parse_args()
     if args.summarize_mfma:
-        print(json.dumps(summarize_mfma(args.summarize_mfma, MFMA_FILE), indent=1))
+        print(json.dumps(summarize_mfma(*args.summarize_mfma), indent=1))
         return
     if args.summarize_hbm:
-        f, w, bj = args.summarize_hbm
-        print(json.dumps(summarize_stage_hbm(f, w, 1024, bj, HBM_STAGES_FILE), indent=1))
+        print(json.dumps(summarize_stage_hbm(args.summarize_hbm[0], args.summarize_hbm[1], 1024,
+                                             args.summarize_hbm[2]), indent=1))
         return
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic, 1024, TRAFFIC_FILE), indent=1))
