@@ -618,13 +618,17 @@ struct ImgStager {
 
 // Past-block tiles of 256 rows over a block that is a whole number of
 // slices, from the K and V^T images.  8 waves (two per SIMD) run in step:
-// per slice the scores, the softmax and P V, one barrier per slice; the
-// loads of slice s+2 are issued at the start of slice s into one of two
-// register sets and written to LDS (double-buffered) at the end of slice
-// s+1, so each load has two slice iterations to arrive.
+// per slice the scores, the softmax and P V, one barrier per slice.  The
+// images go straight from HBM into LDS (global_load_lds, no registers on
+// the way): the loads of slice s+2 are issued at the start of slice s into
+// the third of three LDS buffers, so each has two slice iterations to
+// arrive, and the barrier that ends slice s first waits until only the
+// youngest slice's loads are in flight.
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_past_img_kernel(PastArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * SLICE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lb0[SLICE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lb1[SLICE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lb2[SLICE_BYTES];
   constexpr int ROWS = NW * 32;
   const int32_t total = a.tiles[0];
   const int32_t per_xcd = (total + 7) >> 3;
@@ -664,14 +668,41 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto src = [&](int sl) { return (int64_t)(sl < nsl ? sl : nsl - 1) * (KT * HD); };
   const float c = a.scale_log2;
 
-  ImgStager<NW> st, st2;
-  st.load(kimg, vimg);
-  st.store(smem);
-  // the query rows and slice 0 must be in before the prefetch loads go out:
-  // a wait for them inside the loop would also wait for the younger loads
-  drain_vmem();
-  st2.load(kimg + src(1), vimg + src(1));
-  __syncthreads();
+  // The loads into LDS are written as inline asm, so the compiler neither
+  // tracks them nor adds waits for them; the explicit wait before each
+  // barrier (vmcnt: at most the youngest slice's loads in flight) and the
+  // barrier publish a slice to every wave, and the asm memory clobbers keep
+  // the LDS reads on their side of it.  A buffer is loaded again only after
+  // the barrier that ends the slice that read it.
+  constexpr int NT = NW * 64;
+  constexpr int NU = 1024 / NT;
+  // one 16-byte unit per lane from global memory into LDS at m0 + 16 * lane
+  // (m0 = the wave's base, saved and restored around the load)
+  auto lds_dma16 = [](uint32_t lds_base, const void* gptr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(gptr)
+        : "memory");
+  };
+  auto dma = [&](char* lb, int sl) {
+    const uint16_t* ks = kimg + src(sl);
+    const uint16_t* vs = vimg + src(sl);
+    typedef __attribute__((address_space(3))) char lds_char;
+    const uint32_t lb_addr = (uint32_t)(uintptr_t)((lds_char*)lb);
+#pragma unroll
+    for (int x = 0; x < NU; ++x) {
+      const int u = tid + NT * x;
+      const uint32_t wb = __builtin_amdgcn_readfirstlane(lb_addr + (uint32_t)(((tid & ~63) + NT * x) * 16));
+      lds_dma16(wb, ks + u * 8);
+      lds_dma16(wb + IMG_BYTES, vs + u * 8);
+    }
+  };
   auto slice = [&](const char* buf) {
     f32x16 sc[2];
     uint32_t pk[2][8];
@@ -679,18 +710,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     softmax_p<false>(sc, R, c, lane, NoMask{}, pk);
     pv_img(buf + IMG_BYTES + vofs, pk, R);
   };
-  for (int sl = 0; sl < nsl; sl += 2) {
-    // slice sl in buffer 0; slice sl+1 in flight in st2
-    st.load(kimg + src(sl + 2), vimg + src(sl + 2));
-    slice(smem);
-    if (sl + 1 < nsl) st2.store(smem + SLICE_BYTES);
-    __syncthreads();
+  static_assert(2 * NU == 4, "the barrier below leaves four loads in flight");
+  // wait until at most one slice's loads (this thread's 4) are in flight,
+  // then the barrier; no fence, so the younger slice's loads stay in flight
+  // (a fence would wait for every load into LDS); the memory clobber keeps
+  // the compiler from moving LDS accesses across
+  auto publish = [] { asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory"); };
+  drain_vmem();  // the query rows in before any slice load goes out
+  dma(lb0, 0);
+  dma(lb1, 1);
+  publish();
+  auto step = [&](int sl, char* cur, char* nx2) {
+    dma(nx2, sl + 2);  // past the end: the last slice again
+    slice(cur);
+    publish();  // slice sl + 1 in, in every wave
+  };
+  for (int sl = 0; sl < nsl; sl += 3) {
+    step(sl, lb0, lb2);
     if (sl + 1 >= nsl) break;
-    // slice sl+1 in buffer 1; slice sl+2 in flight in st
-    st2.load(kimg + src(sl + 3), vimg + src(sl + 3));
-    slice(smem + SLICE_BYTES);
-    if (sl + 2 < nsl) st.store(smem);
-    __syncthreads();
+    step(sl + 1, lb1, lb0);
+    if (sl + 2 >= nsl) break;
+    step(sl + 2, lb2, lb1);
   }
   drain_vmem();
 
