@@ -28,8 +28,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (datasheet)
 METRIC = "MoBA prefill fwd useful TFLOP/s + tokens/s at 32K and 1M; MFMA util %"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_past_gqa32x8_1m.json")
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_40_amd", "csrc", "attn_bf16.hip")
-# the past-block attention kernel the 1M workload runs (256-row tiles fed from the K/V slice images)
-PAST_KERNEL = "moba::attn_past_img_kernel<8>"
+# the past-block attention kernel the 1M workload runs (384-row tiles fed from the K/V slice images)
+PAST_KERNEL = "moba::attn_past_img_kernel<12>"
 PAST_TAG = "attn_past"
 
 

@@ -17,11 +17,12 @@
 //       same online softmax as further groups of keys (their loads overlap
 //       the slice loop), then the bf16 output.
 //
-// Work split inside a work-group: every wave owns 32 query rows; 4 or 8
-// waves share each K/V slice staged in LDS, and two waves per SIMD let one
-// wave's softmax arithmetic overlap the other's MFMAs.  Slices are
-// double-buffered: the global loads of slice s+1 are in flight while slice
-// s is computed, and one barrier per slice separates the buffer hand-over.
+// Work split inside a work-group: every wave owns 32 query rows; 4, 8 or 12
+// waves share each K/V slice staged in LDS, and two or three waves per SIMD
+// let one wave's softmax arithmetic overlap another's MFMAs.  Slices are
+// loaded ahead while the current one is computed (into registers, or
+// straight into a third LDS buffer on the slice-image path), and one barrier
+// per slice separates the buffer hand-over.
 //
 // Tile mathematics (per wave, per 64-key slice, D = 128):
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = keys from LDS, B = the
@@ -616,8 +617,8 @@ struct ImgStager {
   }
 };
 
-// Past-block tiles of 256 rows over a block that is a whole number of
-// slices, from the K and V^T images.  8 waves (two per SIMD) run in step:
+// Past-block tiles of 384 rows over a block that is a whole number of
+// slices, from the K and V^T images.  12 waves (three per SIMD) run in step:
 // per slice the scores, the softmax and P V, one barrier per slice.  The
 // images go straight from HBM into LDS (global_load_lds, no registers on
 // the way): the loads of slice s+2 are issued at the start of slice s into
@@ -625,7 +626,7 @@ struct ImgStager {
 // arrive, and the barrier that ends slice s first waits until only the
 // youngest slice's loads are in flight.
 template <int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_past_img_kernel(PastArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void attn_past_img_kernel(PastArgs a) {
   __shared__ __attribute__((aligned(16))) char lb0[SLICE_BYTES];
   __shared__ __attribute__((aligned(16))) char lb1[SLICE_BYTES];
   __shared__ __attribute__((aligned(16))) char lb2[SLICE_BYTES];
@@ -674,8 +675,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // barrier publish a slice to every wave, and the asm memory clobbers keep
   // the LDS reads on their side of it.  A buffer is loaded again only after
   // the barrier that ends the slice that read it.
-  constexpr int NT = NW * 64;
-  constexpr int NU = 1024 / NT;
+  // each image is 16 chunks of 64 units; wave w loads chunks w % 16 and
+  // 15 - w % 16 (with 12 waves chunks 4..11 are loaded twice, same data)
+  static_assert(NW == 8 || NW == 12, "two chunks per image and wave");
   // one 16-byte unit per lane from global memory into LDS at m0 + 16 * lane
   // (m0 = the wave's base, saved and restored around the load)
   auto lds_dma16 = [](uint32_t lds_base, const void* gptr) {
@@ -696,9 +698,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     typedef __attribute__((address_space(3))) char lds_char;
     const uint32_t lb_addr = (uint32_t)(uintptr_t)((lds_char*)lb);
 #pragma unroll
-    for (int x = 0; x < NU; ++x) {
-      const int u = tid + NT * x;
-      const uint32_t wb = __builtin_amdgcn_readfirstlane(lb_addr + (uint32_t)(((tid & ~63) + NT * x) * 16));
+    for (int x = 0; x < 2; ++x) {
+      const int chunk = NW == 8 ? wave + 8 * x : (x == 0 ? wave : 15 - wave);
+      const int u = chunk * 64 + lane;
+      const uint32_t wb = __builtin_amdgcn_readfirstlane(lb_addr + (uint32_t)(chunk * 64 * 16));
       lds_dma16(wb, ks + u * 8);
       lds_dma16(wb + IMG_BYTES, vs + u * 8);
     }
@@ -710,7 +713,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     softmax_p<false>(sc, R, c, lane, NoMask{}, pk);
     pv_img(buf + IMG_BYTES + vofs, pk, R);
   };
-  static_assert(2 * NU == 4, "the barrier below leaves four loads in flight");
+
   // wait until at most one slice's loads (this thread's 4) are in flight,
   // then the barrier; no fence, so the younger slice's loads stay in flight
   // (a fence would wait for every load into LDS); the memory clobber keeps
@@ -915,10 +918,10 @@ int launch_attn_past(const PastArgs& a, hipStream_t st) {
   if (a.tile_rows == 256) {
     // 8 waves, one work-group per CU; from the slice images the loads run two
     // slices ahead, otherwise one (any block size)
-    if (a.block % KT == 0 && a.kimg)
-      hipLaunchKernelGGL((attn_past_img_kernel<8>), grid, dim3(512), 0, st, a);
-    else
-      hipLaunchKernelGGL((attn_past_kernel<8>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((attn_past_kernel<8>), grid, dim3(512), 0, st, a);
+  } else if (a.tile_rows == 384) {
+    // 12 waves (three per SIMD) over the slice images
+    hipLaunchKernelGGL((attn_past_img_kernel<12>), grid, dim3(768), 0, st, a);
   } else {
     // 4 waves, two independent work-groups per CU
     hipLaunchKernelGGL((attn_past_kernel<4>), grid, dim3(256), 0, st, a);

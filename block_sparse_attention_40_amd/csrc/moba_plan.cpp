@@ -56,7 +56,11 @@ int make_plan(const Shape& s, Plan* p) {
   q.max_pairs = chunk_pos * s.hq * (int64_t)q.kp;
   if (q.max_pairs >= (int64_t(1) << 31)) return MOBA_ERR_SHAPE;
   const int64_t lists = (int64_t)s.hkv * q.n;
+  // long lists: 384-row tiles over the K/V slice images (bf16, whole slices),
+  // else 256; short lists: 128
   q.tile_rows = (q.max_pairs / lists >= kLargeTileMinRows) ? kTileRowsLarge : kTileRowsSmall;
+  if (q.tile_rows == kTileRowsLarge && s.dtype == MOBA_DTYPE_BF16 && s.block % kSliceKeys == 0)
+    q.tile_rows = kTileRowsImage;
   q.max_tiles = (q.max_pairs + q.tile_rows - 1) / q.tile_rows + lists;
   q.max_tiles = (q.max_tiles + 7) / 8 * 8;
 
@@ -71,12 +75,12 @@ int make_plan(const Shape& s, Plan* p) {
   q.off_entries = take((size_t)std::max<int64_t>(q.max_pairs, 1) * sizeof(int32_t));
   q.off_part_o = take((size_t)std::max<int64_t>(q.max_pairs, 1) * s.d * sizeof(uint16_t));
   q.off_part_lse = take((size_t)std::max<int64_t>(q.max_pairs, 1) * sizeof(float));
-  // K and V^T slice images for the 256-row past-block tiles:
+  // K and V^T slice images for the 384-row past-block tiles:
   // [batch, hkv, seqlen / 64, 64 x 128] bf16 each, as large as K and V
   // (and for the own-block kernel alone when no past block is chosen and the
   // blocks are long, e.g. block_size = seqlen: dense causal attention)
   q.kv_image = s.dtype == MOBA_DTYPE_BF16 && s.block % kSliceKeys == 0 &&
-               (q.kp > 0 ? q.tile_rows == kTileRowsLarge : s.block >= kOwnImageMinBlock);
+               (q.kp > 0 ? q.tile_rows == kTileRowsImage : s.block >= kOwnImageMinBlock);
   const size_t img = q.kv_image ? (size_t)s.batch * s.hkv * s.seqlen * s.d * sizeof(uint16_t) : 0;
   q.off_kimg = take(img);
   q.off_vimg = take(img);

@@ -9,10 +9,12 @@ namespace moba {
 
 // Rows of one gate work-group (threads; one query row per thread).
 constexpr int kGateRows = 256;
-// Query rows of one past-block attention tile: 4 or 8 waves x 32 rows,
-// the larger when the per-block row lists are long.
+// Query rows of one past-block attention tile: 4, 8 or 12 waves x 32 rows,
+// the larger when the per-block row lists are long; 12 waves (three per
+// SIMD) when the tile reads the K/V slice images (bf16, whole 64-key slices).
 constexpr int kTileRowsSmall = 128;
 constexpr int kTileRowsLarge = 256;
+constexpr int kTileRowsImage = 384;
 // Mean list length from which the large tile is used.
 constexpr int64_t kLargeTileMinRows = 2048;
 // Query rows of one own-block attention tile (8 waves x 32 rows).

@@ -125,7 +125,7 @@ SMALL = [
     small("b16_tiny_blocks", "bf16", 1, 512, 2, 2, 128, 16, 4),
     small("b2048_long", "bf16", 1, 8192, 4, 1, 128, 2048, 2),
     small("single_block", "bf16", 1, 256, 2, 2, 128, 256, 3),
-    # groups that do not divide the 256-row tiles (g = 3: 85 positions x 3
+    # groups that do not divide the 256-row own-block tiles (g = 3: 85 positions x 3
     # heads) and a group of 32 (8 positions x 32 heads per tile)
     small("gqa_g3", "bf16", 1, 2048, 6, 2, 128, 128, 4),
     small("gqa_g32", "bf16", 1, 1024, 32, 1, 128, 128, 3),
@@ -146,7 +146,7 @@ SMALL = [
 
 GRAPH_CASES = [
     small("graph_small_tiles", "bf16", 1, 2048, 4, 2, 128, 256, 3, seed=31),
-    # 256-row tiles: the K/V slice images are built inside the captured call
+    # 384-row tiles: the K/V slice images are built inside the captured call
     small("graph_images", "bf16", 1, 8192, 4, 1, 128, 2048, 2, seed=32),
 ]
 
@@ -284,7 +284,7 @@ def test_workload_tiny_f32_1k_both_topk():
 
 
 def test_forward_batch2_slice_images_sampled():
-    """Long per-block row lists at batch 2: 256-row tiles fed from the K/V
+    """Long per-block row lists at batch 2: 384-row tiles fed from the K/V
     slice images, whose offsets depend on the batch entry."""
     w = small("gqa_b2_images", "bf16", 2, 8192, 32, 8, 128, 256, 8, seed=23)
     run(w, rows=W.sample_rows(w, 48, seed=24), device_inputs=True)
