@@ -754,12 +754,19 @@ constexpr int OWN_NW = 8;  // own-block tiles: 8 waves x 32 rows
 template <bool kImg>
 __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kImg ? 2 * SLICE_BYTES : 2 * BUF_ELEMS * 2];
+  // XCD-aware order: work-group i runs on XCD i % 8, and each XCD takes a
+  // contiguous run of tiles, ordered (block, KV head, tile), so the tiles
+  // that read one block's K/V slices share that XCD's L2
   const int64_t tiles_per_block = (a.block + a.own_t - 1) / a.own_t;
-  const int64_t jl = blockIdx.x / tiles_per_block;               // block inside the chunk
+  const int64_t total = (a.cnt / a.block) * tiles_per_block * a.hkv;
+  const int64_t per_xcd = (total + 7) >> 3;
+  const int64_t lt = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lt >= total) return;
+  const int64_t jl = lt / tiles_per_block / a.hkv;  // block inside the chunk
+  const int hk = (int)(lt / tiles_per_block % a.hkv);
   // the tiles of a block launch last position first: the longest causal
   // ranges start earliest, so the grid does not end on them
-  const int64_t p0 = (tiles_per_block - 1 - blockIdx.x % tiles_per_block) * a.own_t;  // first position
-  const int hk = blockIdx.y;
+  const int64_t p0 = (tiles_per_block - 1 - lt % tiles_per_block) * a.own_t;  // first position
   const int64_t j = a.t0 / a.block + jl;
   const int G = a.g;
 
@@ -939,7 +946,8 @@ int launch_kv_image(const void* k, const void* v, int64_t batch, int64_t seqlen,
 int launch_attn_own(const OwnArgs& a, hipStream_t st) {
   const int64_t tiles_per_block = (a.block + a.own_t - 1) / a.own_t;
   const int64_t nblk = a.cnt / a.block;
-  const dim3 grid((unsigned)(nblk * tiles_per_block), (unsigned)a.hkv);
+  const int64_t per_xcd = (nblk * tiles_per_block * a.hkv + 7) / 8;  // see attn_own_kernel
+  const dim3 grid((unsigned)(8 * per_xcd));
   if (a.kimg && a.block % KT == 0)
     hipLaunchKernelGGL(attn_own_kernel<true>, grid, dim3(OWN_NW * 64), 0, st, a);
   else

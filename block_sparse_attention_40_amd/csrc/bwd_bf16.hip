@@ -96,8 +96,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   int64_t blk, own_p0 = 0;
   int32_t start = 0;
   if constexpr (!kOwn) {
+    // XCD-aware order: work-group i runs on XCD i % 8, and each XCD takes a
+    // contiguous run of tiles, so the tiles of one list share an L2
     const int32_t total = a.tiles[0];
-    const int32_t tile = (int32_t)blockIdx.x;
+    const int32_t per_xcd = (total + 7) >> 3;
+    const int32_t loc = (int32_t)(blockIdx.x >> 3);
+    if (loc >= per_xcd) return;
+    const int32_t tile = (int32_t)(blockIdx.x & 7) * per_xcd + loc;
     if (tile >= total) return;
     const int32_t L = a.tiles[8 + 2 * tile];
     start = a.tiles[9 + 2 * tile];
@@ -108,9 +113,14 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   } else {
     const int ppt = 256 / a.g;  // positions per tile
     const int64_t tpb = (a.block + ppt - 1) / ppt;
-    hk = (int)blockIdx.y;
-    blk = a.t0 / a.block + blockIdx.x / tpb;
-    own_p0 = (int64_t)(blockIdx.x % tpb) * ppt;
+    // the same XCD-aware order over (block, KV head, tile)
+    const int64_t total = tpb * (a.cnt / a.block) * a.hkv;
+    const int64_t per_xcd = (total + 7) >> 3;
+    const int64_t lt = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (lt >= total) return;
+    hk = (int)(lt / tpb % a.hkv);
+    blk = a.t0 / a.block + lt / tpb / a.hkv;
+    own_p0 = (lt % tpb) * ppt;
     const int64_t np = (a.block - own_p0) < ppt ? (a.block - own_p0) : ppt;
     cnt = (int)np * a.g;
   }
@@ -535,7 +545,8 @@ int launch_bwd_dq(const BwdArgs& a, int64_t max_tiles, hipStream_t st) {
     const int ppt = 256 / a.g;
     const int64_t tpb = (a.block + ppt - 1) / ppt;
     const int64_t nblk = a.cnt / a.block;
-    hipLaunchKernelGGL((bwd_dq_kernel<true>), dim3((unsigned)(tpb * nblk), (unsigned)a.hkv), dim3(512), 0, st, a);
+    const int64_t per_xcd = (tpb * nblk * a.hkv + 7) / 8;  // see bwd_dq_kernel
+    hipLaunchKernelGGL((bwd_dq_kernel<true>), dim3((unsigned)(8 * per_xcd)), dim3(512), 0, st, a);
   }
   const int64_t rows = a.cnt * a.hq;
   hipLaunchKernelGGL(bwd_dq_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a);
