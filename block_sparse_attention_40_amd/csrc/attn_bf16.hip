@@ -754,13 +754,16 @@ constexpr int OWN_NW = 8;  // own-block tiles: 8 waves x 32 rows
 template <bool kImg>
 __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kImg ? 2 * SLICE_BYTES : 2 * BUF_ELEMS * 2];
-  // XCD-aware order: work-group i runs on XCD i % 8, and each XCD takes a
-  // contiguous run of tiles, ordered (block, KV head, tile), so the tiles
-  // that read one block's K/V slices share that XCD's L2
+  // Tiles in (block, KV head, tile) order.  XCD-aware: work-group i runs on
+  // XCD i % 8, and with at least 64 (block, KV head) units each XCD takes a
+  // contiguous run of tiles, so the tiles that read one block's K/V slices
+  // share that XCD's L2.  With fewer units a run would hold a few units'
+  // longest tiles (causal tiles differ in length), so they are dealt round
+  // robin instead.
   const int64_t tiles_per_block = (a.block + a.own_t - 1) / a.own_t;
-  const int64_t total = (a.cnt / a.block) * tiles_per_block * a.hkv;
-  const int64_t per_xcd = (total + 7) >> 3;
-  const int64_t lt = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int64_t units = (a.cnt / a.block) * a.hkv;
+  const int64_t total = units * tiles_per_block;
+  const int64_t lt = units >= 64 ? (int64_t)(blockIdx.x & 7) * ((total + 7) >> 3) + (blockIdx.x >> 3) : (int64_t)blockIdx.x;
   if (lt >= total) return;
   const int64_t jl = lt / tiles_per_block / a.hkv;  // block inside the chunk
   const int hk = (int)(lt / tiles_per_block % a.hkv);

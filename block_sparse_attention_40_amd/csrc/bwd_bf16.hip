@@ -113,10 +113,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   } else {
     const int ppt = 256 / a.g;  // positions per tile
     const int64_t tpb = (a.block + ppt - 1) / ppt;
-    // the same XCD-aware order over (block, KV head, tile)
-    const int64_t total = tpb * (a.cnt / a.block) * a.hkv;
-    const int64_t per_xcd = (total + 7) >> 3;
-    const int64_t lt = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    // (block, KV head, tile) order; with at least 64 (block, KV head) units
+    // each XCD takes a contiguous run of tiles, else they are dealt round
+    // robin (a run would hold a few units' longest tiles)
+    const int64_t units = (a.cnt / a.block) * a.hkv;
+    const int64_t total = tpb * units;
+    const int64_t lt = units >= 64 ? (int64_t)(blockIdx.x & 7) * ((total + 7) >> 3) + (blockIdx.x >> 3) : (int64_t)blockIdx.x;
     if (lt >= total) return;
     hk = (int)(lt / tpb % a.hkv);
     blk = a.t0 / a.block + lt / tpb / a.hkv;

@@ -288,8 +288,10 @@ int fwd_impl(const void* q, const void* k, const void* v, int64_t batch, int64_t
   const double elt = bf16 ? 2.0 : 4.0;
   const double D = head_dim;
   float* lohi = reinterpret_cast<float*>(ws + p.off_lohi);
-  // 1. block summaries of the keys (means, or min / max), all blocks of all batch entries
-  {
+  // 1. block summaries of the keys (means, or min / max), all blocks of all
+  // batch entries.  Only the gate's ranking reads them: when the top-k
+  // covers every candidate block no row ranks, and they are not computed.
+  if (p.selective) {
     StageScope sc(MOBA_STAGE_MEANPOOL, s,
                   (double)batch * seqlen * num_kv_heads * D * elt +
                       (double)batch * num_kv_heads * p.n * D * (minmax ? 8.0 : 4.0));
