@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     moba_gate,
     moba_meanpool,
     moba_minmaxpool,
+    plan_chunk_blocks,
     profile_enable,
     profile_read,
     STAGES,

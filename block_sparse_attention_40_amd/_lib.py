@@ -28,6 +28,10 @@ SIGNATURES = {
     "moba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moba_workspace_bytes": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                             _c_i32, ctypes.POINTER(_c_sz)]),
+    "moba_workspace_bytes_chunked": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                    _c_i32, _c_i32, _c_i64, ctypes.POINTER(_c_sz)]),
+    "moba_plan_chunk_blocks": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                              _c_i32, _c_sz, ctypes.POINTER(_c_i64)]),
     "moba_attn_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "moba_attn_fwd_gate": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -108,14 +112,76 @@ def _check_dev(*ts: torch.Tensor):
             raise ValueError("tensors must be contiguous")
 
 
+def _check_shape(t: torch.Tensor, name: str, shape, dtype: torch.dtype):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _check_on(t: torch.Tensor, name: str, device: torch.device):
+    _check_dev(t)
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _check_like(t: torch.Tensor, name: str, shape, dtype: torch.dtype, device: torch.device):
+    """t must be a contiguous GPU tensor of exactly this shape and dtype on
+    `device` (the C ABI derives every extent from q, so a mismatched tensor
+    would be read or written out of bounds)."""
+    _check_shape(t, name, shape, dtype)
+    _check_on(t, name, device)
+
+
+def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    """q [b, S, Hq, D]; k, v [b, S, Hkv, D] with Hq a multiple of Hkv, one
+    dtype and one device.  Returns (b, S, Hq, Hkv, D)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [batch, seqlen, heads, head_dim]")
+    b, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"num_q_heads {Hq} must be a multiple of num_kv_heads {Hkv}")
+    _check_shape(k, "k", (b, S, Hkv, D), q.dtype)
+    _check_shape(v, "v", (b, S, Hkv, D), q.dtype)
+    _check_dev(q)
+    _check_on(k, "k", q.device)
+    _check_on(v, "v", q.device)
+    return b, S, Hq, Hkv, D
+
+
 def workspace_bytes(batch: int, seqlen: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                    dtype: int, block_size: int, topk: int, causal: bool = True) -> int:
+                    dtype: int, block_size: int, topk: int, causal: bool = True, max_chunk_blocks: int = 0) -> int:
+    """Forward workspace bytes; max_chunk_blocks > 0 limits the query blocks
+    per chunk (1 gives the smallest workspace the forward accepts)."""
     out = _c_sz(0)
-    st = lib.moba_workspace_bytes(batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
-                                  int(bool(causal)), ctypes.byref(out))
+    st = lib.moba_workspace_bytes_chunked(batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size,
+                                          topk, int(bool(causal)), int(max_chunk_blocks), ctypes.byref(out))
     if st != MOBA_OK:
-        raise MobaError(st, "moba_workspace_bytes")
+        raise MobaError(st, "moba_workspace_bytes_chunked")
     return int(out.value)
+
+
+def plan_chunk_blocks(batch: int, seqlen: int, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int,
+                      block_size: int, topk: int, causal: bool, workspace_bytes_: int) -> int:
+    """Query blocks per chunk the forward runs with a workspace of that size."""
+    out = _c_i64(0)
+    st = lib.moba_plan_chunk_blocks(batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
+                                    int(bool(causal)), int(workspace_bytes_), ctypes.byref(out))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_plan_chunk_blocks")
+    return int(out.value)
+
+
+def _workspace(workspace: Optional[torch.Tensor], nbytes, device: torch.device) -> torch.Tensor:
+    """The caller's workspace (checked to be on `device`), or a new one of
+    nbytes() bytes.  The C ABI checks its size."""
+    if workspace is None:
+        return torch.empty(nbytes(), dtype=torch.uint8, device=device)
+    _check_dev(workspace)
+    if workspace.device != device:
+        raise ValueError(f"workspace must be on {device}")
+    return workspace
 
 
 def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int, topk: int,
@@ -130,22 +196,19 @@ def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size:
     "mean" calls moba_attn_fwd, "minmax" moba_attn_fwd_gate."""
     if gate not in GATE_KINDS:
         raise ValueError(f"gate must be one of {sorted(GATE_KINDS)}")
-    _check_dev(q, k, v)
-    b, S, Hq, D = q.shape
-    Hkv = k.shape[2]
+    b, S, Hq, Hkv, D = _check_qkv(q, k, v)
     dt = _dtype_code(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype or k.shape != v.shape:
-        raise ValueError("q, k, v must share dtype; k and v must share shape")
     if out is None:
         out = torch.empty_like(q)
+    _check_like(out, "out", q.shape, q.dtype, q.device)
     if sel_idx is None and return_sel:
         sel_idx = torch.empty((b, Hq, S, topk), dtype=torch.int32, device=q.device)
-    nbytes = workspace_bytes(b, S, Hq, Hkv, D, dt, block_size, topk, causal)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    _check_dev(out, workspace)
     if sel_idx is not None:
-        _check_dev(sel_idx)
+        _check_like(sel_idx, "sel_idx", (b, Hq, S, topk), torch.int32, q.device)
+    # a caller's workspace may be smaller than the default: the forward then
+    # runs in more query chunks
+    workspace = _workspace(workspace, lambda: workspace_bytes(b, S, Hq, Hkv, D, dt, block_size, topk, causal),
+                           q.device)
     sel_ptr = sel_idx.data_ptr() if sel_idx is not None else None
     ws_len = workspace.numel() * workspace.element_size()
     if gate == "mean":
@@ -182,10 +245,14 @@ def profile_read() -> dict:
 
 def moba_meanpool(k: torch.Tensor, block_size: int, mu: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Block means of the keys: mu [b, Hkv, S / block_size, D] fp32."""
-    _check_dev(k)
     b, S, Hkv, D = k.shape
+    shape = (b, Hkv, S // max(block_size, 1), D)
+    if mu is not None:
+        _check_shape(mu, "mu", shape, torch.float32)
+    _check_dev(k)
     if mu is None:
-        mu = torch.empty((b, Hkv, S // max(block_size, 1), D), dtype=torch.float32, device=k.device)
+        mu = torch.empty(shape, dtype=torch.float32, device=k.device)
+    _check_on(mu, "mu", k.device)
     st = lib.moba_meanpool(k.data_ptr(), b, S, Hkv, D, _dtype_code(k), block_size, mu.data_ptr(),
                            _stream_ptr(k.device))
     if st != MOBA_OK:
@@ -196,10 +263,14 @@ def moba_meanpool(k: torch.Tensor, block_size: int, mu: Optional[torch.Tensor] =
 def moba_minmaxpool(k: torch.Tensor, block_size: int, lohi: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Element-wise key min and max per block: lohi [b, Hkv, S / block_size,
     2, D] fp32 (index 0 the min, 1 the max)."""
-    _check_dev(k)
     b, S, Hkv, D = k.shape
+    shape = (b, Hkv, S // max(block_size, 1), 2, D)
+    if lohi is not None:
+        _check_shape(lohi, "lohi", shape, torch.float32)
+    _check_dev(k)
     if lohi is None:
-        lohi = torch.empty((b, Hkv, S // max(block_size, 1), 2, D), dtype=torch.float32, device=k.device)
+        lohi = torch.empty(shape, dtype=torch.float32, device=k.device)
+    _check_on(lohi, "lohi", k.device)
     st = lib.moba_minmaxpool(k.data_ptr(), b, S, Hkv, D, _dtype_code(k), block_size, lohi.data_ptr(),
                              _stream_ptr(k.device))
     if st != MOBA_OK:
@@ -210,11 +281,17 @@ def moba_minmaxpool(k: torch.Tensor, block_size: int, lohi: Optional[torch.Tenso
 def moba_gate(q: torch.Tensor, mu: torch.Tensor, block_size: int, topk: int, causal: bool = True,
               sel_idx: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Gate and top-k: sel_idx [b, Hq, S, topk] int32 from q and block means."""
-    _check_dev(q, mu)
+    if q.dim() != 4 or mu.dim() != 4:
+        raise ValueError("q must be [b, S, Hq, D] and mu [b, Hkv, S / block_size, D]")
     b, S, Hq, D = q.shape
     Hkv = mu.shape[1]
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"num_q_heads {Hq} must be a multiple of mu's num_kv_heads {Hkv}")
+    _check_like(mu, "mu", (b, Hkv, S // max(block_size, 1), D), torch.float32, q.device)
+    _check_dev(q)
     if sel_idx is None:
         sel_idx = torch.empty((b, Hq, S, topk), dtype=torch.int32, device=q.device)
+    _check_like(sel_idx, "sel_idx", (b, Hq, S, topk), torch.int32, q.device)
     st = lib.moba_gate(q.data_ptr(), mu.data_ptr(), b, S, Hq, Hkv, D, _dtype_code(q), block_size, topk,
                        int(bool(causal)), sel_idx.data_ptr(), _stream_ptr(q.device))
     if st != MOBA_OK:
@@ -273,14 +350,17 @@ def moba_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
         raise ValueError("cache_lens must be int32 [batch]")
     if mu_cache.dtype != torch.float32 or tuple(mu_cache.shape) != (b, Hkv, Lmax // max(block_size, 1), D):
         raise ValueError("mu_cache must be fp32 [batch, Hkv, max_len / block_size, D]")
+    if k_cache.dim() != 4 or k_cache.shape[0] != b or k_cache.shape[3] != D or Hq % max(Hkv, 1) != 0:
+        raise ValueError("k_cache / v_cache must be [batch, max_len, Hkv, D] matching q [batch, Hq, D]")
     if out is None:
         out = torch.empty_like(q)
+    _check_like(out, "out", q.shape, q.dtype, q.device)
     if sel_idx is None and return_sel:
         sel_idx = torch.empty((b, Hq, topk), dtype=torch.int32, device=q.device)
-    nbytes = decode_workspace_bytes(b, Lmax, Hq, Hkv, D, dt, block_size, topk)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    _check_dev(out, workspace)
+    if sel_idx is not None:
+        _check_like(sel_idx, "sel_idx", (b, Hq, topk), torch.int32, q.device)
+    workspace = _workspace(workspace, lambda: decode_workspace_bytes(b, Lmax, Hq, Hkv, D, dt, block_size, topk),
+                           q.device)
     st = lib.moba_decode_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), mu_cache.data_ptr(),
                              cache_lens.data_ptr(), b, Lmax, Hq, Hkv, D, dt, block_size, topk, out.data_ptr(),
                              sel_idx.data_ptr() if sel_idx is not None else None, workspace.data_ptr(),
@@ -295,16 +375,13 @@ def moba_attn_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
                         ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Forward for training: (out, sel_idx [b, Hq, S, topk] int32, lse [b, Hq,
     S] fp32, natural log of the row's sum of exp of the scaled logits)."""
-    _check_dev(q, k, v)
-    b, S, Hq, D = q.shape
-    Hkv = k.shape[2]
+    b, S, Hq, Hkv, D = _check_qkv(q, k, v)
     dt = _dtype_code(q)
     out = torch.empty_like(q)
     sel = torch.empty((b, Hq, S, topk), dtype=torch.int32, device=q.device)
     lse = torch.empty((b, Hq, S), dtype=torch.float32, device=q.device)
-    nbytes = workspace_bytes(b, S, Hq, Hkv, D, dt, block_size, topk, causal)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, lambda: workspace_bytes(b, S, Hq, Hkv, D, dt, block_size, topk, causal),
+                           q.device)
     st = lib.moba_attn_fwd_train(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, S, Hq, Hkv, D, dt, block_size, topk,
                                  int(bool(causal)), out.data_ptr(), sel.data_ptr(), lse.data_ptr(),
                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -329,16 +406,17 @@ def moba_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
                   workspace: Optional[torch.Tensor] = None
                   ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Backward with the forward's selection held fixed: (dq, dk, dv)."""
-    _check_dev(q, k, v, out, dout, lse, sel_idx)
-    b, S, Hq, D = q.shape
-    Hkv = k.shape[2]
+    b, S, Hq, Hkv, D = _check_qkv(q, k, v)
+    _check_like(out, "out", q.shape, q.dtype, q.device)
+    _check_like(dout, "dout", q.shape, q.dtype, q.device)
+    _check_like(lse, "lse", (b, Hq, S), torch.float32, q.device)
+    _check_like(sel_idx, "sel_idx", (b, Hq, S, topk), torch.int32, q.device)
     dt = _dtype_code(q)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    nbytes = bwd_workspace_bytes(b, S, Hq, Hkv, D, dt, block_size, topk, causal)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, lambda: bwd_workspace_bytes(b, S, Hq, Hkv, D, dt, block_size, topk, causal),
+                           q.device)
     st = lib.moba_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                            lse.data_ptr(), sel_idx.data_ptr(), b, S, Hq, Hkv, D, dt, block_size, topk,
                            int(bool(causal)), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),

@@ -141,6 +141,9 @@ int make_bwd_plan(const Shape& s, BwdPlan* out) {
   const Plan& p = b.p;
   b.kps = p.kp + (s.causal ? 1 : 0);
   const int64_t S = s.seqlen, rows = s.batch * S * s.hq, lists = (int64_t)s.hkv * p.n;
+  // the whole-sequence dk/dv lists hold one int32 entry (row * kp + slot) per
+  // (row, past block) pair of a batch entry, and their offsets are int32
+  if (S * s.hq * (int64_t)std::max(p.kp, 1) >= (int64_t(1) << 31)) return MOBA_ERR_SHAPE;
   b.gate_wg_f = (S + p.gate_t - 1) / p.gate_t;
   b.max_tiles_f = ((S * s.hq * (int64_t)std::max(p.kp, 0) + 255) / 256 + lists + 7) / 8 * 8;
   const uint64_t per_block = (uint64_t)s.block * s.hq * b.kps * 128 * 4;
@@ -226,7 +229,7 @@ const char* moba_status_string(int status) {
     case MOBA_ERR_SEQ_NOT_DIVISIBLE: return "seqlen is not a multiple of block_size";
     case MOBA_ERR_TOPK: return "topk < 1, or a selective topk above MOBA_MAX_SELECTIVE_TOPK";
     case MOBA_ERR_GQA: return "num_q_heads is not a multiple of num_kv_heads, or the group exceeds 128";
-    case MOBA_ERR_WORKSPACE: return "workspace is NULL or smaller than moba_workspace_bytes()";
+    case MOBA_ERR_WORKSPACE: return "workspace is NULL or too small (forward: below moba_workspace_bytes_chunked(..., 1))";
     case MOBA_ERR_HIP: return "a HIP call or kernel launch failed";
     case MOBA_ERR_SHAPE: return "non-positive or too large sizes";
     case MOBA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
@@ -237,13 +240,33 @@ const char* moba_status_string(int status) {
 int moba_workspace_bytes(int64_t batch, int64_t seqlen, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t dtype, int32_t block_size, int32_t topk, int32_t causal,
                          size_t* bytes) {
+  return moba_workspace_bytes_chunked(batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
+                                      causal, 0, bytes);
+}
+
+int moba_workspace_bytes_chunked(int64_t batch, int64_t seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t dtype, int32_t block_size, int32_t topk, int32_t causal,
+                                 int64_t max_chunk_blocks, size_t* bytes) {
   if (!bytes) return MOBA_ERR_NULL;
   Plan p;
   const int st = make_plan(Shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
                                  causal ? 1 : 0},
-                           &p);
+                           &p, max_chunk_blocks);
   if (st != MOBA_OK) return st;
   *bytes = p.total;
+  return MOBA_OK;
+}
+
+int moba_plan_chunk_blocks(int64_t batch, int64_t seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t dtype, int32_t block_size, int32_t topk, int32_t causal,
+                           size_t workspace_bytes, int64_t* chunk_blocks) {
+  if (!chunk_blocks) return MOBA_ERR_NULL;
+  Plan p;
+  const int st = plan_for_workspace(Shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size,
+                                          topk, causal ? 1 : 0},
+                                    workspace_bytes, &p);
+  if (st != MOBA_OK) return st;
+  *chunk_blocks = p.chunk_blocks;
   return MOBA_OK;
 }
 
@@ -258,13 +281,15 @@ int fwd_impl(const void* q, const void* k, const void* v, int64_t batch, int64_t
              void* stream) {
   if (gate_kind != MOBA_GATE_MEAN && gate_kind != MOBA_GATE_MINMAX) return MOBA_ERR_SHAPE;
   const bool minmax = gate_kind == MOBA_GATE_MINMAX;
+  const Shape shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk, causal ? 1 : 0};
   Plan p;
-  const int st = make_plan(Shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
-                                 causal ? 1 : 0},
-                           &p);
+  int st = make_plan(shape, &p);
   if (st != MOBA_OK) return st;
   if (!q || !k || !v || !out) return MOBA_ERR_NULL;
-  if (!workspace || workspace_bytes < p.total) return MOBA_ERR_WORKSPACE;
+  if (!workspace) return MOBA_ERR_WORKSPACE;
+  // the query chunk is the largest whose workspace fits
+  st = plan_for_workspace(shape, workspace_bytes, &p);
+  if (st != MOBA_OK) return st;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(workspace) ||
       (sel_idx && (reinterpret_cast<uintptr_t>(sel_idx) & 3u)))
     return MOBA_ERR_ALIGN;

@@ -9,7 +9,7 @@ namespace moba {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int make_plan(const Shape& s, Plan* p) {
+int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks) {
   if (!p) return MOBA_ERR_NULL;
   if (s.dtype != MOBA_DTYPE_F32 && s.dtype != MOBA_DTYPE_BF16) return MOBA_ERR_DTYPE;
   if (s.batch < 1 || s.seqlen < 1 || s.hq < 1 || s.hkv < 1 || s.block < 1 || s.d < 1)
@@ -51,6 +51,8 @@ int make_plan(const Shape& s, Plan* p) {
     q.chunk_blocks = (int64_t)std::max<uint64_t>(1, kPartialCapBytes / per_block_partial);
     q.chunk_blocks = std::min<int64_t>(q.chunk_blocks, q.n);
   }
+  if (max_chunk_blocks < 0) return MOBA_ERR_SHAPE;
+  if (max_chunk_blocks > 0) q.chunk_blocks = std::min<int64_t>(q.chunk_blocks, max_chunk_blocks);
   const int64_t chunk_pos = q.chunk_blocks * s.block;
   q.gate_wg = (chunk_pos + q.gate_t - 1) / q.gate_t;
   q.max_pairs = chunk_pos * s.hq * (int64_t)q.kp;
@@ -93,6 +95,36 @@ int make_plan(const Shape& s, Plan* p) {
   q.off_lohi = take((size_t)s.batch * s.hkv * q.n * 2 * s.d * sizeof(float));
   q.total = off;
   *p = q;
+  return MOBA_OK;
+}
+
+int plan_for_workspace(const Shape& s, size_t ws_bytes, Plan* p) {
+  Plan best{};
+  int st = make_plan(s, &best);
+  if (st != MOBA_OK) return st;
+  if (best.total <= ws_bytes) {
+    *p = best;
+    return MOBA_OK;
+  }
+  // the workspace grows with the chunk: find the largest chunk that fits
+  int64_t lo = 1, hi = best.chunk_blocks - 1;
+  Plan cand{};
+  st = make_plan(s, &cand, 1);
+  if (st != MOBA_OK) return st;
+  if (cand.total > ws_bytes) return MOBA_ERR_WORKSPACE;
+  best = cand;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    st = make_plan(s, &cand, mid);
+    if (st != MOBA_OK) return st;
+    if (cand.total <= ws_bytes) {
+      lo = mid;
+      best = cand;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  *p = best;
   return MOBA_OK;
 }
 

@@ -56,7 +56,14 @@ struct Plan {
   size_t off_part_o, off_part_lse, off_kimg, off_vimg, off_mu3, off_lohi, total;
 };
 
-// Validate `s` and fill `p`.  Returns a moba_status code.
-int make_plan(const Shape& s, Plan* p);
+// Validate `s` and fill `p`.  max_chunk_blocks > 0 caps the query blocks per
+// chunk (0: the default, partials of one chunk within kPartialCapBytes).
+// Returns a moba_status code.
+int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks = 0);
+
+// The plan with the largest query chunk whose workspace fits in ws_bytes
+// (the default plan when it fits).  MOBA_ERR_WORKSPACE when even one query
+// block per chunk does not fit.
+int plan_for_workspace(const Shape& s, size_t ws_bytes, Plan* p);
 
 }  // namespace moba

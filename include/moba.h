@@ -58,7 +58,7 @@ enum moba_status {
   MOBA_ERR_SEQ_NOT_DIVISIBLE = -4,  /* seqlen % block_size != 0 (no padding is defined) */
   MOBA_ERR_TOPK = -5,               /* topk < 1, or a selective topk above the supported maximum */
   MOBA_ERR_GQA = -6,                /* num_q_heads % num_kv_heads != 0 or group too large */
-  MOBA_ERR_WORKSPACE = -7,          /* workspace NULL or smaller than moba_workspace_bytes() */
+  MOBA_ERR_WORKSPACE = -7,          /* workspace NULL or smaller than the call accepts */
   MOBA_ERR_HIP = -8,                /* a HIP runtime call or kernel launch failed */
   MOBA_ERR_SHAPE = -9,              /* non-positive or overflowing sizes */
   MOBA_ERR_ALIGN = -10              /* a pointer is not 16-byte aligned */
@@ -93,13 +93,40 @@ int moba_workspace_bytes(int64_t batch, int64_t seqlen, int32_t num_q_heads,
                          size_t* bytes);
 
 /*
+ * Query chunks.  The forward processes the query positions in chunks of
+ * whole blocks; the per-(row, past block) partial results, selection rows
+ * and row lists of one chunk live in the workspace at a time.  By default a
+ * chunk is as long as keeps its partials within 8 GiB (the whole sequence up
+ * to that size).  moba_attn_fwd accepts any workspace at least as large as
+ * moba_workspace_bytes_chunked(..., max_chunk_blocks = 1, ...) and then runs
+ * with the longest chunk whose workspace fits (fewer, longer chunks are
+ * faster); the result does not depend on the chunking.
+ *
+ * moba_workspace_bytes_chunked: the workspace for chunks of at most
+ *   max_chunk_blocks query blocks (0 = the default; 1 = the smallest
+ *   workspace the forward accepts).  Pure host arithmetic.
+ * moba_plan_chunk_blocks: the query blocks per chunk the forward uses with a
+ *   workspace of workspace_bytes (MOBA_ERR_WORKSPACE if it is too small).
+ */
+int moba_workspace_bytes_chunked(int64_t batch, int64_t seqlen, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                 int32_t block_size, int32_t topk, int32_t causal,
+                                 int64_t max_chunk_blocks, size_t* bytes);
+int moba_plan_chunk_blocks(int64_t batch, int64_t seqlen, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                           int32_t block_size, int32_t topk, int32_t causal,
+                           size_t workspace_bytes, int64_t* chunk_blocks);
+
+/*
  * moba_attn_fwd: the whole MoBA prefill forward (block means, gate, top-k,
  * block-sparse attention with the own-block causal mask).
  *   q, k, v   : inputs, layouts above, same dtype.
  *   out       : output, same shape and dtype as q.
  *   sel_idx   : optional output of the chosen blocks (may be NULL).
- *   workspace : device scratch of at least moba_workspace_bytes() bytes,
- *               owned by the caller; its contents on entry do not matter.
+ *   workspace : device scratch owned by the caller, at least
+ *               moba_workspace_bytes_chunked(..., 1, ...) bytes (see "Query
+ *               chunks" above; moba_workspace_bytes() gives the fastest
+ *               plan); its contents on entry do not matter.
  * topk >= n is clamped to n (dense causal attention).  Returns a status.
  */
 int moba_attn_fwd(const void* q, const void* k, const void* v,

@@ -163,24 +163,13 @@ def key_positions(sel: Sequence[int], t: int, block_size: int, causal: bool) -> 
 # ----------------------------------------------------------------------------
 # Step 4: softmax attention over the union (report §2.2)
 # ----------------------------------------------------------------------------
-def attend(q_row: np.ndarray, k_head: np.ndarray, v_head: np.ndarray,
-           keys: np.ndarray, scale: float) -> np.ndarray:
-    """o = softmax(scale * q.K[keys]^T) V[keys], fp64, max-subtracted.
-
-    k_head, v_head: [S, D] for the row's KV head."""
-    q64 = np.asarray(q_row, dtype=np.float64)
-    logits = (np.asarray(k_head[keys], dtype=np.float64) @ q64) * scale
-    m = logits.max()
-    p = np.exp(logits - m)
-    return (p @ np.asarray(v_head[keys], dtype=np.float64)) / p.sum()
-
-
 def _attend_blocks(q64: np.ndarray, k_head: np.ndarray, v_head: np.ndarray,
                    sel: Sequence[int], t: int, B: int, causal: bool, scale: float) -> np.ndarray:
-    """Same value as `attend` over key_positions(sel, ...), but reading the
-    chosen blocks as contiguous slices (no gathered copy of K), which keeps
-    the 1M rows affordable.  Logits are laid out in the same ascending key
-    order, so the result is the same softmax."""
+    """o = softmax(scale * q.K[keys]^T) V[keys] over keys = key_positions(sel,
+    t, B, causal), fp64 with the maximum subtracted (report §2.2: softmax
+    attention over the union of the chosen blocks).  The chosen blocks are
+    read as contiguous slices in ascending key order (no gathered copy of K),
+    which keeps the 1M rows affordable."""
     j = t // B
     logit_parts, v_parts = [], []
     for i in sorted(sel):
@@ -392,9 +381,11 @@ def decode_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, lens: S
 
 
 class RowResult:
-    """Per-row oracle results: out [R, D], sel [R, topk] (-1 padded) and, for
-    the gate check, the fp64 gap between the last chosen and the first
-    unchosen past score and an upper bound on the fp32 error of one score."""
+    """Per-row oracle results: out [R, D], sel [R, topk] (-1 padded); for the
+    gate check, the fp64 gap between the last chosen and the first unchosen
+    candidate score and those two scores (`boundary`); and `score_eps`, a
+    worst-case bound on the error of any one of the row's scores when it is
+    formed in fp32 in any order (score_error_bound)."""
 
     def __init__(self, R: int, D: int, topk: int):
         self.out = np.zeros((R, D), dtype=np.float64)
@@ -470,17 +461,34 @@ def moba_rows(q, k, v, block_size: int, topk: int, causal: bool,
     return res
 
 
-def near_tie_rows(res: "RowResult", rel: float = 1e-4) -> np.ndarray:
+def near_tie_rows(res: "RowResult", rel: float = 1e-4,
+                  abs_tol: Optional[np.ndarray] = None) -> np.ndarray:
     """Rows whose gate decision is a near tie: the fp64 gap between the last
-    chosen and the first unchosen past score is at most `rel` times their
-    magnitude, or at most twice the fp32 error bound of a score."""
-    mag = np.max(np.abs(res.boundary), axis=1)
-    return (res.gap <= rel * mag) | (res.gap <= 2.0 * res.score_eps)
+    chosen and the first unchosen candidate score is at most `rel` times the
+    larger of their magnitudes (the parity rule for the gate: selections must
+    agree exactly except at such gaps; two exactly zero scores count too).  `abs_tol` (per row), if given, also
+    counts gaps at or below it."""
+    tie = res.gap <= rel * near_tie_scale(res)
+    if abs_tol is not None:
+        tie = tie | (res.gap <= np.asarray(abs_tol, dtype=np.float64))
+    return tie
+
+
+def near_tie_scale(res: "RowResult") -> np.ndarray:
+    """Per row, the larger magnitude of the two boundary scores (the last
+    chosen and the first unchosen), the scale of the relative gap."""
+    return np.max(np.abs(res.boundary), axis=1)
 
 
 # ----------------------------------------------------------------------------
 # Near-tie protocol (test infrastructure for comparing an fp32 gate)
 # ----------------------------------------------------------------------------
+# The GPU ranks fp32 scores and this oracle ranks exact (fp64) ones.  The gate
+# check therefore forgives a differing selection only where the fp64 gap at
+# the top-k boundary is below 1e-4 of the scores' magnitude (near_tie_rows);
+# the bounds below state how far an fp32 score can be from the exact one at
+# worst, whatever the summation order (Higham, "Accuracy and Stability of
+# Numerical Algorithms", section 3.1: gamma_n bounds n successive roundings).
 def _gamma(n: int, u: float = 2.0 ** -24) -> float:
     """Higham's gamma_n = n u / (1 - n u) for fp32 unit roundoff u."""
     return n * u / (1.0 - n * u)
@@ -508,17 +516,17 @@ def score_error_bound_minmax(q64: np.ndarray, lo_head: np.ndarray, hi_head: np.n
     return float(np.max(_gamma(2 * D + 1) * mag))
 
 
-def valid_topk_set(scores: np.ndarray, chosen_past: Iterable[int], j: int, m: int, eps: float) -> bool:
-    """Whether `chosen_past` is a top-m set of the past scores up to 2*eps:
-    it has m distinct past blocks and no unchosen past block beats any chosen
-    one by more than 2*eps."""
+def valid_topk_set(scores: np.ndarray, chosen_past: Iterable[int], j: int, m: int, tol: float) -> bool:
+    """Whether `chosen_past` is a top-m set of the candidate scores 0..j-1 up
+    to `tol`: it has m distinct candidates and no unchosen candidate beats any
+    chosen one by more than `tol`."""
     chosen = sorted(set(int(i) for i in chosen_past))
     if len(chosen) != m or any(i < 0 or i >= j for i in chosen):
         return False
     rest = [i for i in range(j) if i not in set(chosen)]
     if not rest or not chosen:
         return True
-    return max(scores[i] for i in rest) <= min(scores[i] for i in chosen) + 2.0 * eps
+    return max(scores[i] for i in rest) <= min(scores[i] for i in chosen) + tol
 
 
 def count_selected_keys(seqlen: int, block_size: int, topk: int, causal: bool) -> int:

@@ -196,3 +196,96 @@ def test_decode_entry_points_reject_bad_arguments():
     assert L.moba_decode_means(None, FAKE, 2, 4096, 2, 128, BF16, 128, FAKE, None) == NULL
     assert L.moba_decode_means(FAKE, FAKE, 2, 4000, 2, 128, BF16, 128, FAKE, None) == SEQ
     assert L.moba_decode_means(FAKE, FAKE, 2, 4096, 2, 128, BF16, 128, FAKE + 4, None) == ALIGN
+
+
+def ws_chunked(max_chunk, b=1, S=1 << 20, Hq=32, Hkv=8, D=128, dt=BF16, B=4096, k=12, causal=1):
+    out = ctypes.c_size_t(0)
+    st = _lib.lib.moba_workspace_bytes_chunked(b, S, Hq, Hkv, D, dt, B, k, causal, max_chunk, ctypes.byref(out))
+    return st, out.value
+
+
+def chunk_for(wsb, b=1, S=1 << 20, Hq=32, Hkv=8, D=128, dt=BF16, B=4096, k=12, causal=1):
+    out = ctypes.c_int64(0)
+    st = _lib.lib.moba_plan_chunk_blocks(b, S, Hq, Hkv, D, dt, B, k, causal, wsb, ctypes.byref(out))
+    return st, out.value
+
+
+def test_query_chunks_follow_the_workspace():
+    """The forward runs with the longest query chunk whose workspace fits:
+    the default workspace gives the default chunk (1M tokens, 32/8 heads,
+    block 4096, top-12: 22 blocks, partials within 8 GiB), the smallest one
+    chunks of one block, sizes in between the largest chunk that fits."""
+    st, full = ws_chunked(0)
+    assert st == OK and full == ws(S=1 << 20, Hq=32, Hkv=8, B=4096, k=12)[1]
+    assert chunk_for(full) == (OK, 22)
+    st, one = ws_chunked(1)
+    assert st == OK and one < full
+    assert chunk_for(one) == (OK, 1)
+    assert chunk_for(one - 1)[0] == WS
+    sizes = [ws_chunked(c)[1] for c in (1, 2, 5, 11, 22)]
+    assert sizes == sorted(sizes)
+    for c in (2, 5, 11):
+        st, n = ws_chunked(c)
+        assert chunk_for(n) == (OK, c)
+        assert chunk_for(n - 1)[1] < c
+    # capped at the default; negative caps are invalid
+    assert ws_chunked(1000)[1] == full
+    assert ws_chunked(-1)[0] == SHAPE
+    # a small workload: the default is one chunk of all 8 blocks
+    st, n = ws_chunked(0, S=1024, Hq=4, Hkv=2, B=128, k=3)
+    assert chunk_for(n, S=1024, Hq=4, Hkv=2, B=128, k=3) == (OK, 8)
+
+
+def test_forward_accepts_a_workspace_down_to_one_block_per_chunk():
+    st, one = ws_chunked(1, S=1024, Hq=4, Hkv=2, B=128, k=3)
+    assert st == OK
+    assert call_fwd(wsb=one - 1) == WS
+
+
+def bws(b=1, S=1024, Hq=4, Hkv=2, D=128, dt=BF16, B=128, k=3, causal=1):
+    out = ctypes.c_size_t(0)
+    st = _lib.lib.moba_bwd_workspace_bytes(b, S, Hq, Hkv, D, dt, B, k, causal, ctypes.byref(out))
+    return st, out.value
+
+
+def test_backward_rejects_list_entries_beyond_int32():
+    """The backward's whole-sequence dk/dv lists hold one int32 entry per (row,
+    past block) pair: 8M positions x 8 heads x 32 past blocks = 2^31 entries
+    is refused, one past block fewer is accepted (the forward accepts both:
+    it chunks its lists)."""
+    big = dict(S=8 << 20, Hq=8, Hkv=8, B=1024)
+    assert bws(**big, k=33)[0] == SHAPE
+    assert ws(**big, k=33)[0] == OK
+    assert bws(**big, k=32)[0] == OK
+    assert bws(dt=F32)[0] == DTYPE
+    assert bws(B=96, S=960)[0] == SHAPE
+
+
+def test_binding_checks_shapes_before_calling():
+    """Mismatched tensors never reach the C ABI (it derives every extent from
+    q): the binding raises ValueError naming the tensor."""
+    q = torch.zeros(1, 256, 4, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 256, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="k must have shape"):
+        M.moba_attn_fwd(q, torch.zeros(1, 128, 2, 128, dtype=torch.bfloat16), k, 128, 3)
+    with pytest.raises(ValueError, match="v must have shape"):
+        M.moba_attn_fwd(q, k, torch.zeros(1, 256, 2, 64, dtype=torch.bfloat16), 128, 3)
+    with pytest.raises(ValueError, match="k must be"):
+        M.moba_attn_fwd(q, k.float(), k, 128, 3)
+    with pytest.raises(ValueError, match="multiple of num_kv_heads"):
+        M.moba_attn_fwd(q, torch.zeros(1, 256, 3, 128, dtype=torch.bfloat16),
+                        torch.zeros(1, 256, 3, 128, dtype=torch.bfloat16), 128, 3)
+    with pytest.raises(ValueError, match="mu must have shape"):
+        M.moba_gate(q, torch.zeros(1, 2, 4, 128), 128, 3)
+    with pytest.raises(ValueError, match="mu must be"):
+        M.moba_gate(q, torch.zeros(1, 2, 2, 128, dtype=torch.float64), 128, 3)
+    with pytest.raises(ValueError, match="mu must have shape"):
+        M.moba_meanpool(k, 128, mu=torch.zeros(1, 2, 3, 128))
+    with pytest.raises(ValueError, match="lohi must have shape"):
+        M.moba_minmaxpool(k, 128, lohi=torch.zeros(1, 2, 2, 128))
+    with pytest.raises(ValueError, match="lse must be"):
+        _lib._check_like(torch.zeros(1, 4, 256, dtype=torch.float64), "lse", (1, 4, 256), torch.float32,
+                         torch.device("cpu"))
+    with pytest.raises(ValueError, match="sel_idx must have shape"):
+        _lib._check_like(torch.zeros(1, 4, 256, 2, dtype=torch.int32), "sel_idx", (1, 4, 256, 3), torch.int32,
+                         torch.device("cpu"))

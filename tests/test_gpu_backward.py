@@ -2,9 +2,11 @@
 through the C ABI) against the fp64 oracle's moba_backward, run with the
 GPU's own selection (selection parity is the forward's test).
 
-Tolerance, per gradient tensor: max |gpu - oracle| <= 0.02 max|oracle| + 0.01.
-The bf16 path rounds P and dS to bf16 for the MFMAs (relative 2^-9 each),
-accumulates in fp32 and rounds each gradient to bf16 once (2^-9 relative)."""
+Tolerance, element by element: |gpu - oracle| <= 2^-7 |oracle| + 0.015
+max|oracle| (per gradient tensor).  The bf16 path rounds P and dS to bf16 for
+the MFMAs (relative 2^-9 each, errors that add up over the keys or rows of a
+sum and so scale with the tensor's largest values), accumulates in fp32 and
+rounds each gradient to bf16 once (2^-9 of the element)."""
 import sys
 
 import numpy as np
@@ -37,10 +39,13 @@ def dout_for(w, device):
 
 
 def check(name, got, ref):
-    err = float(np.abs(got.astype(np.float64) - ref).max())
+    diff = np.abs(got.astype(np.float64) - ref)
     scale = float(np.abs(ref).max())
-    say(f"[grad] {name}: max err {err:.3e}, max |ref| {scale:.3e}")
-    assert err <= 0.02 * scale + 0.01, (name, err, scale)
+    allowed = 2.0 ** -7 * np.abs(ref) + 0.015 * scale
+    worst = float((diff / np.maximum(allowed, 1e-300)).max())
+    say(f"[grad] {name}: max err {float(diff.max()):.3e} ({float(diff.max()) / max(scale, 1e-300):.2%} of "
+        f"max |ref| {scale:.3e}), worst error / allowed {worst:.2f}")
+    assert scale > 0 and np.all(diff <= allowed), (name, float(diff.max()), scale)
 
 
 def run(w):

@@ -315,16 +315,77 @@ def test_workload_mha32_32k_needle_sampled():
     assert rep.rows >= 32 * 200
 
 
+def chunk_edges(w: W.Workload, workspace_bytes=None):
+    """First and last position of every query chunk the forward runs with the
+    default workspace (or one of workspace_bytes)."""
+    dt = M.DTYPE_BF16 if w.dtype == "bf16" else M.DTYPE_F32
+    if workspace_bytes is None:
+        workspace_bytes = M.workspace_bytes(w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, dt,
+                                            w.block_size, w.topk, w.causal)
+    cb = M.plan_chunk_blocks(w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, dt, w.block_size,
+                             w.topk, w.causal, workspace_bytes)
+    step = cb * w.block_size
+    edges = []
+    for t0 in range(0, w.seqlen, step):
+        edges += [t0, min(t0 + step, w.seqlen) - 1]
+    return cb, edges
+
+
 @pytest.mark.slow
 def test_workload_gqa32x8_128k_sampled():
+    """128K positions at 256 seeded rows per head, with the first and last
+    position of each query chunk (two chunks: 22 + 10 blocks)."""
     w = W.WORKLOADS["gqa32x8_128k"]
-    run(w, rows=W.sample_rows(w, 24, seed=23), device_inputs=True)
+    cb, edges = chunk_edges(w)
+    say(f"[chunks] {cb} blocks per chunk, edges {edges}")
+    rep, _ = run(w, rows=W.sample_rows(w, 256, seed=23, extra_positions=edges), device_inputs=True)
+    assert rep.rows >= 32 * 256
 
 
 @pytest.mark.slow
 def test_workload_gqa32x8_1m_sampled():
+    """1M positions at 256 seeded rows per head, with the first and last
+    position of each of the twelve query chunks."""
     w = W.WORKLOADS["gqa32x8_1m"]
-    run(w, rows=W.sample_rows(w, 8, seed=24), device_inputs=True)
+    cb, edges = chunk_edges(w)
+    say(f"[chunks] {cb} blocks per chunk, edges {edges}")
+    assert len(edges) == 24
+    rep, _ = run(w, rows=W.sample_rows(w, 256, seed=24, extra_positions=edges), device_inputs=True)
+    assert rep.rows >= 32 * 256
+
+
+CHUNKED = [
+    # slice-image path (384-row tiles) in four chunks of 8 blocks
+    (small("chunks_images", "bf16", 1, 16384, 8, 1, 128, 512, 3, seed=61), 8),
+    # direct K/V path over ragged 96-key blocks in six chunks of 7 (+ 5) blocks
+    (small("chunks_b96", "bf16", 1, 3840, 4, 2, 128, 96, 4, seed=62), 7),
+    # fp32 path in three chunks
+    (small("chunks_f32", "f32", 1, 1024, 2, 1, 64, 64, 5, seed=63), 6),
+]
+
+
+@pytest.mark.parametrize("w,cap", CHUNKED, ids=[c[0].name for c in CHUNKED])
+def test_forward_small_workspace_runs_in_query_chunks(w, cap):
+    """A workspace smaller than the default makes the forward run in more
+    query chunks (the longest that fit); every row is compared with the
+    oracle, across every chunk boundary."""
+    dt = M.DTYPE_BF16 if w.dtype == "bf16" else M.DTYPE_F32
+    nbytes = M.workspace_bytes(w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, dt, w.block_size,
+                               w.topk, w.causal, max_chunk_blocks=cap)
+    cb, edges = chunk_edges(w, nbytes)
+    assert cb == cap and len(edges) >= 6
+    say(f"[case] {w}: {cb} blocks per chunk, {len(edges) // 2} chunks")
+    q, k, v, _ = W.make_inputs(w, device=DEV)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    out, sel = M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal, workspace=ws)
+    torch.cuda.synchronize()
+    rep = compare(q, k, v, out, sel, w.block_size, w.topk, w.causal, tol=TOL[w.dtype])
+    say(f"[parity] {w.name}: {rep.as_dict()}")
+    # the same selection as with the default workspace (one chunk here)
+    out1, sel1 = M.moba_attn_fwd(q, k, v, w.block_size, w.topk, w.causal)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel1)
+    assert (out.float() - out1.float()).abs().max().item() <= 2 * TOL[w.dtype]
 
 
 @pytest.mark.parametrize("n", [8, 128])

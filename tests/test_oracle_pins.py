@@ -333,29 +333,203 @@ def test_block_means_definition():
 
 
 # ----------------------------------------------------------------------------
-# near-tie protocol
+# near-tie protocol: the relative-gap rule, and the fp32 score error bounds
 # ----------------------------------------------------------------------------
-def test_near_tie_detection_and_valid_set():
-    b, S, Hq, Hkv, D, B = 1, 64, 1, 1, 4, 16
+def _tie_case(delta):
+    """One query row (t = 63, B = 16, topk = 2: one past slot among blocks
+    0..2) whose block 1 mean is block 0's scaled by (1 + delta), with block 2
+    far below both: the top-1 boundary lies between blocks 1 and 0 and their
+    fp64 gap is delta / (1 + delta) of the larger score."""
     rng = np.random.default_rng(14)
-    q, k, v = rand_qkv(rng, b, S, Hq, Hkv, D)
-    # make blocks 0 and 1 means nearly equal: differ by 1e-9 relative
-    k[0, 16:32] = k[0, 0:16] * (1 + 1e-9)
+    q, k, v = rand_qkv(rng, 1, 64, 1, 1, 8)
     t = 63
-    res = O.moba_rows(q, k, v, B, 2, True, [(0, t, 0)], keep_scores=True)
-    s = res.scores[0]
-    if abs(s[0] - s[1]) < abs(s[2] - max(s[0], s[1])) and max(s[0], s[1]) > s[2]:
-        assert O.near_tie_rows(res)[0]
-    # a clear separation is not a near tie
-    k2 = k.copy()
-    k2[0, 16:32] += 3.0 * np.sign(q[0, t, 0])
-    res2 = O.moba_rows(q, k2, v, B, 2, True, [(0, t, 0)], keep_scores=True)
+    qd = q[0, t, 0] / np.linalg.norm(q[0, t, 0])
+    k[0, 0:16, 0] = rng.standard_normal((16, 8)) + 2.0 * qd  # block 0 scores well above 0
+    k[0, 16:32] = k[0, 0:16] * (1.0 + delta)
+    k[0, 32:48, 0] = k[0, 0:16, 0] - 6.0 * qd
+    return O.moba_rows(q, k, v, 16, 2, True, [(0, t, 0)], keep_scores=True)
+
+
+def test_near_tie_rule_is_the_relative_gap():
+    # an almost exact tie, gap 1e-9 relative: a near tie
+    res = _tie_case(1e-9)
+    assert res.sel[0].tolist()[:1] == [1] and O.near_tie_rows(res)[0]
+    # just inside and just outside 1e-4 relative
+    assert O.near_tie_rows(_tie_case(0.9e-4))[0]
+    assert not O.near_tie_rows(_tie_case(1.2e-4))[0]
+    # a clear separation is not a near tie; the valid-set check uses the
+    # relative tolerance on the candidates' scores
+    res2 = _tie_case(0.5)
     assert not O.near_tie_rows(res2)[0]
     s2 = res2.scores[0]
-    best = int(np.argmax(s2[:3]))
-    assert O.valid_topk_set(s2, [best], 3, 1, res2.score_eps[0])
-    worst = int(np.argmin(s2[:3]))
-    assert not O.valid_topk_set(s2, [worst], 3, 1, res2.score_eps[0])
+    tol = 1e-4 * O.near_tie_scale(res2)[0]
+    assert O.valid_topk_set(s2, [1], 3, 1, tol)
+    assert not O.valid_topk_set(s2, [0], 3, 1, tol)
+    assert not O.valid_topk_set(s2, [2], 3, 1, tol)
+    # at the near tie either of the two tied blocks is a valid choice
+    res3 = _tie_case(1e-9)
+    tol3 = 1e-4 * O.near_tie_scale(res3)[0]
+    assert O.valid_topk_set(res3.scores[0], [0], 3, 1, tol3)
+    assert O.valid_topk_set(res3.scores[0], [1], 3, 1, tol3)
+    assert not O.valid_topk_set(res3.scores[0], [2], 3, 1, tol3)
+
+
+F32 = np.float32
+
+
+def _fp32_sum(x, order, groups=4):
+    """Sum the rows of x [n, ...] in fp32, rounding after every addition, in
+    the given order: sequential, reverse, pairwise (recursive halves), or
+    `groups` interleaved partial sums (rows r, r + groups, ...) added at the
+    end."""
+    x = np.asarray(x, dtype=F32)
+
+    def seq(rows):
+        acc = rows[0].copy()
+        for row in rows[1:]:
+            acc = (acc + row).astype(F32)
+        return acc
+
+    def pw(rows):
+        if len(rows) == 1:
+            return rows[0].copy()
+        h = len(rows) // 2
+        return (pw(rows[:h]) + pw(rows[h:])).astype(F32)
+
+    if order == "sequential":
+        return seq(x)
+    if order == "reverse":
+        return seq(x[::-1])
+    if order == "pairwise":
+        return pw(x)
+    if order == "interleaved":
+        g = min(groups, len(x))
+        return seq(np.stack([seq(x[r::g]) for r in range(g)]))
+    raise ValueError(order)
+
+
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+ORDERS = ("sequential", "reverse", "pairwise", "interleaved")
+
+
+def _fp32_mean_gate_scores(q, kb, mean_order, dot_order, split):
+    """fp32 emulation of one row's gate scores: the block means summed in fp32
+    in `mean_order` and divided by B in fp32, then q . mu in fp32 in
+    `dot_order`, either from fp32-rounded products (fp32 inputs) or with each
+    mean split exactly into three bf16 parts (q in bf16, exact products).
+    q: [D]; kb: [n, B, D] fp32 values.  Returns [n]."""
+    n, B, D = kb.shape
+    mu = np.stack([(_fp32_sum(kb[i], mean_order) / F32(B)).astype(F32) for i in range(n)])  # [n, D]
+    if split:
+        hi = _bf16(mu)
+        mid = _bf16((mu - hi).astype(F32))
+        lo = _bf16((mu - hi - mid).astype(F32))
+        assert np.array_equal((hi.astype(np.float64) + mid + lo), mu.astype(np.float64))
+        terms = np.concatenate([q * hi, q * mid, q * lo], axis=1).astype(F32)  # exact products
+    else:
+        terms = (q.astype(F32) * mu).astype(F32)
+    return _fp32_sum(terms.T, dot_order)
+
+
+def _mean_bound_worst_ratio():
+    """Largest |emulated fp32 score - exact score| / score_error_bound over
+    random inputs (bf16 and fp32, several B) and inputs built to make every
+    fp32 addition lose half an ulp, in every summation order."""
+    u = 2.0 ** -24
+    worst = 0.0
+    cases = []
+    rng = np.random.default_rng(40)
+    for B, D, split in ((16, 128, True), (256, 128, True), (4096, 128, True), (128, 64, False), (64, 128, False)):
+        kb = rng.standard_normal((3, B, D)).astype(F32)
+        q = rng.standard_normal(D).astype(F32)
+        if split:
+            kb, q = _bf16(kb), _bf16(q)
+        cases.append((q, kb, split))
+    # adversarial mean: one coordinate holds [1, u, u, ...]; 1 + u rounds back
+    # to 1 at every step of a sequential sum
+    B = 4096
+    kb = np.zeros((1, B, 128), dtype=F32)
+    kb[0, 0, 0] = 1.0
+    kb[0, 1:, 0] = u
+    q = np.zeros(128, dtype=F32)
+    q[0] = 1.0
+    cases.append((q, kb, True))
+    # adversarial dot product: mean [1, u, ..., u] (every key equal to it),
+    # q all ones: the products 1, u, u, ... lose every u
+    B = 16
+    kb = np.zeros((1, B, 128), dtype=F32)
+    kb[0, :, 0] = 1.0
+    kb[0, :, 1:] = u
+    cases.append((np.ones(128, dtype=F32), kb, True))
+    for q, kb, split in cases:
+        n, B, D = kb.shape
+        q64 = q.astype(np.float64)
+        k64 = kb.astype(np.float64)
+        mu64 = k64.mean(axis=1)
+        exact = mu64 @ q64
+        bound = O.score_error_bound(q64, mu64, np.abs(k64).mean(axis=1), B)
+        for mo in ORDERS:
+            for do in ORDERS:
+                got = _fp32_mean_gate_scores(q, kb, mo, do, split).astype(np.float64)
+                worst = max(worst, float(np.max(np.abs(got - exact))) / bound)
+    return worst
+
+
+def _minmax_bound_worst_ratio():
+    """The same for the min/max gate: the score sum_d max(q_d lo_d, q_d hi_d)
+    formed in fp32 as the larger of two rounded products per d (fp32 inputs)
+    or as the 2 D exact products q+ . hi + q- . lo (bf16 inputs), summed in
+    every order."""
+    u = 2.0 ** -24
+    rng = np.random.default_rng(41)
+    cases = []
+    for D, split in ((128, True), (64, False)):
+        kb = rng.standard_normal((3, 64, D)).astype(F32)
+        q = rng.standard_normal(D).astype(F32)
+        if split:
+            kb, q = _bf16(kb), _bf16(q)
+        cases.append((q, kb.min(axis=1), kb.max(axis=1), split))
+    hi = np.full((1, 128), u, dtype=F32)
+    hi[0, 0] = 1.0
+    cases.append((np.ones(128, dtype=F32), hi.copy(), hi, True))
+    worst = 0.0
+    for q, lo, hi, split in cases:
+        q64 = q.astype(np.float64)
+        exact = np.maximum(lo.astype(np.float64) * q64, hi.astype(np.float64) * q64).sum(axis=1)
+        bound = O.score_error_bound_minmax(q64, lo.astype(np.float64), hi.astype(np.float64))
+        if split:
+            qp, qm = np.maximum(q, F32(0)), np.minimum(q, F32(0))
+            terms = np.concatenate([qp * hi, qm * lo], axis=1).astype(F32)
+        else:
+            terms = np.maximum((q * lo).astype(F32), (q * hi).astype(F32))
+        for o in ORDERS:
+            got = _fp32_sum(terms.T, o).astype(np.float64)
+            worst = max(worst, float(np.max(np.abs(got - exact))) / bound)
+    return worst
+
+
+def test_score_error_bound_holds_and_is_attained():
+    """The worst-case fp32 error bound of a mean-gate score holds for every
+    summation order, and inputs built so that each addition loses half an ulp
+    reach more than a tenth of it (so a bound ten times too small fails)."""
+    r = _mean_bound_worst_ratio()
+    assert 0.1 < r <= 1.0, r
+
+
+def test_score_error_bound_minmax_holds_and_is_attained():
+    r = _minmax_bound_worst_ratio()
+    assert 0.1 < r <= 1.0, r
+
+
+def test_planted_small_error_bounds_are_caught(monkeypatch):
+    """Both bounds planted ten times too small: the emulated errors exceed them."""
+    gamma = O._gamma
+    monkeypatch.setattr(O, "_gamma", lambda n, u=2.0 ** -24: 0.1 * gamma(n, u))
+    assert _mean_bound_worst_ratio() > 1.0
+    assert _minmax_bound_worst_ratio() > 1.0
 
 
 # ----------------------------------------------------------------------------
