@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     moba_meanpool,
     moba_minmaxpool,
     plan_chunk_blocks,
+    plan_info,
     profile_enable,
     profile_read,
     STAGES,

@@ -30,8 +30,8 @@ SIGNATURES = {
                                             _c_i32, ctypes.POINTER(_c_sz)]),
     "moba_workspace_bytes_chunked": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                                     _c_i32, _c_i32, _c_i64, ctypes.POINTER(_c_sz)]),
-    "moba_plan_chunk_blocks": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
-                                              _c_i32, _c_sz, ctypes.POINTER(_c_i64)]),
+    "moba_plan_info": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_sz,
+                                      ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
     "moba_attn_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "moba_attn_fwd_gate": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -162,15 +162,23 @@ def workspace_bytes(batch: int, seqlen: int, num_q_heads: int, num_kv_heads: int
     return int(out.value)
 
 
-def plan_chunk_blocks(batch: int, seqlen: int, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int,
-                      block_size: int, topk: int, causal: bool, workspace_bytes_: int) -> int:
-    """Query blocks per chunk the forward runs with a workspace of that size."""
-    out = _c_i64(0)
-    st = lib.moba_plan_chunk_blocks(batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
-                                    int(bool(causal)), int(workspace_bytes_), ctypes.byref(out))
+def plan_info(batch: int, seqlen: int, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int,
+              block_size: int, topk: int, causal: bool, workspace_bytes_: int) -> dict:
+    """The forward's plan with a workspace of that size: query blocks per
+    chunk, rows per past-block tile, whether K/V slice images are built."""
+    cb, tr, img = _c_i64(0), _c_i32(0), _c_i32(0)
+    st = lib.moba_plan_info(batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
+                            int(bool(causal)), int(workspace_bytes_), ctypes.byref(cb), ctypes.byref(tr),
+                            ctypes.byref(img))
     if st != MOBA_OK:
-        raise MobaError(st, "moba_plan_chunk_blocks")
-    return int(out.value)
+        raise MobaError(st, "moba_plan_info")
+    return {"chunk_blocks": int(cb.value), "tile_rows": int(tr.value), "slice_images": bool(img.value)}
+
+
+def plan_chunk_blocks(*args) -> int:
+    """Query blocks per chunk the forward runs with a workspace of that size
+    (same arguments as plan_info)."""
+    return plan_info(*args)["chunk_blocks"]
 
 
 def _workspace(workspace: Optional[torch.Tensor], nbytes, device: torch.device) -> torch.Tensor:

@@ -925,6 +925,8 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
 
 int launch_attn_past(const PastArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.max_tiles);
+  // the 384-row tiles read K and V only from the slice images
+  if (a.tile_rows == 384 && (!a.kimg || !a.vimg || a.block % KT != 0)) return -1;
   if (a.tile_rows == 256) {
     // 8 waves, one work-group per CU; from the slice images the loads run two
     // slices ahead, otherwise one (any block size)

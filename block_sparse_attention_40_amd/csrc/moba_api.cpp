@@ -249,24 +249,27 @@ int moba_workspace_bytes_chunked(int64_t batch, int64_t seqlen, int32_t num_q_he
                                  int64_t max_chunk_blocks, size_t* bytes) {
   if (!bytes) return MOBA_ERR_NULL;
   Plan p;
+  // one block per chunk: the smallest plan, without the K/V slice images
   const int st = make_plan(Shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk,
                                  causal ? 1 : 0},
-                           &p, max_chunk_blocks);
+                           &p, max_chunk_blocks, max_chunk_blocks != 1);
   if (st != MOBA_OK) return st;
   *bytes = p.total;
   return MOBA_OK;
 }
 
-int moba_plan_chunk_blocks(int64_t batch, int64_t seqlen, int32_t num_q_heads, int32_t num_kv_heads,
-                           int32_t head_dim, int32_t dtype, int32_t block_size, int32_t topk, int32_t causal,
-                           size_t workspace_bytes, int64_t* chunk_blocks) {
-  if (!chunk_blocks) return MOBA_ERR_NULL;
+int moba_plan_info(int64_t batch, int64_t seqlen, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t dtype, int32_t block_size, int32_t topk, int32_t causal, size_t workspace_bytes,
+                   int64_t* chunk_blocks, int32_t* tile_rows, int32_t* slice_images) {
+  if (!chunk_blocks || !tile_rows || !slice_images) return MOBA_ERR_NULL;
   Plan p;
   const int st = plan_for_workspace(Shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size,
                                           topk, causal ? 1 : 0},
                                     workspace_bytes, &p);
   if (st != MOBA_OK) return st;
   *chunk_blocks = p.chunk_blocks;
+  *tile_rows = p.tile_rows;
+  *slice_images = p.kv_image ? 1 : 0;
   return MOBA_OK;
 }
 

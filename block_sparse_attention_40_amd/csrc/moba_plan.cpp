@@ -9,7 +9,7 @@ namespace moba {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks) {
+int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks, bool allow_image) {
   if (!p) return MOBA_ERR_NULL;
   if (s.dtype != MOBA_DTYPE_F32 && s.dtype != MOBA_DTYPE_BF16) return MOBA_ERR_DTYPE;
   if (s.batch < 1 || s.seqlen < 1 || s.hq < 1 || s.hkv < 1 || s.block < 1 || s.d < 1)
@@ -61,7 +61,7 @@ int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks) {
   // long lists: 384-row tiles over the K/V slice images (bf16, whole slices),
   // else 256; short lists: 128
   q.tile_rows = (q.max_pairs / lists >= kLargeTileMinRows) ? kTileRowsLarge : kTileRowsSmall;
-  if (q.tile_rows == kTileRowsLarge && s.dtype == MOBA_DTYPE_BF16 && s.block % kSliceKeys == 0)
+  if (allow_image && q.tile_rows == kTileRowsLarge && s.dtype == MOBA_DTYPE_BF16 && s.block % kSliceKeys == 0)
     q.tile_rows = kTileRowsImage;
   q.max_tiles = (q.max_pairs + q.tile_rows - 1) / q.tile_rows + lists;
   q.max_tiles = (q.max_tiles + 7) / 8 * 8;
@@ -81,7 +81,7 @@ int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks) {
   // [batch, hkv, seqlen / 64, 64 x 128] bf16 each, as large as K and V
   // (and for the own-block kernel alone when no past block is chosen and the
   // blocks are long, e.g. block_size = seqlen: dense causal attention)
-  q.kv_image = s.dtype == MOBA_DTYPE_BF16 && s.block % kSliceKeys == 0 &&
+  q.kv_image = allow_image && s.dtype == MOBA_DTYPE_BF16 && s.block % kSliceKeys == 0 &&
                (q.kp > 0 ? q.tile_rows == kTileRowsImage : s.block >= kOwnImageMinBlock);
   const size_t img = q.kv_image ? (size_t)s.batch * s.hkv * s.seqlen * s.d * sizeof(uint16_t) : 0;
   q.off_kimg = take(img);
@@ -98,34 +98,41 @@ int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks) {
   return MOBA_OK;
 }
 
-int plan_for_workspace(const Shape& s, size_t ws_bytes, Plan* p) {
-  Plan best{};
-  int st = make_plan(s, &best);
-  if (st != MOBA_OK) return st;
-  if (best.total <= ws_bytes) {
-    *p = best;
-    return MOBA_OK;
-  }
-  // the workspace grows with the chunk: find the largest chunk that fits
-  int64_t lo = 1, hi = best.chunk_blocks - 1;
+// The largest chunk (at most the default one) whose workspace fits, or 0.
+static int64_t largest_fitting_chunk(const Shape& s, size_t ws_bytes, int64_t hi, bool allow_image, Plan* best) {
   Plan cand{};
-  st = make_plan(s, &cand, 1);
-  if (st != MOBA_OK) return st;
-  if (cand.total > ws_bytes) return MOBA_ERR_WORKSPACE;
-  best = cand;
+  if (make_plan(s, &cand, 1, allow_image) != MOBA_OK || cand.total > ws_bytes) return 0;
+  *best = cand;
+  int64_t lo = 1;
   while (lo < hi) {
     const int64_t mid = lo + (hi - lo + 1) / 2;
-    st = make_plan(s, &cand, mid);
-    if (st != MOBA_OK) return st;
-    if (cand.total <= ws_bytes) {
+    if (make_plan(s, &cand, mid, allow_image) == MOBA_OK && cand.total <= ws_bytes) {
       lo = mid;
-      best = cand;
+      *best = cand;
     } else {
       hi = mid - 1;
     }
   }
-  *p = best;
-  return MOBA_OK;
+  return lo;
+}
+
+int plan_for_workspace(const Shape& s, size_t ws_bytes, Plan* p) {
+  Plan def{};
+  const int st = make_plan(s, &def);
+  if (st != MOBA_OK) return st;
+  if (def.total <= ws_bytes) {
+    *p = def;
+    return MOBA_OK;
+  }
+  // the workspace grows with the chunk: the largest chunk that fits, with
+  // the slice images if any chunk fits with them
+  Plan best{};
+  if (largest_fitting_chunk(s, ws_bytes, def.chunk_blocks, true, &best) > 0 ||
+      largest_fitting_chunk(s, ws_bytes, def.chunk_blocks, false, &best) > 0) {
+    *p = best;
+    return MOBA_OK;
+  }
+  return MOBA_ERR_WORKSPACE;
 }
 
 }  // namespace moba

@@ -57,13 +57,15 @@ struct Plan {
 };
 
 // Validate `s` and fill `p`.  max_chunk_blocks > 0 caps the query blocks per
-// chunk (0: the default, partials of one chunk within kPartialCapBytes).
-// Returns a moba_status code.
-int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks = 0);
+// chunk (0: the default, partials of one chunk within kPartialCapBytes);
+// allow_image = false never re-lays K and V out as slice images.  Returns a
+// moba_status code.
+int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks = 0, bool allow_image = true);
 
 // The plan with the largest query chunk whose workspace fits in ws_bytes
-// (the default plan when it fits).  MOBA_ERR_WORKSPACE when even one query
-// block per chunk does not fit.
+// (the default plan when it fits); without the K/V slice images when no plan
+// with them fits.  MOBA_ERR_WORKSPACE when even one query block per chunk
+// does not fit.
 int plan_for_workspace(const Shape& s, size_t ws_bytes, Plan* p);
 
 }  // namespace moba

@@ -104,18 +104,23 @@ int moba_workspace_bytes(int64_t batch, int64_t seqlen, int32_t num_q_heads,
  *
  * moba_workspace_bytes_chunked: the workspace for chunks of at most
  *   max_chunk_blocks query blocks (0 = the default; 1 = the smallest
- *   workspace the forward accepts).  Pure host arithmetic.
- * moba_plan_chunk_blocks: the query blocks per chunk the forward uses with a
- *   workspace of workspace_bytes (MOBA_ERR_WORKSPACE if it is too small).
+ *   workspace the forward accepts: one block per chunk and K, V read as they
+ *   are, not re-laid out as slice images).  Pure host arithmetic.
+ * moba_plan_info: the plan the forward uses with a workspace of
+ *   workspace_bytes (MOBA_ERR_WORKSPACE if it is too small): *chunk_blocks
+ *   query blocks per chunk, *tile_rows rows per past-block attention tile
+ *   (128, 256, or 384 for tiles read from K/V slice images), *slice_images
+ *   1 if K and V are re-laid out as per-64-key slice images.  Host only.
  */
 int moba_workspace_bytes_chunked(int64_t batch, int64_t seqlen, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                                  int32_t block_size, int32_t topk, int32_t causal,
                                  int64_t max_chunk_blocks, size_t* bytes);
-int moba_plan_chunk_blocks(int64_t batch, int64_t seqlen, int32_t num_q_heads,
-                           int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
-                           int32_t block_size, int32_t topk, int32_t causal,
-                           size_t workspace_bytes, int64_t* chunk_blocks);
+int moba_plan_info(int64_t batch, int64_t seqlen, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                   int32_t block_size, int32_t topk, int32_t causal,
+                   size_t workspace_bytes, int64_t* chunk_blocks,
+                   int32_t* tile_rows, int32_t* slice_images);
 
 /*
  * moba_attn_fwd: the whole MoBA prefill forward (block means, gate, top-k,

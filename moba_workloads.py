@@ -126,20 +126,25 @@ def make_inputs(w: Workload, device: str = "cpu", seed: Optional[int] = None):
 
 def sample_rows(w: Workload, per_head: int, seed: int, extra_positions=()):
     """Seeded sample of query rows (batch, position, head) for checking the big
-    workloads row by row.  Always includes the first and last query, the first
-    and last query of the first block, the first query after the warm-up
-    blocks (where the gate first has to choose), plus uniform draws."""
+    workloads row by row: `per_head` distinct positions per head (or all of
+    the fixed ones, if more).  Always includes the first and last query, the
+    first and last query of the first block, the first query after the warm-up
+    blocks (where the gate first has to choose) and `extra_positions`, plus
+    uniform draws."""
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed)
     S, B, H = w.seqlen, w.block_size, w.num_q_heads
     fixed = [0, B - 1, min(B, S - 1), min((w.topk - 1) * B, S - 1), min(w.topk * B + B // 2, S - 1), S - 1]
-    fixed += [int(p) for p in extra_positions]
+    fixed = set(fixed + [int(p) for p in extra_positions])
+    want = min(S, max(per_head, len(fixed)))
     rows = []
     for b in range(w.batch):
         for h in range(H):
-            n_rand = max(0, per_head - len(fixed))
-            rnd = torch.randint(0, S, (n_rand,), generator=gen).tolist()
-            for t in sorted(set(fixed + rnd)):
+            pos = set(fixed)
+            # uniform draws until the head has `want` distinct positions
+            while len(pos) < want:
+                pos.update(torch.randint(0, S, (want - len(pos),), generator=gen).tolist())
+            for t in sorted(pos):
                 rows.append((b, t, h))
     return rows
 

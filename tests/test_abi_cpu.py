@@ -204,10 +204,16 @@ def ws_chunked(max_chunk, b=1, S=1 << 20, Hq=32, Hkv=8, D=128, dt=BF16, B=4096, 
     return st, out.value
 
 
-def chunk_for(wsb, b=1, S=1 << 20, Hq=32, Hkv=8, D=128, dt=BF16, B=4096, k=12, causal=1):
-    out = ctypes.c_int64(0)
-    st = _lib.lib.moba_plan_chunk_blocks(b, S, Hq, Hkv, D, dt, B, k, causal, wsb, ctypes.byref(out))
-    return st, out.value
+def plan_of(wsb, b=1, S=1 << 20, Hq=32, Hkv=8, D=128, dt=BF16, B=4096, k=12, causal=1):
+    cb, tr, img = ctypes.c_int64(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    st = _lib.lib.moba_plan_info(b, S, Hq, Hkv, D, dt, B, k, causal, wsb, ctypes.byref(cb), ctypes.byref(tr),
+                                 ctypes.byref(img))
+    return st, cb.value, tr.value, img.value
+
+
+def chunk_for(wsb, **kw):
+    st, cb, _, _ = plan_of(wsb, **kw)
+    return st, cb
 
 
 def test_query_chunks_follow_the_workspace():
@@ -289,3 +295,35 @@ def test_binding_checks_shapes_before_calling():
     with pytest.raises(ValueError, match="sel_idx must have shape"):
         _lib._check_like(torch.zeros(1, 4, 256, 2, dtype=torch.int32), "sel_idx", (1, 4, 256, 3), torch.int32,
                          torch.device("cpu"))
+
+
+@pytest.mark.parametrize("shape", [
+    dict(S=1 << 20, Hq=32, Hkv=8, B=4096, k=12),
+    dict(S=131072, Hq=32, Hkv=8, B=4096, k=12),
+    dict(S=32768, Hq=32, Hkv=32, B=512, k=3),
+    dict(S=16384, Hq=8, Hkv=1, B=512, k=3),
+    dict(S=3840, Hq=8, Hkv=1, B=96, k=4),
+    dict(S=8192, Hq=4, Hkv=1, B=2048, k=2),
+    dict(S=16384, Hq=8, Hkv=2, B=16384, k=1),
+    dict(S=1024, Hq=1, Hkv=1, B=128, k=3, D=64, dt=F32),
+])
+def test_every_plan_reads_images_only_when_it_builds_them(shape):
+    """Over workspaces from the smallest to the default, every plan that cuts
+    384-row past-block tiles (read from the K/V slice images) builds the
+    images, and 384-row tiles exist only with whole 64-key slices."""
+    lo = ws_chunked(1, **shape)[1]
+    hi = ws_chunked(0, **shape)[1]
+    seen = set()
+    for f in [0.0, 0.01, 0.05, 0.1, 0.25, 0.5, 0.75, 0.9, 0.99, 1.0, 1.5]:
+        wsb = int(lo + (hi - lo) * f)
+        st, cb, tr, img = plan_of(wsb, **shape)
+        assert st == OK
+        assert tr in (128, 256, 384)
+        if tr == 384:
+            assert img == 1 and shape["B"] % 64 == 0
+        seen.add((cb, tr, img))
+    assert plan_of(lo - 1, **shape)[0] == WS
+    # 128K, 32/8 heads, block 4096, top-12 in 512 MiB: one block per chunk,
+    # 256-row tiles on K and V as they are
+    if shape == dict(S=131072, Hq=32, Hkv=8, B=4096, k=12):
+        assert plan_of(512 << 20, **shape) == (OK, 1, 256, 0)

@@ -361,6 +361,9 @@ CHUNKED = [
     (small("chunks_b96", "bf16", 1, 3840, 4, 2, 128, 96, 4, seed=62), 7),
     # fp32 path in three chunks
     (small("chunks_f32", "f32", 1, 1024, 2, 1, 64, 64, 5, seed=63), 6),
+    # the smallest workspace: one block per chunk and no slice images, so the
+    # long lists take 256-row tiles on K and V as they are (whole 64-key slices)
+    (small("chunks_min_no_images", "bf16", 1, 8192, 4, 1, 128, 2048, 2, seed=64), 1),
 ]
 
 
@@ -374,6 +377,10 @@ def test_forward_small_workspace_runs_in_query_chunks(w, cap):
                                w.topk, w.causal, max_chunk_blocks=cap)
     cb, edges = chunk_edges(w, nbytes)
     assert cb == cap and len(edges) >= 6
+    if w.name == "chunks_min_no_images":
+        info = M.plan_info(w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, dt, w.block_size, w.topk,
+                           w.causal, nbytes)
+        assert info["tile_rows"] == 256 and not info["slice_images"], info
     say(f"[case] {w}: {cb} blocks per chunk, {len(edges) // 2} chunks")
     q, k, v, _ = W.make_inputs(w, device=DEV)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
