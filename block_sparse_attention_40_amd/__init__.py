@@ -19,6 +19,8 @@ from ._lib import (  # noqa: F401
     bwd_workspace_bytes,
     moba_attn_bwd,
     moba_attn_fwd,
+    moba_attn_fwd_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     moba_attn_fwd_train,
     moba_gate,
     moba_meanpool,

@@ -19,6 +19,7 @@ MOBA_OK = 0
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 MAX_SELECTIVE_TOPK = 32
+NOALLOC_SCRATCH_BYTES = 512 << 20  # MOBA_NOALLOC_SCRATCH_BYTES
 
 _c_i64, _c_i32, _c_p, _c_sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
 
@@ -34,6 +35,8 @@ SIGNATURES = {
                                       ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
     "moba_attn_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "moba_attn_fwd_noalloc": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                             _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
     "moba_attn_fwd_gate": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "moba_minmaxpool": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p]),
@@ -231,6 +234,27 @@ def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size:
         where = "moba_attn_fwd_gate"
     if st != MOBA_OK:
         raise MobaError(st, where)
+    return out, sel_idx
+
+
+def moba_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int, topk: int,
+                          causal: bool = True, out: Optional[torch.Tensor] = None,
+                          sel_idx: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """moba_attn_fwd_noalloc: the forward on the library's fixed per-GPU
+    scratch (no workspace; the C call allocates nothing).  Pass out and
+    sel_idx to allocate nothing here either."""
+    b, S, Hq, Hkv, D = _check_qkv(q, k, v)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_like(out, "out", q.shape, q.dtype, q.device)
+    if sel_idx is None:
+        sel_idx = torch.empty((b, Hq, S, topk), dtype=torch.int32, device=q.device)
+    _check_like(sel_idx, "sel_idx", (b, Hq, S, topk), torch.int32, q.device)
+    st = lib.moba_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, S, Hq, Hkv, D, dt, block_size, topk,
+                                   int(bool(causal)), out.data_ptr(), sel_idx.data_ptr(), _stream_ptr(q.device))
+    if st != MOBA_OK:
+        raise MobaError(st, "moba_attn_fwd_noalloc")
     return out, sel_idx
 
 

@@ -181,6 +181,38 @@ int make_bwd_plan(const Shape& s, BwdPlan* out) {
   return MOBA_OK;
 }
 
+// moba_attn_fwd_noalloc's fixed scratch.  In host code `scratch` names a
+// host-side stand-in, not the device array: the device address comes from
+// hipGetSymbolAddress, once per device (each GPU holds its own copy of the
+// array, at its own address, until the process ends).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[MOBA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The scratch of the current device (which `stream` must belong to).
+int scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOBA_ERR_HIP;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return MOBA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOBA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOBA_OK;
+}
+
 float scale_log2_for(int d) {
   // log2(e) / sqrt(D): the softmax scale 1/sqrt(D) folded into base-2 exponentials
   return (float)(1.4426950408889634 / std::sqrt((double)d));
@@ -445,6 +477,28 @@ int moba_attn_fwd(const void* q, const void* k, const void* v, int64_t batch, in
                   void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_impl(q, k, v, batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk, causal,
                   MOBA_GATE_MEAN, out, sel_idx, nullptr, workspace, workspace_bytes, stream);
+}
+
+int moba_attn_fwd_noalloc(const void* q, const void* k, const void* v, int64_t batch, int64_t seqlen,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                          int32_t block_size, int32_t topk, int32_t causal, void* out, int32_t* sel_idx,
+                          void* stream) {
+  // every check is host arithmetic and comes before the scratch is looked up
+  const Shape shape{batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk, causal ? 1 : 0};
+  Plan p;
+  int st = make_plan(shape, &p);
+  if (st != MOBA_OK) return st;
+  if (!q || !k || !v || !out) return MOBA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) ||
+      (sel_idx && (reinterpret_cast<uintptr_t>(sel_idx) & 3u)))
+    return MOBA_ERR_ALIGN;
+  st = plan_for_workspace(shape, MOBA_NOALLOC_SCRATCH_BYTES, &p);  // MOBA_ERR_WORKSPACE: beyond the scratch
+  if (st != MOBA_OK) return st;
+  void* ws = nullptr;
+  st = scratch_for_current_device(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (st != MOBA_OK) return st;
+  return fwd_impl(q, k, v, batch, seqlen, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk, causal,
+                  MOBA_GATE_MEAN, out, sel_idx, nullptr, ws, MOBA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int moba_attn_fwd_gate(const void* q, const void* k, const void* v, int64_t batch, int64_t seqlen,

@@ -142,6 +142,32 @@ int moba_attn_fwd(const void* q, const void* k, const void* v,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moba_attn_fwd_noalloc: moba_attn_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument, and the call
+ * allocates nothing.  Its scratch is a static device array of
+ * MOBA_NOALLOC_SCRATCH_BYTES (512 MiB) in the library, one per GPU the
+ * library runs on, held until the process ends; its address is looked up on
+ * the first call on a device.  The forward runs with the longest query chunk
+ * whose workspace fits in it (see "Query chunks"); shapes whose smallest
+ * workspace (moba_workspace_bytes_chunked(..., 1, ...)) exceeds it return
+ * MOBA_ERR_WORKSPACE (all five benchmark shapes of this library fit, up to
+ * 1M positions with 32/8 heads, block 4096, top-12).  Nothing in the scratch
+ * has to start at zero: every call writes what it reads.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.  `stream` must belong
+ * to the current device (MOBA_ERR_HIP otherwise).  Other arguments, layouts,
+ * results and errors as moba_attn_fwd (mean gate).
+ */
+#define MOBA_NOALLOC_SCRATCH_BYTES (512ull << 20)
+int moba_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                          int64_t batch, int64_t seqlen, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                          int32_t block_size, int32_t topk, int32_t causal,
+                          void* out, int32_t* sel_idx, void* stream);
+
+/*
  * Block summary and gate score (the method's gate, report 2.2, or the
  * Quest-style variant the report places in the same family, report 1.3:
  * min/max pooling of the block's keys).

@@ -297,6 +297,35 @@ def test_binding_checks_shapes_before_calling():
                          torch.device("cpu"))
 
 
+def test_noalloc_entry_point_checks_on_the_host():
+    """The fixed-scratch forward validates like moba_attn_fwd and refuses
+    shapes whose smallest workspace exceeds its scratch, all before it looks
+    the scratch up (so on a machine without a GPU nothing reaches HIP)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define MOBA_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES == M.NOALLOC_SCRATCH_BYTES
+    L = _lib.lib
+
+    def call(q=FAKE, out=FAKE, sel=None, b=1, S=1024, Hq=4, Hkv=2, D=128, dt=BF16, B=128, topk=3, causal=1):
+        return L.moba_attn_fwd_noalloc(q, FAKE, FAKE, b, S, Hq, Hkv, D, dt, B, topk, causal, out, sel, None)
+
+    assert call(q=None) == NULL
+    assert call(out=None) == NULL
+    assert call(q=FAKE + 8) == ALIGN
+    assert call(sel=FAKE + 2) == ALIGN
+    assert call(S=1000) == SEQ
+    assert call(topk=0) == TOPK
+    assert call(Hq=3) == GQA
+    assert call(D=64) == HEAD_DIM
+    # 2M positions in blocks of 8192, 32/8 heads, top-12: the partials of one
+    # query block alone (8192 x 32 x 11 x 260 bytes) exceed 512 MiB
+    big = dict(S=2 << 20, Hq=32, Hkv=8, B=8192, topk=12)
+    assert ws_chunked(1, **{"S": big["S"], "Hq": 32, "Hkv": 8, "B": 8192, "k": 12})[1] > _lib.NOALLOC_SCRATCH_BYTES
+    assert call(**big) == WS
+    # the 1M shape fits (one query block per chunk)
+    assert ws_chunked(1)[1] <= _lib.NOALLOC_SCRATCH_BYTES
+
+
 @pytest.mark.parametrize("shape", [
     dict(S=1 << 20, Hq=32, Hkv=8, B=4096, k=12),
     dict(S=131072, Hq=32, Hkv=8, B=4096, k=12),
