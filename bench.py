@@ -79,7 +79,7 @@ def graph_replay(M, w, q, k, v, out, sel, ws, steps, gate, log):
     return ms
 
 
-def measure(M, W, w, steps, warmup, log, gate="mean", graph=False):
+def measure(M, W, w, steps, warmup, log, gate="mean", graph=False, max_chunk_blocks=0):
     import torch
     dev = "cuda"
     t0 = time.perf_counter()
@@ -87,7 +87,8 @@ def measure(M, W, w, steps, warmup, log, gate="mean", graph=False):
     out = torch.empty_like(q)
     sel = torch.empty((w.batch, w.num_q_heads, w.seqlen, w.topk), dtype=torch.int32, device=dev)
     nbytes = M.workspace_bytes(w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                               M.DTYPE_BF16 if w.dtype == "bf16" else M.DTYPE_F32, w.block_size, w.topk, w.causal)
+                               M.DTYPE_BF16 if w.dtype == "bf16" else M.DTYPE_F32, w.block_size, w.topk, w.causal,
+                               max_chunk_blocks=max_chunk_blocks)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: inputs ready in {time.perf_counter() - t0:.1f}s, workspace {nbytes / 2**30:.2f} GiB")
@@ -871,6 +872,9 @@ def main():
                     help="write the decode kernel-trace summary from a rocprofv3 --stats run, then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain copy of MIB MiB first (reference dispatch for HBM byte counters)")
+    ap.add_argument("--chunk-sweep", nargs="+", default=None, metavar="WORKLOAD [CHUNK_BLOCKS ...]",
+                    help="time a workload with workspaces that hold at most these many query blocks per chunk "
+                         "(one JSON line each; default 0 = the library's default chunk)")
     ap.add_argument("--granularity", action="store_true",
                     help="time the 32K forward at the report's five block granularities (75 %% sparsity), then exit")
     ap.add_argument("--gemm-peak", action="store_true",
@@ -925,6 +929,19 @@ def main():
 
     if args.granularity:
         granularity(M, W, log)
+        return
+    if args.chunk_sweep:
+        wc = W.WORKLOADS[args.chunk_sweep[0]]
+        for cap in [int(x) for x in args.chunk_sweep[1:]] or [0]:
+            dt = M.DTYPE_BF16 if wc.dtype == "bf16" else M.DTYPE_F32
+            nbytes = M.workspace_bytes(wc.batch, wc.seqlen, wc.num_q_heads, wc.num_kv_heads, wc.head_dim, dt,
+                                       wc.block_size, wc.topk, wc.causal, max_chunk_blocks=cap)
+            plan = M.plan_info(wc.batch, wc.seqlen, wc.num_q_heads, wc.num_kv_heads, wc.head_dim, dt,
+                               wc.block_size, wc.topk, wc.causal, nbytes)
+            r, inp, _ = measure(M, W, wc, args.steps, args.warmup, log, gate=args.gate, max_chunk_blocks=cap)
+            del inp
+            print(json.dumps({"workload": wc.name, "max_chunk_blocks": cap, "plan": plan,
+                              "workspace_bytes": nbytes, **r}), flush=True)
         return
     if args.gemm_peak:
         gemm_peak(log)

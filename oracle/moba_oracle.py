@@ -146,17 +146,18 @@ def select_blocks(scores: np.ndarray, j: int, topk: int, causal: bool) -> List[i
     return sorted(chosen)
 
 
-def key_positions(sel: Sequence[int], t: int, block_size: int, causal: bool) -> np.ndarray:
-    """Union of the chosen blocks' positions, ascending (report §2.2); the own
-    block is cut at the query itself (report §2.3, causal mask in-block)."""
+def key_ranges(sel: Sequence[int], t: int, block_size: int, causal: bool) -> List[Tuple[int, int]]:
+    """The chosen blocks' positions as [start, end) ranges, ascending (report
+    §2.2); the own block is cut at the query itself (report §2.3, causal mask
+    in-block)."""
     B = block_size
     j = t // B
-    parts = []
-    for i in sorted(sel):
-        if causal and i == j:
-            parts.append(np.arange(j * B, t + 1))
-        else:
-            parts.append(np.arange(i * B, (i + 1) * B))
+    return [(i * B, t + 1 if (causal and i == j) else (i + 1) * B) for i in sorted(sel)]
+
+
+def key_positions(sel: Sequence[int], t: int, block_size: int, causal: bool) -> np.ndarray:
+    """Union of the chosen blocks' positions, ascending (key_ranges)."""
+    parts = [np.arange(a, e) for a, e in key_ranges(sel, t, block_size, causal)]
     return np.concatenate(parts) if parts else np.zeros((0,), dtype=np.int64)
 
 
@@ -170,13 +171,10 @@ def _attend_blocks(q64: np.ndarray, k_head: np.ndarray, v_head: np.ndarray,
     attention over the union of the chosen blocks).  The chosen blocks are
     read as contiguous slices in ascending key order (no gathered copy of K),
     which keeps the 1M rows affordable."""
-    j = t // B
     logit_parts, v_parts = [], []
-    for i in sorted(sel):
-        hi = (t + 1) if (causal and i == j) else (i + 1) * B
-        kb = k_head[i * B:hi]
-        logit_parts.append((kb @ q64) * scale)
-        v_parts.append(v_head[i * B:hi])
+    for a, e in key_ranges(sel, t, B, causal):
+        logit_parts.append((k_head[a:e] @ q64) * scale)
+        v_parts.append(v_head[a:e])
     logits = np.concatenate(logit_parts)
     m = logits.max()
     p = np.exp(logits - m)
@@ -263,9 +261,11 @@ def moba_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
             hk = h // g
             for t in range(S):
                 sel = [int(i) for i in sel_idx[bb, h, t] if i >= 0]
-                keys = key_positions(sel, t, B, causal)
-                kk = k64[bb, keys, hk]
-                vv = v64[bb, keys, hk]
+                # the row's keys as the contiguous ranges of the chosen
+                # blocks in ascending order
+                ranges = key_ranges(sel, t, B, causal)
+                kk = np.concatenate([k64[bb, a:e, hk] for a, e in ranges])
+                vv = np.concatenate([v64[bb, a:e, hk] for a, e in ranges])
                 logits = (kk @ q64[bb, t, h]) * scale
                 m = logits.max()
                 z = np.exp(logits - m).sum()
@@ -275,8 +275,11 @@ def moba_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
                 dp = vv @ do64[bb, t, h]
                 ds = p * (dp - do64[bb, t, h] @ o)
                 dq[bb, t, h] = scale * (ds @ kk)
-                dk[bb, keys, hk] += scale * np.outer(ds, q64[bb, t, h])
-                dv[bb, keys, hk] += np.outer(p, do64[bb, t, h])
+                off = 0
+                for a, e in ranges:
+                    dk[bb, a:e, hk] += scale * np.outer(ds[off:off + e - a], q64[bb, t, h])
+                    dv[bb, a:e, hk] += np.outer(p[off:off + e - a], do64[bb, t, h])
+                    off += e - a
     return dq, dk, dv, lse
 
 
@@ -313,6 +316,86 @@ def backward_dq_rows(q, k, v, dout, block_size: int, causal: bool,
         ds = p * (vv @ do64 - do64 @ (p @ vv))
         dq[r] = scale * (ds @ kk)
     return dq, lse
+
+
+def backward_row_stats(q, k, v, dout, block_size: int, causal: bool,
+                       rows: Sequence[Tuple[int, int, int]], sels: Sequence[Sequence[int]]) -> dict:
+    """Per row (b, t, h) with its chosen blocks given: the row's log-sum-exp
+    of the scaled logits (natural log) and delta = dout . out over all of its
+    keys, the two row quantities every key's gradient needs (the same
+    formulas as moba_backward).  Returns {(b, t, h): (lse, delta)}."""
+    D = q.shape[3]
+    g = q.shape[2] // k.shape[2]
+    B = block_size
+    scale = 1.0 / math.sqrt(D)
+    out = {}
+    order = sorted(range(len(rows)), key=lambda r: (rows[r][0], rows[r][2] // g, r))
+    cur = None
+    for r in order:
+        bb, t, h = rows[r]
+        hk = h // g
+        if cur != (bb, hk):  # each (batch, KV head) converted once
+            cur = (bb, hk)
+            k_head = np.asarray(k[bb, :, hk, :], dtype=np.float64)
+            v_head = np.asarray(v[bb, :, hk, :], dtype=np.float64)
+        q64 = np.asarray(q[bb, t, h], dtype=np.float64)
+        do64 = np.asarray(dout[bb, t, h], dtype=np.float64)
+        sel = sorted(int(c) for c in sels[r] if c >= 0)
+        o = _attend_blocks(q64, k_head, v_head, sel, t, B, causal, scale)
+        # the log-sum-exp over the same keys, block by block in ascending order
+        logits = np.concatenate([(k_head[a:e] @ q64) * scale for a, e in key_ranges(sel, t, B, causal)])
+        m = logits.max()
+        out[(bb, t, h)] = (m + math.log(np.exp(logits - m).sum()), float(do64 @ o))
+    return out
+
+
+def attending_rows(sel_idx, block_size: int, causal: bool, b: int, s: int, hk: int, g: int):
+    """The rows (b, t, h) of KV head hk that attend key position s: the key's
+    block is in the row's selection and, in the row's own block, s <= t
+    (report §2.3)."""
+    B = block_size
+    i = s // B
+    rows = []
+    for h in range(hk * g, (hk + 1) * g):
+        for t in np.nonzero((np.asarray(sel_idx[b, h]) == i).any(axis=1))[0].tolist():
+            if causal and t // B == i and t < s:
+                continue
+            rows.append((b, t, h))
+    return rows
+
+
+def backward_dkdv_keys(q, k, v, dout, block_size: int, causal: bool,
+                       keys: Sequence[Tuple[int, int, int]], sel_idx,
+                       row_stats: Optional[dict] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """dk and dv of single keys (b, s, hk) with every row's chosen blocks
+    given by sel_idx [b, Hq, S, topk]: the same formulas as moba_backward,
+    summed over the rows that attend key s (attending_rows), for checking
+    sampled keys of large inputs:
+      dv_s = sum p_s dout,  dk_s = scale sum p_s (dout . v_s - delta) q.
+    Each row's (lse, delta) comes from backward_row_stats (computed here for
+    the rows `row_stats` lacks).  Arrays may be any type with numpy indexing."""
+    b, S, Hq, D = q.shape
+    g = Hq // k.shape[2]
+    scale = 1.0 / math.sqrt(D)
+    stats = dict(row_stats or {})
+    dk = np.zeros((len(keys), D))
+    dv = np.zeros((len(keys), D))
+    for x, (bb, s_pos, hk) in enumerate(keys):
+        rows = attending_rows(sel_idx, block_size, causal, bb, s_pos, hk, g)
+        need = [r for r in rows if r not in stats]
+        if need:
+            stats.update(backward_row_stats(q, k, v, dout, block_size, causal, need,
+                                            [sel_idx[r[0], r[2], r[1]] for r in need]))
+        k_s = np.asarray(k[bb, s_pos, hk], dtype=np.float64)
+        v_s = np.asarray(v[bb, s_pos, hk], dtype=np.float64)
+        for (_, t, h) in rows:
+            q64 = np.asarray(q[bb, t, h], dtype=np.float64)
+            do64 = np.asarray(dout[bb, t, h], dtype=np.float64)
+            lse, delta = stats[(bb, t, h)]
+            p = math.exp(float(k_s @ q64) * scale - lse)
+            dk[x] += scale * p * (float(v_s @ do64) - delta) * q64
+            dv[x] += p * do64
+    return dk, dv
 
 
 # ----------------------------------------------------------------------------

@@ -7,6 +7,7 @@ max|oracle| (per gradient tensor).  The bf16 path rounds P and dS to bf16 for
 the MFMAs (relative 2^-9 each, errors that add up over the keys or rows of a
 sum and so scale with the tensor's largest values), accumulates in fp32 and
 rounds each gradient to bf16 once (2^-9 of the element)."""
+import concurrent.futures as cf
 import sys
 
 import numpy as np
@@ -88,12 +89,91 @@ def test_backward_small(w):
     run(w)
 
 
+def oracle_backward_per_kv_head(q, k, v, do, w, sel):
+    """O.moba_backward run per KV head (a head group's gradients depend on
+    its own rows and keys only), the groups in threads."""
+    g = w.num_q_heads // w.num_kv_heads
+
+    def one(hk):
+        hs = slice(hk * g, (hk + 1) * g)
+        return hk, O.moba_backward(q[:, :, hs], k[:, :, hk:hk + 1], v[:, :, hk:hk + 1], do[:, :, hs], w.block_size,
+                                   w.topk, w.causal, sel_idx=sel[:, hs])
+
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    lse = np.zeros((w.batch, w.num_q_heads, w.seqlen))
+    with cf.ThreadPoolExecutor(max_workers=min(16, w.num_kv_heads)) as ex:
+        for hk, (a, b, c, l) in ex.map(one, range(w.num_kv_heads)):
+            dq[:, :, hk * g:(hk + 1) * g] = a
+            dk[:, :, hk:hk + 1] = b
+            dv[:, :, hk:hk + 1] = c
+            lse[:, hk * g:(hk + 1) * g] = l
+    return dq, dk, dv, lse
+
+
+def test_backward_gqa32x8_top12_full():
+    """The training configuration's head layout and top-k (32 query / 8 KV
+    heads, top-12) at 2K positions in blocks of 128 (16 blocks, so the gate
+    ranks 11 of up to 15 past blocks): every element of dq, dk and dv against
+    the oracle's full backward with the GPU's selection."""
+    w = small("bwd_gqa32x8_2k_top12", 1, 2048, 32, 8, 128, 12, seed=29)
+    say(f"[case] backward full {w}")
+    q, k, v, _ = W.make_inputs(w, device=DEV)
+    do = dout_for(w, DEV)
+    out, sel, lse = M.moba_attn_fwd_train(q, k, v, w.block_size, w.topk, w.causal)
+    dq, dk, dv = M.moba_attn_bwd(q, k, v, out, do, lse, sel, w.block_size, w.topk, w.causal)
+    torch.cuda.synchronize()
+    rq, rk, rv, rl = oracle_backward_per_kv_head(to_np32(q), to_np32(k), to_np32(v), to_np32(do), w,
+                                                 sel.cpu().numpy())
+    assert float(np.abs(lse.cpu().numpy().astype(np.float64) - rl).max()) < 2.5e-3
+    check("dq", to_np32(dq), rq)
+    check("dk", to_np32(dk), rk)
+    check("dv", to_np32(dv), rv)
+
+
+def test_backward_workload_128k_sampled_dkdv():
+    """dk and dv at the backward's benchmark configuration (128K positions,
+    32/8 heads, block 4096, top-12) for sampled keys of two KV heads: the last
+    eight keys of block 30 (attended by the rows of block 31 that chose block
+    30 and by the own-block rows at or after them) and of block 31 (own-block
+    rows only), against the oracle's per-key gradients with the GPU's
+    selection; each attending row's log-sum-exp and delta come from the
+    oracle's full row, computed in threads."""
+    from parity_utils import RowSource
+    w = W.WORKLOADS["gqa32x8_128k"]
+    say(f"[case] backward sampled dk/dv {w}")
+    q, k, v, _ = W.make_inputs(w, device=DEV)
+    do = dout_for(w, DEV)
+    out, sel, lse = M.moba_attn_fwd_train(q, k, v, w.block_size, w.topk, w.causal)
+    dq, dk, dv = M.moba_attn_bwd(q, k, v, out, do, lse, sel, w.block_size, w.topk, w.causal)
+    torch.cuda.synchronize()
+    B, g = w.block_size, w.num_q_heads // w.num_kv_heads
+    keys = [(0, i * B + B - 8 + x, hk) for hk in (0, 7) for i in (30, 31) for x in range(8)]
+    selh = sel.cpu().numpy()
+    qh, kh, vh, doh = RowSource(q.cpu()), RowSource(k.cpu()), RowSource(v.cpu()), RowSource(do.cpu())
+    rows = sorted({r for (bb, s_, hk) in keys for r in O.attending_rows(selh, B, w.causal, bb, s_, hk, g)})
+    say(f"[bwd sampled] {len(keys)} keys, {len(rows)} attending rows")
+    parts = [rows[i::16] for i in range(16)]
+
+    def stats(part):
+        return O.backward_row_stats(qh, kh, vh, doh, B, w.causal, part, [selh[r[0], r[2], r[1]] for r in part])
+
+    row_stats = {}
+    with cf.ThreadPoolExecutor(max_workers=16) as ex:
+        for st in ex.map(stats, parts):
+            row_stats.update(st)
+    rk, rv = O.backward_dkdv_keys(qh, kh, vh, doh, B, w.causal, keys, selh, row_stats=row_stats)
+    got_k = np.stack([to_np32(dk[bb, s_, hk]) for (bb, s_, hk) in keys])
+    got_v = np.stack([to_np32(dv[bb, s_, hk]) for (bb, s_, hk) in keys])
+    check("dk (sampled keys)", got_k, rk)
+    check("dv (sampled keys)", got_v, rv)
+
+
 def test_backward_workload_128k_sampled_dq():
     """The backward's benchmark configuration (128K positions, 32/8 heads,
     block 4096, top-12): dq of seeded sample rows against the oracle's per-row
     dq, with the oracle's own selection (rows whose GPU selection differs by a
-    near tie are counted and skipped); dk and dv depend on every row attending
-    a key and are checked on the small shapes above."""
+    near tie are counted and skipped); dk and dv are checked on sampled keys
+    below and in full at 2K."""
     from parity_utils import RowSource
     w = W.WORKLOADS["gqa32x8_128k"]
     say(f"[case] backward sampled {w}")

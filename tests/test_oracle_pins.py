@@ -953,15 +953,15 @@ def test_planted_backward_mistakes_are_caught(monkeypatch):
     dout = rng.standard_normal(q.shape)
     _, sel = O.moba_forward(q, k, v, B, topk, True)
     rq, rk, rv = _autograd_masked(q, k, v, dout, _mask_from_sel(sel, S, B, True))
-    real = O.key_positions
+    real = O.key_ranges
 
     def own_uncut(sel_, t, B_, causal):
         return real(sel_, (t // B_) * B_ + B_ - 1, B_, causal) if causal else real(sel_, t, B_, causal)
 
-    monkeypatch.setattr(O, "key_positions", own_uncut)
+    monkeypatch.setattr(O, "key_ranges", own_uncut)
     dq, dk, dv, _ = O.moba_backward(q, k, v, dout, B, topk, True, sel_idx=sel)
     assert not np.allclose(dv, rv, atol=1e-6)
-    monkeypatch.setattr(O, "key_positions", real)
+    monkeypatch.setattr(O, "key_ranges", real)
     dq, dk, dv, _ = O.moba_backward(q, k, v, dout, B, topk, True, sel_idx=sel)
     np.testing.assert_allclose(dv, rv, rtol=0, atol=1e-10)
 
@@ -980,3 +980,23 @@ def test_backward_dq_rows_equal_the_full_backward():
     for x, (bb, t, h) in enumerate(rows):
         np.testing.assert_allclose(got[x], dq[bb, t, h], rtol=0, atol=1e-12)
         assert abs(gl[x] - lse[bb, h, t]) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_dkdv_keys_equal_the_full_backward(causal):
+    """The per-key dk / dv (for sampled checks at large sizes) is the full
+    backward's, key by key, up to summation order: keys in own blocks, in
+    blocks chosen as past blocks, and in blocks nobody chose."""
+    rng = np.random.default_rng(32)
+    S, B, topk, D = 64, 16, 2, 8
+    q, k, v = rand_qkv(rng, 2, S, 4, 2, D)
+    dout = rng.standard_normal(q.shape)
+    _, sel = O.moba_forward(q, k, v, B, topk, causal)
+    _, dk, dv, _ = O.moba_backward(q, k, v, dout, B, topk, causal, sel_idx=sel)
+    keys = [(bb, s, hk) for bb in range(2) for s in (0, 7, 15, 16, 31, 40, 47, 48, 63) for hk in range(2)]
+    gk, gv = O.backward_dkdv_keys(q, k, v, dout, B, causal, keys, sel)
+    for x, (bb, s, hk) in enumerate(keys):
+        np.testing.assert_allclose(gk[x], dk[bb, s, hk], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(gv[x], dv[bb, s, hk], rtol=0, atol=1e-12)
+    # a key of the last block is attended only by its own rows at or after it
+    assert np.abs(dk[:, 63]).max() > 0
