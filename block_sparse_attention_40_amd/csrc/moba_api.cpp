@@ -73,114 +73,6 @@ double past_blocks_sum(const Plan& p, int64_t t0, int64_t cnt) {
   return tot;
 }
 
-// Decode: sizes, limits and the workspace carve-up.
-struct DecodePlan {
-  int64_t nmax;
-  int32_t g, U, nchunk;
-  size_t off_sc, off_uni, off_uslot, off_ucount, off_sel, off_po, off_pml, off_ksum, total;
-};
-
-int make_decode_plan(int64_t batch, int64_t lmax, int32_t hq, int32_t hkv, int32_t d, int32_t dtype, int32_t block,
-                     int32_t topk, DecodePlan* p) {
-  if (dtype != MOBA_DTYPE_F32 && dtype != MOBA_DTYPE_BF16) return MOBA_ERR_DTYPE;
-  if (batch < 1 || lmax < 1 || hq < 1 || hkv < 1 || block < 1 || d < 1) return MOBA_ERR_SHAPE;
-  if (dtype == MOBA_DTYPE_BF16 && d != 128) return MOBA_ERR_HEAD_DIM;
-  if (dtype == MOBA_DTYPE_F32 && d != 64 && d != 128) return MOBA_ERR_HEAD_DIM;
-  if (hq % hkv != 0 || hq / hkv > kDecodeMaxGroup) return MOBA_ERR_GQA;
-  if (topk < 1 || topk > kDecodeMaxTopk) return MOBA_ERR_TOPK;
-  if (lmax % block != 0) return MOBA_ERR_SEQ_NOT_DIVISIBLE;
-  DecodePlan q{};
-  q.nmax = lmax / block;
-  q.g = hq / hkv;
-  q.U = q.g * topk;
-  q.nchunk = (block + kDecodeChunk - 1) / kDecodeChunk;
-  // grid limits: (batch * hkv, nchunk, U), (hkv, batch), (hq, batch)
-  if (q.nmax > kDecodeMaxBlocks || batch > 65535 || q.nchunk > 65535 || batch * hkv > (int64_t(1) << 31) - 1 ||
-      lmax > (int64_t(1) << 31) - 1)
-    return MOBA_ERR_SHAPE;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off += (bytes + 255) & ~size_t(255);
-    return o;
-  };
-  const size_t rows = (size_t)batch * hq;
-  q.off_sc = take(rows * q.nmax * sizeof(float));
-  q.off_uni = take((size_t)batch * hkv * q.U * sizeof(int32_t));
-  q.off_uslot = take((size_t)batch * hkv * q.U * q.g * sizeof(int32_t));
-  q.off_ucount = take((size_t)batch * hkv * sizeof(int32_t));
-  q.off_sel = take(rows * topk * sizeof(int32_t));
-  q.off_po = take(rows * topk * q.nchunk * (size_t)d * sizeof(float));
-  q.off_pml = take(rows * topk * q.nchunk * 2 * sizeof(float));
-  q.off_ksum = take((size_t)batch * hkv * q.nchunk * (size_t)d * sizeof(float));
-  q.total = off;
-  *p = q;
-  return MOBA_OK;
-}
-
-// Backward: sizes and the workspace carve-up (bf16, head dim 128).
-constexpr uint64_t kBwdPartialCapBytes = 2ull << 30;  // per-chunk dq contributions
-struct BwdPlan {
-  Plan p;
-  int32_t kps;              // dq slots per row: kp past + 1 own (causal)
-  int64_t gate_wg_f;        // rows-per-work-group units of the whole sequence
-  int64_t max_tiles_f;
-  int64_t chunk;            // query positions per dq chunk (whole blocks)
-  int64_t gate_wg_c, max_tiles_c;
-  size_t off_lse2, off_delta, off_kimg, off_vtmp, off_vkimg, off_kvimg;
-  size_t off_hist_f, off_count_f, off_listoff_f, off_tiles_f, off_entries_f;
-  size_t off_hist_c, off_count_c, off_listoff_c, off_tiles_c, off_entries_c, off_dqp, total;
-};
-
-int make_bwd_plan(const Shape& s, BwdPlan* out) {
-  BwdPlan b{};
-  const int st = make_plan(s, &b.p);
-  if (st != MOBA_OK) return st;
-  if (s.dtype != MOBA_DTYPE_BF16) return MOBA_ERR_DTYPE;  // the backward runs on bf16 MFMA
-  if (s.block % 64 != 0) return MOBA_ERR_SHAPE;            // whole 64-key slices
-  const Plan& p = b.p;
-  b.kps = p.kp + (s.causal ? 1 : 0);
-  const int64_t S = s.seqlen, rows = s.batch * S * s.hq, lists = (int64_t)s.hkv * p.n;
-  // the whole-sequence dk/dv lists hold one int32 entry (row * kp + slot) per
-  // (row, past block) pair of a batch entry, and their offsets are int32
-  if (S * s.hq * (int64_t)std::max(p.kp, 1) >= (int64_t(1) << 31)) return MOBA_ERR_SHAPE;
-  b.gate_wg_f = (S + p.gate_t - 1) / p.gate_t;
-  b.max_tiles_f = ((S * s.hq * (int64_t)std::max(p.kp, 0) + 255) / 256 + lists + 7) / 8 * 8;
-  const uint64_t per_block = (uint64_t)s.block * s.hq * b.kps * 128 * 4;
-  int64_t cb = (int64_t)std::max<uint64_t>(1, kBwdPartialCapBytes / per_block);
-  cb = std::min<int64_t>(cb, p.n);
-  b.chunk = cb * s.block;
-  b.gate_wg_c = (b.chunk + p.gate_t - 1) / p.gate_t;
-  b.max_tiles_c = ((b.chunk * s.hq * (int64_t)std::max(p.kp, 0) + 255) / 256 + lists + 7) / 8 * 8;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off += (bytes + 255) & ~size_t(255);
-    return o;
-  };
-  const size_t img = (size_t)s.batch * S * s.hkv * 128 * 2;
-  b.off_lse2 = take(rows * 4);
-  b.off_delta = take(rows * 4);
-  b.off_kimg = take(img);
-  b.off_vtmp = take(img);
-  b.off_vkimg = take(img);
-  b.off_kvimg = take(img);
-  b.off_hist_f = take((size_t)lists * b.gate_wg_f * 4);
-  b.off_count_f = take((size_t)lists * 4);
-  b.off_listoff_f = take((size_t)(lists + 1) * 4);
-  b.off_tiles_f = take((size_t)(8 + 2 * b.max_tiles_f) * 4);
-  b.off_entries_f = take((size_t)S * s.hq * std::max(p.kp, 1) * 4);
-  b.off_hist_c = take((size_t)lists * b.gate_wg_c * 4);
-  b.off_count_c = take((size_t)lists * 4);
-  b.off_listoff_c = take((size_t)(lists + 1) * 4);
-  b.off_tiles_c = take((size_t)(8 + 2 * b.max_tiles_c) * 4);
-  b.off_entries_c = take((size_t)b.chunk * s.hq * std::max(p.kp, 1) * 4);
-  b.off_dqp = take((size_t)b.chunk * s.hq * b.kps * 128 * 4);
-  b.total = off;
-  *out = b;
-  return MOBA_OK;
-}
-
 // moba_attn_fwd_noalloc's fixed scratch.  In host code `scratch` names a
 // host-side stand-in, not the device array: the device address comes from
 // hipGetSymbolAddress, once per device (each GPU holds its own copy of the

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moba_plan.h"
+
 namespace moba {
 
 // Gate over one query chunk: positions [t0, t0 + cnt) of batch entry bb.
@@ -87,11 +89,8 @@ struct F32Args {
   float scale_log2;
 };
 
-// Decode (one new query per sequence against its cache).
-constexpr int kDecodeMaxGroup = 16;     // query heads per KV head
-constexpr int kDecodeMaxTopk = 64;
-constexpr int kDecodeMaxBlocks = 16384;  // cache capacity in blocks
-constexpr int kDecodeChunk = 512;        // keys per attention work-group (8 steps of 64)
+// Decode (one new query per sequence against its cache); the limits are in
+// moba_plan.h.
 struct DecodeArgs {
   const void* q;           // [batch, hq, d]
   const void* k;           // [batch, lmax, hkv, d]

@@ -56,6 +56,24 @@ struct Plan {
   size_t off_part_o, off_part_lse, off_kimg, off_vimg, off_mu3, off_lohi, total;
 };
 
+// Decode (one new query per sequence against its cache).
+constexpr int kDecodeMaxGroup = 16;     // query heads per KV head
+constexpr int kDecodeMaxTopk = 64;
+constexpr int kDecodeMaxBlocks = 16384;  // cache capacity in blocks
+constexpr int kDecodeChunk = 512;        // keys per attention work-group (8 steps of 64)
+
+// Decode: sizes, limits and the workspace carve-up.
+struct DecodePlan {
+  int64_t nmax;
+  int32_t g, U, nchunk;
+  size_t off_sc, off_uni, off_uslot, off_ucount, off_sel, off_po, off_pml, off_ksum, total;
+};
+int make_decode_plan(int64_t batch, int64_t lmax, int32_t hq, int32_t hkv, int32_t d, int32_t dtype, int32_t block,
+                     int32_t topk, DecodePlan* p);
+
+// Backward: sizes and the workspace carve-up (bf16, head dim 128).
+constexpr uint64_t kBwdPartialCapBytes = 2ull << 30;  // per-chunk dq contributions
+
 // Validate `s` and fill `p`.  max_chunk_blocks > 0 caps the query blocks per
 // chunk (0: the default, partials of one chunk within kPartialCapBytes);
 // allow_image = false never re-lays K and V out as slice images.  Returns a
@@ -67,5 +85,18 @@ int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks = 0, bool allow_
 // with them fits.  MOBA_ERR_WORKSPACE when even one query block per chunk
 // does not fit.
 int plan_for_workspace(const Shape& s, size_t ws_bytes, Plan* p);
+
+struct BwdPlan {
+  Plan p;
+  int32_t kps;              // dq slots per row: kp past + 1 own (causal)
+  int64_t gate_wg_f;        // rows-per-work-group units of the whole sequence
+  int64_t max_tiles_f;
+  int64_t chunk;            // query positions per dq chunk (whole blocks)
+  int64_t gate_wg_c, max_tiles_c;
+  size_t off_lse2, off_delta, off_kimg, off_vtmp, off_vkimg, off_kvimg;
+  size_t off_hist_f, off_count_f, off_listoff_f, off_tiles_f, off_entries_f;
+  size_t off_hist_c, off_count_c, off_listoff_c, off_tiles_c, off_entries_c, off_dqp, total;
+};
+int make_bwd_plan(const Shape& s, BwdPlan* out);
 
 }  // namespace moba
