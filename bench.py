@@ -313,15 +313,22 @@ MFMA_CMD = ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_AC
 PMC32_CMD = ("rocprofv3 --pmc {counters} --output-format csv -d gpurun_out/pmc32k_{tag} -o run -- "
              "python3 -u bench.py --workload mha32_32k_needle --steps 1 --warmup 2 --secondary '' "
              "--no-cpu-baseline --no-gemm-reference --copy-calibration 1024 > gpurun_out/pmc32k_{tag}.json")
+# VALU counters (the gate's bound, the attention kernels' co-issue)
+VALU_COUNTERS = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES "
+                 "SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_LDS SQ_WAIT_INST_ANY SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
+VALU_CMD = ("rocprofv3 --pmc " + VALU_COUNTERS + " --output-format csv -d gpurun_out/pmc_valu -o run -- "
+            "python3 -u bench.py --steps 1 --warmup 0 --secondary '' --no-cpu-baseline --no-gemm-reference "
+            "> gpurun_out/pmc_valu.json")
 PROFILE_CMDS = {
     "gqa32x8_1m": {"title": "gqa32x8_1m workload (1M tokens, 32/8 heads, D 128, block 4096, top-12)",
                    "fetch": PMC_CMD.format(counter="FETCH_SIZE"), "write": PMC_CMD.format(counter="WRITE_SIZE"),
-                   "mfma": MFMA_CMD},
+                   "mfma": MFMA_CMD, "valu": VALU_CMD},
     "mha32_32k_needle": {"title": "mha32_32k_needle workload (32K tokens, 32 heads, D 128, block 512, top-3)",
                          "fetch": PMC32_CMD.format(counters="FETCH_SIZE", tag="FETCH_SIZE"),
                          "write": PMC32_CMD.format(counters="WRITE_SIZE", tag="WRITE_SIZE"),
                          "mfma": PMC32_CMD.format(counters="SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
-                                                  tag="mfma")},
+                                                  tag="mfma"),
+                         "valu": PMC32_CMD.format(counters=VALU_COUNTERS, tag="valu")},
 }
 
 
@@ -389,6 +396,58 @@ def summarize_mfma(pmc_dir, bench_json):
         busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * simds)
         res[k] = {"busy": busy, "clock_ghz": cyc / t / 1e9, "ms": t * 1e3}
         out.append(f"| {k} | {len(d['disp'])} | {t * 1e3:.2f} | {100 * busy:.1f} % | {cyc / t / 1e9:.2f} |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    return res
+
+
+def summarize_valu(pmc_dir, bench_json):
+    """Per kernel, from one counter run: VALU and MFMA instructions per wave-
+    instruction slot, the VALU issue fraction (VALU instructions x 4 cycles,
+    a wave64 VALU instruction's issue time, over the SIMD cycles), the MFMA-
+    busy fraction, the fraction of MFMA-busy cycles in which a VALU
+    instruction was issued beside it (co-issue), and the wave-cycles spent
+    waiting to issue."""
+    info = _agent_info(pmc_dir)
+    simds, xcc = int(info["Simd_Count"]), int(info["Num_Xcc"])
+    wl = _workload_of(bench_json)
+    cmds = PROFILE_CMDS[wl]
+    out_path = os.path.join(ROOT, "profiles", f"valu_{wl}.md")
+    per = {}
+    for r in _counter_rows(pmc_dir):
+        k = _short(r["Kernel_Name"])
+        if not k.startswith("moba::"):
+            continue
+        d = per.setdefault(k, {"disp": set(), "t": {}})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["disp"].add(r["Dispatch_Id"])
+        d["t"][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    out = [f"# VALU and MFMA issue: MoBA forward, {cmds['title']}",
+           "", "Command (run from the repository root on one MI355X):", "", "```", cmds["valu"], "```", "",
+           f"Counters summed over the dispatches of the run's forward calls; {simds} SIMDs, {xcc} XCDs; SIMD cycles "
+           "= GRBM_GUI_ACTIVE / XCDs x SIMDs.  VALU issue = SQ_INSTS_VALU x 4 / SIMD cycles (a wave64 VALU "
+           "instruction issues over 4 cycles); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMD cycles; co-issue = "
+           "SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES; VALU per MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) "
+           "/ SQ_INSTS_MFMA (SQ_INSTS_VALU counts the MFMA instructions too).", "",
+           "| Kernel | Dispatches | Kernel ms (sum) | VALU issue | MFMA busy | co-issue | VALU per MFMA | "
+           "LDS per MFMA |", "|---|---|---|---|---|---|---|---|"]
+    res = {}
+    for k, d in sorted(per.items(), key=lambda x: -sum(x[1]["t"].values())):
+        if d.get("GRBM_GUI_ACTIVE", 0.0) <= 0:
+            continue
+        cyc = d["GRBM_GUI_ACTIVE"] / xcc * simds
+        t = sum(d["t"].values())
+        valu = d.get("SQ_INSTS_VALU", 0.0)
+        mfma = d.get("SQ_INSTS_MFMA", 0.0)
+        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        r = {"valu_issue": valu * 4 / cyc, "mfma_busy": busy / cyc,
+             "coissue": d.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / busy if busy else None,
+             "valu_per_mfma": (valu - mfma) / mfma if mfma else None,
+             "lds_per_mfma": d.get("SQ_INSTS_LDS", 0.0) / mfma if mfma else None, "ms": t * 1e3}
+        res[k] = r
+        f = lambda x, pct=True: "-" if x is None else (f"{100 * x:.1f} %" if pct else f"{x:.2f}")
+        out.append(f"| {k} | {len(d['disp'])} | {t * 1e3:.2f} | {f(r['valu_issue'])} | {f(r['mfma_busy'])} | "
+                   f"{f(r['coissue'])} | {f(r['valu_per_mfma'], False)} | {f(r['lds_per_mfma'], False)} |")
     with open(out_path, "w") as fh:
         fh.write("\n".join(out) + "\n")
     return res
@@ -889,6 +948,8 @@ def main():
                     help="write the kernel-trace summary from a rocprofv3 --stats run, then exit")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "BENCH_JSON"),
                     help="write the MFMA-busy summary from a rocprofv3 --pmc run, then exit")
+    ap.add_argument("--summarize-valu", nargs=2, metavar=("PMC_DIR", "BENCH_JSON"),
+                    help="write profiles/valu_<workload>.md from a VALU counter run")
     ap.add_argument("--summarize-hbm", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
                     help="write the per-kernel HBM summary from the two traffic runs, then exit")
     args = ap.parse_args()
@@ -898,6 +959,9 @@ def main():
     if args.summarize_hbm:
         print(json.dumps(summarize_stage_hbm(args.summarize_hbm[0], args.summarize_hbm[1], 1024,
                                              args.summarize_hbm[2]), indent=1))
+        return
+    if args.summarize_valu:
+        print(json.dumps(summarize_valu(*args.summarize_valu), indent=1))
         return
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic, 1024, TRAFFIC_FILE), indent=1))
