@@ -297,6 +297,29 @@ def test_forward_dense_one_block_sampled():
     run(w, rows=W.sample_rows(w, 48, seed=26), device_inputs=True)
 
 
+@pytest.mark.slow
+def test_forward_curve_dense_1m_sampled():
+    """The speedup curve's dense baseline at its longest length: one causal
+    block of 1M positions (block_size = seqlen, topk = 1), GQA 32/8; sampled
+    rows including the first and last position (up to 1M keys per row)."""
+    w = small("dense_1m", "bf16", 1, 1 << 20, 32, 8, 128, 1 << 20, 1, seed=33)
+    rows = W.sample_rows(w, 4, seed=34, extra_positions=(1, 63, 64, 65535, 524288))
+    run(w, rows=rows, device_inputs=True)
+
+
+@pytest.mark.slow
+def test_forward_block_40960_sampled():
+    """The block size of the curve's 10M point (40960 keys: 640 slices per
+    block), 16 blocks, top-12, GQA 32/8 (655 360 positions; the 10M point
+    itself holds 200 GiB of inputs); sampled rows including every block's
+    first and last position for head 0."""
+    B = 40960
+    w = small("b40960", "bf16", 1, 16 * B, 32, 8, 128, B, 12, seed=35)
+    edges = [x for i in range(16) for x in (i * B, i * B + B - 1)]
+    rows = W.sample_rows(w, 8, seed=36, extra_positions=edges[:8]) + [(0, t, 0) for t in edges[8:]]
+    run(w, rows=sorted(set(rows)), device_inputs=True)
+
+
 def test_forward_curve_config_32k_sampled():
     """The speedup curve's MoBA configuration at its shortest length: 256 blocks
     of 128, top-12, GQA 32/8."""
