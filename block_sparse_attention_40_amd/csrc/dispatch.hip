@@ -108,6 +108,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(DispatchArgs a) {
   for (int c = 0; c < a.topk && slot < a.kp; ++c) {
     const int32_t i = row[c];
     if (i < 0) break;
+    // never a valid choice (a block beyond the sequence, or after the own
+    // block): skipped, so a malformed selection given to the backward stays
+    // inside the lists
+    if (i >= n || (a.causal && i > j)) continue;
     if (a.causal && i == j) continue;  // own block: handled by the own-block kernel
     const int32_t r = atomicAdd(&lcnt[i], 1);
     const int64_t L = (int64_t)hk * n + i;
@@ -138,6 +142,7 @@ __global__ __launch_bounds__(256) void hist_kernel(DispatchArgs a) {
     for (int c = 0; c < a.topk && slot < a.kp; ++c) {
       const int32_t i = row[c];
       if (i < 0) break;
+      if (i >= n || (a.causal && i > j)) continue;  // never a valid choice (as in scatter_kernel)
       if (a.causal && i == j) continue;
       atomicAdd(&lcnt[i], 1);
       ++slot;

@@ -246,7 +246,12 @@ int moba_attn_fwd_train(const void* q, const void* k, const void* v,
  * gradient of the forward as computed.
  *
  * Inputs: q, k, v, out, dout as for moba_attn_fwd (out and dout like q); lse
- * and sel_idx as written by moba_attn_fwd_train with the same shapes.
+ * and sel_idx as written by moba_attn_fwd_train with the same shapes.  A
+ * selection entry that can never be chosen (beyond the last block, or after
+ * the row's own block) is skipped, so no memory outside the given buffers is
+ * touched; any other departure from a forward's selection (repeated blocks,
+ * fewer past blocks than min(topk - 1, own block)) gives unspecified
+ * gradients.
  * Outputs: dq like q, dk and dv like k, written in full (every key gets its
  * gradient, zero for a key no row attends).  bf16 only (MOBA_ERR_DTYPE for
  * fp32), head_dim 128, block_size a multiple of 64 (MOBA_ERR_SHAPE).
