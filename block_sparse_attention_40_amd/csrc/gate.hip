@@ -262,6 +262,22 @@ __device__ __forceinline__ void sign_split(u32x4 w, bf16x8& pos, bf16x8& neg) {
   neg = __builtin_bit_cast(bf16x8, n);
 }
 
+// A value and the one lane l ^ 32 holds (v_permlane32_swap with both inputs
+// the same value: lane l < 32 gets (x[l], x[l + 32]), lane l >= 32 gets
+// (x[l - 32], x[l])); the two results are copied to scalars first.
+__device__ __forceinline__ void pair_values_u(uint32_t x, uint32_t& u, uint32_t& v) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  const uint32_t r0 = pr[0], r1 = pr[1];
+  u = r0;
+  v = r1;
+}
+__device__ __forceinline__ void pair_values_f(float x, float& u, float& v) {
+  uint32_t a, b;
+  pair_values_u(__builtin_bit_cast(uint32_t, x), a, b);
+  u = __builtin_bit_cast(float, a);
+  v = __builtin_bit_cast(float, b);
+}
+
 // Insert a 64-bit key into a descending top list (ks[0] largest).
 template <int KCAP>
 __device__ __forceinline__ void topk_insert(uint64_t* ks, uint64_t key) {
@@ -277,12 +293,47 @@ __device__ __forceinline__ void topk_insert(uint64_t* ks, uint64_t key) {
   }
 }
 
+// The m-th largest of a row's candidate scores (m <= KCAP) and how many of
+// them lie above it, from a descending list of the row's top KCAP scores.
+template <int KCAP>
+__device__ __forceinline__ void list_insert(float* tv, float x) {
+  // tv sorted descending; with x inserted, entry p becomes the median of
+  // (tv[p-1], tv[p], x) of the list before (x above tv[p-1]: tv[p-1]; x
+  // between: x; x below tv[p]: tv[p]).  One v_med3_f32 per entry, from the
+  // old values (highest index first, in place), and no chain between them.
+#pragma unroll
+  for (int p = KCAP - 1; p > 0; --p) tv[p] = __builtin_amdgcn_fmed3f(tv[p - 1], tv[p], x);
+  tv[0] = __builtin_fmaxf(tv[0], x);
+}
+
+// Bits e (0..15) of a lane half's 16 scores of a 32-block score tile, placed
+// at their block offsets inside the tile: score e of lane half lg is block
+// 8 (e >> 2) + 4 lg + (e & 3).
+__device__ __forceinline__ uint32_t spread_tile_bits(uint32_t m16, int lg) {
+  const uint32_t x = (m16 & 0xfu) | ((m16 & 0xf0u) << 4) | ((m16 & 0xf00u) << 8) | ((m16 & 0xf000u) << 12);
+  return x << (4 * lg);
+}
+
+// Lists of up to this many entries take the one-pass choice (a short 64-bit
+// insertion list costs less than scoring every tile twice); longer lists take
+// the two passes.
+constexpr int kGateOnePassMaxKcap = 4;
+
 // One work-group = 256 rows (gate_t positions x the group's heads of one KV
 // head), 8 waves of 32 rows.  Per tile of 32 blocks a wave computes the
 // 32 x 32 score tile S^T = Mu Q^T (24 MFMAs: 3 parts x 8 steps of 16 d);
 // lane l then holds 16 of the 32 scores of row l % 32 (the other 16 are in
-// lane l ^ 32) and keeps its own top list; at the end the two lists of a
-// row are merged.
+// lane l ^ 32).  The top-m choice is exact.  Short lists (KCAP at most
+// kGateOnePassMaxKcap) keep 64-bit (score, index) keys in one pass; longer
+// ones take two passes over the tiles:
+//   1. every lane keeps the descending top-KCAP list of its scores (fp32
+//      values only, one median-of-three per entry and score, no branch); the
+//      two half-row lists are merged, and the row's m-th largest score T and
+//      the number of its scores above T follow;
+//   2. the tiles are scored again (the same MFMAs on the same operands give
+//      the same fp32 scores) and a row keeps every block scoring above T and,
+//      of those scoring exactly T, the lowest-index ones up to m: the tie
+//      rule.  The kept blocks come out tile by tile in ascending order.
 template <int KCAP, bool kMinMax>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(KCAP <= 12 ? 4 : 1))) void gate_mfma_kernel(
     GateArgs a, const uint16_t* __restrict__ mu3) {
@@ -314,9 +365,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(KCAP <= 12 
   const int64_t ntile = (n + kGateTile - 1) / kGateTile;
   const int64_t wg_tiles = (wg_cand + kGateTile - 1) / kGateTile;
 
-  uint64_t ks[KCAP];
-#pragma unroll
-  for (int p = 0; p < KCAP; ++p) ks[p] = (p < KCAP - m) ? ~0ull : 0ull;
+  int32_t* row = a.sel + (int64_t)h * a.sel_stride_h + (t - a.sel_pos_base) * a.topk;
+  int nout = 0;  // entries written to the row so far
 
   const int any_rank = __syncthreads_or(rank ? 1 : 0);
   if (any_rank) {
@@ -339,105 +389,192 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(KCAP <= 12 
 #pragma unroll
       for (int x = 0; x < NPART; ++x) *reinterpret_cast<u32x4*>(dst + (tid + 512 * x) * 16) = stg[x];
     };
-    load_tile(0);
-    store_tile(tbuf);
-    __syncthreads();
-    for (int64_t c = 0; c < wg_tiles; ++c) {
-      char* cur = tbuf + (c & 1) * (kMu3TileElems * 2);
-      if (c + 1 < wg_tiles) load_tile(c + 1);
-      // the MFMAs run on the whole wave (wave-uniform branch); only the
-      // insertions depend on the row
-      if (__any(rank && c * kGateTile < ncand)) {
-        f32x16 s0, s1;
+    // this lane's 16 scores of tile c (LDS image cur), NaN ranked lowest
+    auto score_tile = [&](const char* cur, float* sc) {
+      f32x16 s0, s1;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
-        if constexpr (kMinMax) {
-          // B operands q+ (with hi, part 0) and q- (with lo, part 1), formed
-          // from q per tile: the opaque copy keeps the compiler from holding
-          // all 16 of them live across the loop (32 more VGPRs, half the
-          // work-groups per CU)
+      for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+      if constexpr (kMinMax) {
+        // B operands q+ (with hi, part 0) and q- (with lo, part 1), formed
+        // from q per tile: the opaque copy keeps the compiler from holding
+        // all 16 of them live across the loop
+#pragma unroll
+        for (int st = 0; st < 8; st += 2) {
+          u32x4 w0 = __builtin_bit_cast(u32x4, qb[st]), w1 = __builtin_bit_cast(u32x4, qb[st + 1]);
+          asm volatile("" : "+v"(w0));
+          asm volatile("" : "+v"(w1));
+          bf16x8 p0, n0, p1, n1;
+          sign_split(w0, p0, n0);
+          sign_split(w1, p1, n1);
+          const bf16x8 h0 = *reinterpret_cast<const bf16x8*>(cur + aofs + (2 * st) * 512);
+          const bf16x8 h1 = *reinterpret_cast<const bf16x8*>(cur + aofs + (2 * st + 2) * 512);
+          const bf16x8 l0 = *reinterpret_cast<const bf16x8*>(cur + aofs + (16 + 2 * st) * 512);
+          const bf16x8 l1 = *reinterpret_cast<const bf16x8*>(cur + aofs + (16 + 2 * st + 2) * 512);
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, p0, s0, 0, 0, 0);
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, p1, s0, 0, 0, 0);
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l0, n0, s0, 0, 0, 0);
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l1, n1, s0, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int part = 0; part < NPART; ++part)
 #pragma unroll
           for (int st = 0; st < 8; st += 2) {
-            u32x4 w0 = __builtin_bit_cast(u32x4, qb[st]), w1 = __builtin_bit_cast(u32x4, qb[st + 1]);
-            asm volatile("" : "+v"(w0));
-            asm volatile("" : "+v"(w1));
-            bf16x8 p0, n0, p1, n1;
-            sign_split(w0, p0, n0);
-            sign_split(w1, p1, n1);
-            const bf16x8 h0 = *reinterpret_cast<const bf16x8*>(cur + aofs + (2 * st) * 512);
-            const bf16x8 h1 = *reinterpret_cast<const bf16x8*>(cur + aofs + (2 * st + 2) * 512);
-            const bf16x8 l0 = *reinterpret_cast<const bf16x8*>(cur + aofs + (16 + 2 * st) * 512);
-            const bf16x8 l1 = *reinterpret_cast<const bf16x8*>(cur + aofs + (16 + 2 * st + 2) * 512);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, p0, s0, 0, 0, 0);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, p1, s0, 0, 0, 0);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l0, n0, s0, 0, 0, 0);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l1, n1, s0, 0, 0, 0);
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(cur + aofs + (part * 16 + 2 * st) * 512);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(cur + aofs + (part * 16 + 2 * st + 2) * 512);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[st], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[st + 1], s1, 0, 0, 0);
           }
-        } else {
+      }
 #pragma unroll
-          for (int part = 0; part < NPART; ++part)
+      for (int e = 0; e < 16; ++e) {
+        const float v = kMinMax ? s0[e] : s0[e] + s1[e];
+        sc[e] = v != v ? -__builtin_inff() : v;
+      }
+    };
+    // every tile of the work-group's candidates through LDS (double-buffered,
+    // the next tile's loads in flight), `body(c, image)` on each
+    auto for_each_tile = [&](auto&& body) {
+      load_tile(0);
+      store_tile(tbuf);
+      __syncthreads();
+      for (int64_t c = 0; c < wg_tiles; ++c) {
+        char* cur = tbuf + (c & 1) * (kMu3TileElems * 2);
+        if (c + 1 < wg_tiles) load_tile(c + 1);
+        // the MFMAs run on the whole wave (wave-uniform branch)
+        if (__any(rank && c * kGateTile < ncand)) body(c, cur);
+        if (c + 1 < wg_tiles) store_tile(tbuf + ((c + 1) & 1) * (kMu3TileElems * 2));
+        __syncthreads();
+      }
+    };
+    auto is_cand = [&](int64_t c, int e) {
+      const int64_t i = c * kGateTile + 8 * (e >> 2) + 4 * lg + (e & 3);
+      return rank && i < ncand;
+    };
+
+    if constexpr (KCAP <= kGateOnePassMaxKcap) {
+      // one pass: each lane keeps its top-KCAP 64-bit keys (orderable score
+      // bits, then the complemented index, so equal scores rank the lower
+      // index higher); the partner's list is merged in and the m kept
+      // indices are emitted ascending
+      uint64_t ks[KCAP];
 #pragma unroll
-            for (int st = 0; st < 8; st += 2) {
-              const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(cur + aofs + (part * 16 + 2 * st) * 512);
-              const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(cur + aofs + (part * 16 + 2 * st + 2) * 512);
-              s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[st], s0, 0, 0, 0);
-              s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[st + 1], s1, 0, 0, 0);
-            }
-        }
+      for (int p = 0; p < KCAP; ++p) ks[p] = (p < KCAP - m) ? ~0ull : 0ull;
+      for_each_tile([&](int64_t c, const char* cur) {
+        float sc[16];
+        score_tile(cur, sc);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int64_t i = c * kGateTile + 8 * (e >> 2) + 4 * lg + (e & 3);
-          float sc = kMinMax ? s0[e] : s0[e] + s1[e];
-          if (sc != sc) sc = -__builtin_inff();  // NaN ranks lowest
-          const uint64_t key = ((uint64_t)orderable(sc) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
-          if (rank && i < ncand) topk_insert<KCAP>(ks, key);
+          const uint64_t key = ((uint64_t)orderable(sc[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
+          if (is_cand(c, e)) topk_insert<KCAP>(ks, key);
+        }
+      });
+      uint64_t pk_[KCAP];
+#pragma unroll
+      for (int p = 0; p < KCAP; ++p) {
+        uint32_t l0, l1, h0, h1;
+        pair_values_u((uint32_t)ks[p], l0, l1);
+        pair_values_u((uint32_t)(ks[p] >> 32), h0, h1);
+        pk_[p] = lg ? (((uint64_t)h0 << 32) | l0) : (((uint64_t)h1 << 32) | l1);
+      }
+#pragma unroll
+      for (int p = 0; p < KCAP; ++p)
+        if (rank && p >= KCAP - m) topk_insert<KCAP>(ks, pk_[p]);
+      if (rank && lg == 0) {
+        uint32_t idx[KCAP];
+#pragma unroll
+        for (int p = 0; p < KCAP; ++p)
+          idx[p] = (p >= KCAP - m) ? (0xffffffffu - (uint32_t)ks[p]) : 0xffffffffu;
+#pragma unroll
+        for (int pass = 0; pass < KCAP; ++pass) {
+#pragma unroll
+          for (int p = pass & 1; p + 1 < KCAP; p += 2) {
+            const uint32_t x = idx[p], y = idx[p + 1];
+            idx[p] = x < y ? x : y;
+            idx[p + 1] = x < y ? y : x;
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < KCAP; ++p) {
+          if (p < m) {
+            row[nout++] = (int32_t)idx[p];
+            if (a.hist) atomicAdd(&lhist[idx[p]], 1);
+          }
         }
       }
-      if (c + 1 < wg_tiles) store_tile(tbuf + ((c + 1) & 1) * (kMu3TileElems * 2));
-      __syncthreads();
+    } else {
+      // pass 1: the row's m-th largest score
+      float tv[KCAP];
+  #pragma unroll
+      for (int p = 0; p < KCAP; ++p) tv[p] = -__builtin_inff();
+      for_each_tile([&](int64_t c, const char* cur) {
+        float sc[16];
+        score_tile(cur, sc);
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) list_insert<KCAP>(tv, is_cand(c, e) ? sc[e] : -__builtin_inff());
+      });
+      {
+        // merge the partner lane's list (lane l ^ 32 holds the row's other half)
+        float pv[KCAP];
+  #pragma unroll
+        for (int p = 0; p < KCAP; ++p) {
+          float u, v;
+          pair_values_f(tv[p], u, v);
+          pv[p] = lg ? u : v;
+        }
+  #pragma unroll
+        for (int p = 0; p < KCAP; ++p) list_insert<KCAP>(tv, pv[p]);
+      }
+      float thr = tv[0];
+      int above = 0;
+  #pragma unroll
+      for (int p = 1; p < KCAP; ++p)
+        if (p < m) thr = tv[p];
+  #pragma unroll
+      for (int p = 0; p < KCAP; ++p)
+        if (p < m && tv[p] > thr) ++above;
+      int ties_left = m - above;  // blocks scoring exactly thr still to keep, lowest index first
+
+      // pass 2: the kept blocks, ascending
+      for_each_tile([&](int64_t c, const char* cur) {
+        float sc[16];
+        score_tile(cur, sc);
+        uint32_t gt = 0u, eq = 0u;
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const bool cand = is_cand(c, e);
+          gt |= (cand && sc[e] > thr) ? (1u << e) : 0u;
+          eq |= (cand && sc[e] == thr) ? (1u << e) : 0u;
+        }
+        // the row's 32-block masks of this tile, the same in both lanes
+        uint32_t gu, gw, eu, ew;
+        pair_values_u(spread_tile_bits(gt, lg), gu, gw);
+        pair_values_u(spread_tile_bits(eq, lg), eu, ew);
+        uint32_t keep = gu | gw;
+        uint32_t ties = eu | ew;
+        while (ties && ties_left > 0) {
+          const uint32_t b = ties & (0u - ties);
+          keep |= b;
+          ties ^= b;
+          --ties_left;
+        }
+        if (rank && lg == 0) {
+          while (keep) {
+            const int b = __builtin_ctz(keep);
+            keep &= keep - 1u;
+            const int32_t idx = (int32_t)(c * kGateTile + b);
+            row[nout++] = idx;
+            if (a.hist) atomicAdd(&lhist[idx], 1);
+          }
+        }
+      });
     }
-    // merge the two half-row lists: each lane takes a copy of its partner's
-    // list (lane l ^ 32), then inserts the partner's kept keys into its own
-    uint64_t pk_[KCAP];
-#pragma unroll
-    for (int p = 0; p < KCAP; ++p) {
-      const uint32_t klo = (uint32_t)ks[p], khi = (uint32_t)(ks[p] >> 32);
-      const auto xl = __builtin_amdgcn_permlane32_swap(klo, klo, false, false);
-      const auto xh = __builtin_amdgcn_permlane32_swap(khi, khi, false, false);
-      const uint32_t l0 = xl[0], l1 = xl[1], h0 = xh[0], h1 = xh[1];
-      pk_[p] = lg ? (((uint64_t)h0 << 32) | l0) : (((uint64_t)h1 << 32) | l1);
-    }
-#pragma unroll
-    for (int p = 0; p < KCAP; ++p)
-      if (rank && p >= KCAP - m) topk_insert<KCAP>(ks, pk_[p]);
   }
 
   if (valid && lg == 0) {
-    int32_t* row = a.sel + (int64_t)h * a.sel_stride_h + (t - a.sel_pos_base) * a.topk;
-    int c = 0;
-    if (rank) {
-      // the m kept blocks sit in ks[KCAP-m .. KCAP-1]; emit them ascending
-      uint32_t idx[KCAP];
-#pragma unroll
-      for (int p = 0; p < KCAP; ++p)
-        idx[p] = (p >= KCAP - m) ? (0xffffffffu - (uint32_t)ks[p]) : 0xffffffffu;
-#pragma unroll
-      for (int pass = 0; pass < KCAP; ++pass) {
-#pragma unroll
-        for (int p = pass & 1; p + 1 < KCAP; p += 2) {
-          const uint32_t x = idx[p], y = idx[p + 1];
-          idx[p] = x < y ? x : y;
-          idx[p + 1] = x < y ? y : x;
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < KCAP; ++p) {
-        if (p < m) {
-          row[c++] = (int32_t)idx[p];
-          if (a.hist) atomicAdd(&lhist[idx[p]], 1);
-        }
-      }
-    } else if ((int64_t)m >= ncand) {
+    int c = nout;
+    if (!rank && (int64_t)m >= ncand) {
       for (int64_t i = 0; i < ncand; ++i) {
         row[c++] = (int32_t)i;
         if (a.hist) atomicAdd(&lhist[i], 1);
