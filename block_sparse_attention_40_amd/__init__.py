@@ -11,7 +11,6 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     MAX_DECODE_GROUP,
     MAX_DECODE_TOPK,
-    MAX_SELECTIVE_TOPK,
     MobaError,
     decode_workspace_bytes,
     moba_decode_fwd,

@@ -18,7 +18,6 @@ LIB_PATH = os.path.join(_PKG, "libmoba.so")
 MOBA_OK = 0
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
-MAX_SELECTIVE_TOPK = 32
 NOALLOC_SCRATCH_BYTES = 512 << 20  # MOBA_NOALLOC_SCRATCH_BYTES
 
 _c_i64, _c_i32, _c_p, _c_sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t

@@ -21,6 +21,35 @@ namespace moba {
 
 constexpr int kMuSlice = 32;  // block means staged in LDS at a time
 
+// fp32 score of one block for one row: q (registers) against the block's
+// summary in LDS (D means, or D minima then D maxima); NaN ranks lowest.
+template <int D, bool kMinMax>
+__device__ __forceinline__ float gate_score(const float* qr, const float* mrow) {
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int d0 = 0; d0 < D; d0 += 4) {
+    const f32x4 mv = *reinterpret_cast<const f32x4*>(mrow + d0);
+    if constexpr (kMinMax) {
+      // term d: max(q_d lo_d, q_d hi_d), each product rounded once (a per-d
+      // select on the sign of q would keep 128 lane masks live across the
+      // block loop)
+      const f32x4 hv = *reinterpret_cast<const f32x4*>(mrow + D + d0);
+      s0 += __builtin_fmaxf(qr[d0 + 0] * mv[0], qr[d0 + 0] * hv[0]);
+      s1 += __builtin_fmaxf(qr[d0 + 1] * mv[1], qr[d0 + 1] * hv[1]);
+      s2 += __builtin_fmaxf(qr[d0 + 2] * mv[2], qr[d0 + 2] * hv[2]);
+      s3 += __builtin_fmaxf(qr[d0 + 3] * mv[3], qr[d0 + 3] * hv[3]);
+    } else {
+      s0 = __builtin_fmaf(qr[d0 + 0], mv[0], s0);
+      s1 = __builtin_fmaf(qr[d0 + 1], mv[1], s1);
+      s2 = __builtin_fmaf(qr[d0 + 2], mv[2], s2);
+      s3 = __builtin_fmaf(qr[d0 + 3], mv[3], s3);
+    }
+  }
+  float s = (s0 + s1) + (s2 + s3);
+  if (s != s) s = -__builtin_inff();
+  return s;
+}
+
 template <typename T, int D, int KCAP, bool kMinMax>
 __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
   // per block: D floats of the mean, or 2 D (min, then max) for min/max
@@ -73,29 +102,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
       if (rank) {
         const int64_t cend = ncand < c1 ? ncand : c1;
         for (int64_t i = c0; i < cend; ++i) {
-          const float* mrow = mu_s + (i - c0) * SD;
-          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-          for (int d0 = 0; d0 < D; d0 += 4) {
-            const f32x4 mv = *reinterpret_cast<const f32x4*>(mrow + d0);
-            if constexpr (kMinMax) {
-              // term d: max(q_d lo_d, q_d hi_d), each product rounded once
-              // (a per-d select on the sign of q would keep 128 lane masks
-              // live across the block loop)
-              const f32x4 hv = *reinterpret_cast<const f32x4*>(mrow + D + d0);
-              s0 += __builtin_fmaxf(qr[d0 + 0] * mv[0], qr[d0 + 0] * hv[0]);
-              s1 += __builtin_fmaxf(qr[d0 + 1] * mv[1], qr[d0 + 1] * hv[1]);
-              s2 += __builtin_fmaxf(qr[d0 + 2] * mv[2], qr[d0 + 2] * hv[2]);
-              s3 += __builtin_fmaxf(qr[d0 + 3] * mv[3], qr[d0 + 3] * hv[3]);
-            } else {
-              s0 = __builtin_fmaf(qr[d0 + 0], mv[0], s0);
-              s1 = __builtin_fmaf(qr[d0 + 1], mv[1], s1);
-              s2 = __builtin_fmaf(qr[d0 + 2], mv[2], s2);
-              s3 = __builtin_fmaf(qr[d0 + 3], mv[3], s3);
-            }
-          }
-          float s = (s0 + s1) + (s2 + s3);
-          if (s != s) s = -__builtin_inff();  // NaN ranks lowest
+          const float s = gate_score<D, kMinMax>(qr, mu_s + (i - c0) * SD);
           const uint64_t key = ((uint64_t)orderable(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
           if (key > ks[KCAP - 1]) {
             ks[KCAP - 1] = key;
@@ -306,6 +313,56 @@ __device__ __forceinline__ void list_insert(float* tv, float x) {
   tv[0] = __builtin_fmaxf(tv[0], x);
 }
 
+// Search for a row's m-th largest score T in rounds, for m beyond one list
+// of KCAP.  Before a round, `acc` scores are known to lie above `hi` and the
+// rest are not accounted for; the round lists the KCAP largest scores below
+// `hi` (descending, -inf padded) and counts `eqc` scores equal to `hi`.  Then
+// T is hi (when the acc + eqc scores at or above hi already reach m), or an
+// entry of the list (when the rest of m fits in it), or the next round starts
+// below the list's last entry.  `hi` falls strictly every round, so the
+// search ends; it takes about m / KCAP rounds.  `above` is the number of
+// scores above T.
+struct RoundState {
+  float hi;
+  int acc;
+  bool done;
+  float thr;
+  int above;
+};
+template <int KCAP>
+__device__ __forceinline__ void round_update(RoundState& st, const float* tv, int eqc, int m) {
+  if (st.done) return;
+  const int at_or_above = st.acc + eqc;
+  if (m <= at_or_above) {
+    st.thr = st.hi;
+    st.above = st.acc;
+    st.done = true;
+    return;
+  }
+  const int mp = m - at_or_above;  // still to find, below hi
+  if (mp <= KCAP) {
+    float thr = tv[0];
+#pragma unroll
+    for (int p = 1; p < KCAP; ++p)
+      if (p < mp) thr = tv[p];
+    int ab = at_or_above;
+#pragma unroll
+    for (int p = 0; p < KCAP; ++p)
+      if (p < mp && tv[p] > thr) ++ab;
+    st.thr = thr;
+    st.above = ab;
+    st.done = true;
+  } else {
+    const float hn = tv[KCAP - 1];
+    int ab = at_or_above;
+#pragma unroll
+    for (int p = 0; p < KCAP; ++p)
+      if (tv[p] > hn) ++ab;
+    st.acc = ab;
+    st.hi = hn;
+  }
+}
+
 // Bits e (0..15) of a lane half's 16 scores of a 32-block score tile, placed
 // at their block offsets inside the tile: score e of lane half lg is block
 // 8 (e >> 2) + 4 lg + (e & 3).
@@ -334,7 +391,7 @@ constexpr int kGateOnePassMaxKcap = 4;
 //      the same fp32 scores) and a row keeps every block scoring above T and,
 //      of those scoring exactly T, the lowest-index ones up to m: the tie
 //      rule.  The kept blocks come out tile by tile in ascending order.
-template <int KCAP, bool kMinMax>
+template <int KCAP, bool kMinMax, bool kRounds = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(KCAP <= 12 ? 4 : 1))) void gate_mfma_kernel(
     GateArgs a, const uint16_t* __restrict__ mu3) {
   constexpr int NPART = kMinMax ? 2 : 3;
@@ -504,36 +561,74 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(KCAP <= 12 
         }
       }
     } else {
-      // pass 1: the row's m-th largest score
-      float tv[KCAP];
-  #pragma unroll
-      for (int p = 0; p < KCAP; ++p) tv[p] = -__builtin_inff();
-      for_each_tile([&](int64_t c, const char* cur) {
-        float sc[16];
-        score_tile(cur, sc);
-  #pragma unroll
-        for (int e = 0; e < 16; ++e) list_insert<KCAP>(tv, is_cand(c, e) ? sc[e] : -__builtin_inff());
-      });
-      {
-        // merge the partner lane's list (lane l ^ 32 holds the row's other half)
-        float pv[KCAP];
-  #pragma unroll
-        for (int p = 0; p < KCAP; ++p) {
-          float u, v;
-          pair_values_f(tv[p], u, v);
-          pv[p] = lg ? u : v;
+      float thr;
+      int above;
+      if constexpr (!kRounds) {
+        // pass 1: the row's m-th largest score
+        float tv[KCAP];
+#pragma unroll
+        for (int p = 0; p < KCAP; ++p) tv[p] = -__builtin_inff();
+        for_each_tile([&](int64_t c, const char* cur) {
+          float sc[16];
+          score_tile(cur, sc);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) list_insert<KCAP>(tv, is_cand(c, e) ? sc[e] : -__builtin_inff());
+        });
+        {
+          // merge the partner lane's list (lane l ^ 32 holds the row's other half)
+          float pv[KCAP];
+#pragma unroll
+          for (int p = 0; p < KCAP; ++p) {
+            float u, v;
+            pair_values_f(tv[p], u, v);
+            pv[p] = lg ? u : v;
+          }
+#pragma unroll
+          for (int p = 0; p < KCAP; ++p) list_insert<KCAP>(tv, pv[p]);
         }
-  #pragma unroll
-        for (int p = 0; p < KCAP; ++p) list_insert<KCAP>(tv, pv[p]);
+        thr = tv[0];
+        above = 0;
+#pragma unroll
+        for (int p = 1; p < KCAP; ++p)
+          if (p < m) thr = tv[p];
+#pragma unroll
+        for (int p = 0; p < KCAP; ++p)
+          if (p < m && tv[p] > thr) ++above;
+      } else {
+        // m may exceed the list: rounds over the tiles (RoundState), the
+        // loop uniform over the work-group (each round streams the tiles)
+        RoundState rs{__builtin_inff(), 0, !rank, 0.f, 0};
+        while (__syncthreads_or(rs.done ? 0 : 1)) {
+          float tv[KCAP];
+#pragma unroll
+          for (int p = 0; p < KCAP; ++p) tv[p] = -__builtin_inff();
+          int eqc = 0;
+          for_each_tile([&](int64_t c, const char* cur) {
+            float sc[16];
+            score_tile(cur, sc);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const bool cd = !rs.done && is_cand(c, e);
+              list_insert<KCAP>(tv, (cd && sc[e] < rs.hi) ? sc[e] : -__builtin_inff());
+              eqc += (cd && sc[e] == rs.hi) ? 1 : 0;
+            }
+          });
+          float pv[KCAP];
+#pragma unroll
+          for (int p = 0; p < KCAP; ++p) {
+            float u, v;
+            pair_values_f(tv[p], u, v);
+            pv[p] = lg ? u : v;
+          }
+#pragma unroll
+          for (int p = 0; p < KCAP; ++p) list_insert<KCAP>(tv, pv[p]);
+          uint32_t e0, e1;
+          pair_values_u((uint32_t)eqc, e0, e1);
+          round_update<KCAP>(rs, tv, (int)(e0 + e1), m);
+        }
+        thr = rs.thr;
+        above = rs.above;
       }
-      float thr = tv[0];
-      int above = 0;
-  #pragma unroll
-      for (int p = 1; p < KCAP; ++p)
-        if (p < m) thr = tv[p];
-  #pragma unroll
-      for (int p = 0; p < KCAP; ++p)
-        if (p < m && tv[p] > thr) ++above;
       int ties_left = m - above;  // blocks scoring exactly thr still to keep, lowest index first
 
       // pass 2: the kept blocks, ascending
@@ -541,7 +636,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(KCAP <= 12 
         float sc[16];
         score_tile(cur, sc);
         uint32_t gt = 0u, eq = 0u;
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 16; ++e) {
           const bool cand = is_cand(c, e);
           gt |= (cand && sc[e] > thr) ? (1u << e) : 0u;
@@ -591,14 +686,125 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(KCAP <= 12 
   }
 }
 
+// VALU gate for a selective top-m beyond one register list (m > 32, any
+// input dtype): one row per thread as in gate_kernel, the block summaries
+// staged through LDS in slices.  The row's m-th largest score T is found in
+// rounds (RoundState: each round a pass over the row's blocks listing the 32
+// largest scores below the previous threshold and counting those equal to
+// it); a last pass keeps, in ascending block order, every block scoring above
+// T and the lowest-index blocks scoring exactly T up to m.  Every pass
+// computes the same fp32 scores (gate_score), so the passes agree.
+template <typename T, int D, bool kMinMax>
+__global__ __launch_bounds__(256) void gate_rounds_kernel(GateArgs a) {
+  constexpr int SD = kMinMax ? 2 * D : D;
+  constexpr int KCAP = 32;
+  extern __shared__ float smem[];
+  float* mu_s = smem;                                       // [kMuSlice][SD]
+  int* lhist = reinterpret_cast<int*>(smem + kMuSlice * SD);  // [n]
+  const int tid = threadIdx.x;
+  const int64_t w = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int64_t n = a.n;
+  const int g = a.g;
+
+  if (a.hist)
+    for (int64_t i = tid; i < n; i += 256) lhist[i] = 0;
+
+  const int64_t pic = w * a.gate_t + tid / g;  // position inside the chunk
+  const int h = hk * g + tid % g;
+  const bool valid = tid < a.gate_t * g && pic < a.cnt;
+  const int64_t t = a.t0 + (valid ? pic : 0);
+  const int64_t j = t / a.block;
+  const int64_t ncand = a.causal ? j : n;
+  const int m = (int)(a.causal ? (j < a.kp ? j : a.kp) : a.kp);
+  const bool rank = valid && m > 0 && (int64_t)m < ncand;
+
+  const int64_t last_pic = (w * a.gate_t + a.gate_t < a.cnt ? w * a.gate_t + a.gate_t : a.cnt) - 1;
+  const int64_t wg_cand = a.causal ? (a.t0 + last_pic) / a.block : n;
+
+  int32_t* row = a.sel + (int64_t)h * a.sel_stride_h + (t - a.sel_pos_base) * a.topk;
+  int nout = 0;
+
+  const int any_rank = __syncthreads_or(rank ? 1 : 0);
+  if (any_rank) {
+    float qr[D];
+    if (rank) {
+      const T* qp = reinterpret_cast<const T*>(a.q) + ((a.bb * a.seqlen + t) * a.hq + h) * (int64_t)D;
+#pragma unroll
+      for (int d0 = 0; d0 < D; d0 += 8) load8(qp + d0, qr + d0);
+    }
+    const float* mu_h = (kMinMax ? a.lohi : a.mu) + ((int64_t)a.bb * a.hkv + hk) * n * SD;
+    // one pass over the work-group's candidate blocks: body(i, score) for
+    // each candidate of each ranking row, in ascending i
+    auto scan = [&](auto&& body) {
+      for (int64_t c0 = 0; c0 < wg_cand; c0 += kMuSlice) {
+        const int64_t c1 = (c0 + kMuSlice < wg_cand) ? c0 + kMuSlice : wg_cand;
+        __syncthreads();
+        const int nel = (int)(c1 - c0) * SD;
+        for (int e = tid * 4; e < nel; e += 256 * 4)
+          *reinterpret_cast<f32x4*>(mu_s + e) = *reinterpret_cast<const f32x4*>(mu_h + c0 * SD + e);
+        __syncthreads();
+        if (rank) {
+          const int64_t cend = ncand < c1 ? ncand : c1;
+          for (int64_t i = c0; i < cend; ++i) body(i, gate_score<D, kMinMax>(qr, mu_s + (i - c0) * SD));
+        }
+      }
+    };
+    RoundState rs{__builtin_inff(), 0, !rank, 0.f, 0};
+    while (__syncthreads_or(rs.done ? 0 : 1)) {
+      float tv[KCAP];
+#pragma unroll
+      for (int p = 0; p < KCAP; ++p) tv[p] = -__builtin_inff();
+      int eqc = 0;
+      scan([&](int64_t, float x) {
+        if (!rs.done) {
+          list_insert<KCAP>(tv, x < rs.hi ? x : -__builtin_inff());
+          eqc += x == rs.hi ? 1 : 0;
+        }
+      });
+      round_update<KCAP>(rs, tv, eqc, m);
+    }
+    int ties_left = m - rs.above;  // blocks scoring exactly T still to keep, lowest index first
+    scan([&](int64_t i, float x) {
+      const bool tie = x == rs.thr && ties_left > 0;
+      if (x > rs.thr || tie) {
+        ties_left -= tie ? 1 : 0;
+        row[nout++] = (int32_t)i;
+        if (a.hist) atomicAdd(&lhist[i], 1);
+      }
+    });
+  }
+
+  if (valid) {
+    int c = nout;
+    if (!rank && (int64_t)m >= ncand) {
+      // no more candidates than slots: every candidate is chosen
+      for (int64_t i = 0; i < ncand; ++i) {
+        row[c++] = (int32_t)i;
+        if (a.hist) atomicAdd(&lhist[i], 1);
+      }
+    }
+    if (a.causal) row[c++] = (int32_t)j;  // the own block, always kept
+    for (; c < a.topk; ++c) row[c] = -1;
+  }
+
+  if (a.hist) {
+    __syncthreads();
+    int32_t* dst = a.hist + (int64_t)hk * n * a.gate_wg + w;  // [hkv, n, gate_wg]
+    for (int64_t i = tid; i < n; i += 256) dst[i * a.gate_wg] = lhist[i];
+  }
+}
+
 template <typename T, int D, bool kMinMax>
 static void launch_gate_kcap(const GateArgs& a, int kcap, size_t shmem, hipStream_t st, dim3 grid) {
   if (kcap <= 4)
     hipLaunchKernelGGL((gate_kernel<T, D, 4, kMinMax>), grid, dim3(256), shmem, st, a);
   else if (kcap <= 16)
     hipLaunchKernelGGL((gate_kernel<T, D, 16, kMinMax>), grid, dim3(256), shmem, st, a);
-  else
+  else if (kcap <= 32)
     hipLaunchKernelGGL((gate_kernel<T, D, 32, kMinMax>), grid, dim3(256), shmem, st, a);
+  else
+    hipLaunchKernelGGL((gate_rounds_kernel<T, D, kMinMax>), grid, dim3(256), shmem, st, a);
 }
 template <typename T, int D>
 static void launch_gate_valu(const GateArgs& a, int kcap, hipStream_t st, dim3 grid) {
@@ -619,8 +825,10 @@ static void launch_gate_mfma(const GateArgs& a, int kc, size_t sh, hipStream_t s
     hipLaunchKernelGGL((gate_mfma_kernel<12, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);
   else if (kc <= 16)
     hipLaunchKernelGGL((gate_mfma_kernel<16, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);
-  else
+  else if (kc <= 32)
     hipLaunchKernelGGL((gate_mfma_kernel<32, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);
+  else
+    hipLaunchKernelGGL((gate_mfma_kernel<32, kMinMax, true>), grid, dim3(512), sh, st, a, a.mu3);
 }
 
 int launch_mm_split(const float* lohi, int64_t batch, int64_t n, int hkv, uint16_t* mu3, hipStream_t st) {

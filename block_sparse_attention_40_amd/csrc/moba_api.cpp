@@ -151,7 +151,7 @@ const char* moba_status_string(int status) {
     case MOBA_ERR_DTYPE: return "unknown dtype";
     case MOBA_ERR_HEAD_DIM: return "head_dim not supported for this dtype (bf16: 128; fp32: 64 or 128)";
     case MOBA_ERR_SEQ_NOT_DIVISIBLE: return "seqlen is not a multiple of block_size";
-    case MOBA_ERR_TOPK: return "topk < 1, or a selective topk above MOBA_MAX_SELECTIVE_TOPK";
+    case MOBA_ERR_TOPK: return "topk < 1 (decode: also topk above its maximum)";
     case MOBA_ERR_GQA: return "num_q_heads is not a multiple of num_kv_heads, or the group exceeds 128";
     case MOBA_ERR_WORKSPACE: return "workspace is NULL or too small (forward: below moba_workspace_bytes_chunked(..., 1))";
     case MOBA_ERR_HIP: return "a HIP call or kernel launch failed";

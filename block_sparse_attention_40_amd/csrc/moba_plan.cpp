@@ -33,7 +33,6 @@ int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks, bool allow_imag
   // candidates the gate ranks: past blocks (at most n-1) or all n blocks
   const int64_t cand = s.causal ? q.n - 1 : q.n;
   q.selective = q.kp < cand;
-  if (q.selective && q.kp > MOBA_MAX_SELECTIVE_TOPK) return MOBA_ERR_TOPK;
 
   // index arithmetic bounds: the rows of one batch entry (positions x heads)
   // and row * slot products stay in int32 range; tested by division, before

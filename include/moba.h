@@ -56,7 +56,7 @@ enum moba_status {
   MOBA_ERR_DTYPE = -2,              /* unknown dtype */
   MOBA_ERR_HEAD_DIM = -3,           /* head_dim not supported for this dtype */
   MOBA_ERR_SEQ_NOT_DIVISIBLE = -4,  /* seqlen % block_size != 0 (no padding is defined) */
-  MOBA_ERR_TOPK = -5,               /* topk < 1, or a selective topk above the supported maximum */
+  MOBA_ERR_TOPK = -5,               /* topk < 1 (decode: also topk above its maximum) */
   MOBA_ERR_GQA = -6,                /* num_q_heads % num_kv_heads != 0 or group too large */
   MOBA_ERR_WORKSPACE = -7,          /* workspace NULL or smaller than the call accepts */
   MOBA_ERR_HIP = -8,                /* a HIP runtime call or kernel launch failed */
@@ -65,11 +65,6 @@ enum moba_status {
 };
 
 enum moba_dtype { MOBA_DTYPE_F32 = 0, MOBA_DTYPE_BF16 = 1 };
-
-/* Largest topk - 1 (causal) or topk (non-causal) for which the gate really has
- * to choose, i.e. when it is smaller than the number of candidate blocks.  A
- * topk that already covers every candidate block is always accepted. */
-#define MOBA_MAX_SELECTIVE_TOPK 32
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int moba_version(void);
@@ -132,7 +127,10 @@ int moba_plan_info(int64_t batch, int64_t seqlen, int32_t num_q_heads,
  *               moba_workspace_bytes_chunked(..., 1, ...) bytes (see "Query
  *               chunks" above; moba_workspace_bytes() gives the fastest
  *               plan); its contents on entry do not matter.
- * topk >= n is clamped to n (dense causal attention).  Returns a status.
+ * topk >= n is clamped to n (dense causal attention).  Any topk >= 1 is
+ * accepted: when more than 32 past blocks must be ranked (topk - 1 > 32, or
+ * topk > 32 non-causal) the gate finds the cut-off score in rounds, each a
+ * further pass over the row's blocks.  Returns a status.
  */
 int moba_attn_fwd(const void* q, const void* k, const void* v,
                   int64_t batch, int64_t seqlen, int32_t num_q_heads,

@@ -62,8 +62,10 @@ def ws(b=1, S=1024, Hq=4, Hkv=2, D=128, dt=BF16, B=128, k=3, causal=1):
     (dict(S=0), SHAPE),
     (dict(B=0), SHAPE),
     (dict(S=1 << 20, B=64), SHAPE),  # 16384 blocks: more than the gate's LDS counters
-    (dict(S=8192, B=64, k=40), TOPK),  # 127 past candidates, 39 to choose: above the maximum
+    (dict(S=8192, B=64, k=40), OK),  # 127 past candidates, 39 to choose: the gate ranks in rounds
     (dict(S=8192, B=64, k=33), OK),
+    (dict(S=8192, B=64, k=127), OK),  # 126 of 127 past candidates
+    (dict(S=8192, B=64, k=100, causal=0), OK),  # 100 of 128 blocks, non-causal
     (dict(S=8192, B=64, k=128), OK),  # every causal block: no ranking needed
     (dict(S=8192, B=64, k=500), OK),  # clamped
 ])

@@ -85,6 +85,8 @@ def test_minmaxpool_matches_oracle(dtype, b, S, Hkv, D, B):
     ("bf16", 2048, 4, 2, 128, 128, 3, True), ("bf16", 4096, 8, 1, 128, 64, 9, True),
     ("bf16", 2048, 2, 2, 128, 128, 20, True), ("bf16", 1024, 2, 1, 128, 64, 5, False),
     ("f32", 1024, 1, 1, 64, 128, 3, True), ("bf16", 4096, 2, 2, 128, 32, 33, True),
+    # more than 32 past blocks to rank: the cut-off score found in rounds
+    ("bf16", 4096, 2, 2, 128, 32, 60, True), ("f32", 2048, 2, 1, 64, 16, 90, False),
 ])
 def test_gate_matches_oracle(dtype, S, Hq, Hkv, D, B, topk, causal):
     w = small("gate", dtype, 1, S, Hq, Hkv, D, B, topk, causal, seed=11)
@@ -141,6 +143,12 @@ SMALL = [
     small("gate_noncausal_n40", "bf16", 1, 2560, 2, 1, 128, 64, 6, causal=False),
     small("f32_d128_gqa", "f32", 1, 1024, 4, 2, 128, 128, 3),
     small("f32_noncausal", "f32", 1, 512, 2, 1, 64, 64, 3, causal=False),
+    # more than 32 past blocks to rank (the gate's rounds): 2 and 4 rounds on
+    # the MFMA gate, non-causal, and the fp32 VALU gate
+    small("topk50_rounds", "bf16", 1, 8192, 4, 2, 128, 64, 50),
+    small("topk100_rounds_b32", "bf16", 1, 8192, 2, 1, 128, 32, 100),
+    small("noncausal_topk70", "bf16", 1, 4096, 2, 2, 128, 32, 70, causal=False),
+    small("f32_topk40_rounds", "f32", 1, 2048, 2, 1, 64, 32, 40),
 ]
 
 
@@ -212,12 +220,60 @@ SMALL_MINMAX = [
     small("mm_f32_d128_gqa", "f32", 1, 1024, 4, 2, 128, 128, 3),
     small("mm_f32_d64_k20", "f32", 1, 2048, 2, 1, 64, 32, 20),
     small("mm_f32_noncausal", "f32", 1, 512, 2, 1, 64, 64, 3, causal=False),
+    small("mm_topk45_rounds", "bf16", 1, 4096, 2, 1, 128, 32, 45),
+    small("mm_f32_topk36_rounds", "f32", 1, 2048, 2, 1, 64, 32, 36),
 ]
 
 
 @pytest.mark.parametrize("w", SMALL_MINMAX, ids=[w.name for w in SMALL_MINMAX])
 def test_forward_minmax_small(w):
     run(w, gate="minmax")
+
+
+TIE_CASES = [(dtype, topk, gate) for dtype in ("bf16", "f32") for topk in (3, 9, 13, 20, 50)
+             for gate in ("mean", "minmax")]
+
+
+@pytest.mark.parametrize("dtype,topk,gate", TIE_CASES)
+def test_forward_exact_ties_go_to_lower_index(dtype, topk, gate):
+    """Key blocks repeat with period 4 (block i is a copy of block i % 4), so
+    a row's block scores take four values and most rows have exact ties at
+    the cut-off: equal blocks get bit-identical summaries and scores on both
+    sides, and the report's tie rule (section 2.3: the lower block index
+    wins) fixes the selection.  Every row whose oracle gap is exactly 0 must
+    match the oracle's selection; only rows with a non-zero gap below the
+    near-tie threshold may differ.  Covers each gate list capacity (one pass,
+    two passes, rounds) on 128 blocks (four 32-block score tiles)."""
+    D = 128 if dtype == "bf16" else 64
+    w = small(f"ties_{dtype}_k{topk}", dtype, 1, 4096, 2, 1, D, 32, topk, seed=43)
+    say(f"[case] exact ties {w} gate={gate}")
+    q, k, v, _ = W.make_inputs(w, device="cpu")
+    B = w.block_size
+    for i in range(4, w.num_blocks):
+        k[:, i * B:(i + 1) * B] = k[:, (i % 4) * B:(i % 4 + 1) * B]
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, sel = M.moba_attn_fwd(q, k, v, B, topk, True, gate=gate)
+    torch.cuda.synchronize()
+    from parity_utils import RowSource
+    rows = [(0, t, h) for h in range(w.num_q_heads) for t in range(w.seqlen)]
+    k32 = to_np32(k)
+    mm = O.block_minmax(k32, B) if gate == "minmax" else None
+    res = O.moba_rows(RowSource(q.cpu()), k32, to_np32(v), B, topk, True, rows, keep_scores=True, gate=gate,
+                      minmax=mm)
+    selh = sel.cpu().numpy()
+    ties = O.near_tie_rows(res)
+    exact = 0
+    for r, (bb, t, h) in enumerate(rows):
+        same = np.array_equal(selh[bb, h, t], res.sel[r])
+        if res.gap[r] == 0:
+            exact += 1
+            assert same, f"exact tie row {(bb, t, h)}: gpu {selh[bb, h, t].tolist()} oracle {res.sel[r].tolist()}"
+        elif not same:
+            assert ties[r], f"row {(bb, t, h)}: selection differs, gap {res.gap[r]}"
+    say(f"[ties] {exact} rows with an exact tie at the cut-off of {len(rows)}")
+    assert exact > len(rows) // 4
+    rep = compare(q, k, v, out, sel, B, topk, True, tol=TOL[dtype], gate=gate)
+    say(f"[parity] {w.name}: {rep.as_dict()}")
 
 
 def test_forward_minmax_gqa32x8_32k_sampled():
