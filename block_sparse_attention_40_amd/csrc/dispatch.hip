@@ -86,76 +86,94 @@ __global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restri
   }
 }
 
-__global__ __launch_bounds__(256) void scatter_kernel(DispatchArgs a) {
-  extern __shared__ int32_t lcnt[];  // [n]
-  const int tid = threadIdx.x;
-  const int64_t w = blockIdx.x;
-  const int hk = blockIdx.y;
-  const int64_t n = a.n;
-  for (int64_t i = tid; i < n; i += 256) lcnt[i] = 0;
-  __syncthreads();
-  const int g = a.g;
-  const int64_t pic = w * a.gate_t + tid / g;
-  const int h = hk * g + tid % g;
-  const bool valid = tid < a.gate_t * g && pic < a.cnt;
-  if (!valid) return;
-  const int64_t t = a.t0 + pic;
-  const int64_t j = t / a.block;
-  const int32_t* row = a.sel + (int64_t)h * a.sel_stride_h + (t - a.sel_pos_base) * a.topk;
-  const int32_t* wstart = a.hist + (int64_t)hk * n * a.gate_wg + w;  // list i: wstart[i * gate_wg]
-  const int64_t local_row = pic * a.hq + h;
+// The (row, slot) entries of one gate work-group's rows: each row's s-th
+// valid past block (ascending in its selection) is slot s.  Entries that can
+// never be a valid choice (a block beyond the sequence, or after the own
+// block) are skipped, so a malformed selection given to the backward stays
+// inside the lists; the own block is handled by the own-block kernel.
+// body(i, slot) is called for each remaining entry of a valid row.
+template <typename Body>
+__device__ __forceinline__ void for_each_past_entry(const DispatchArgs& a, const int32_t* row, int64_t j,
+                                                    Body&& body) {
   int slot = 0;
   for (int c = 0; c < a.topk && slot < a.kp; ++c) {
     const int32_t i = row[c];
     if (i < 0) break;
-    // never a valid choice (a block beyond the sequence, or after the own
-    // block): skipped, so a malformed selection given to the backward stays
-    // inside the lists
-    if (i >= n || (a.causal && i > j)) continue;
-    if (a.causal && i == j) continue;  // own block: handled by the own-block kernel
-    const int32_t r = atomicAdd(&lcnt[i], 1);
-    const int64_t L = (int64_t)hk * n + i;
-    a.entries[a.listoff[L] + wstart[(int64_t)i * a.gate_wg] + r] = (int32_t)(local_row * a.kp + slot);
+    if (i >= a.n || (a.causal && i > j)) continue;
+    if (a.causal && i == j) continue;
+    body(i, slot);
     ++slot;
+  }
+}
+
+// Blocks are counted in ranges of kDispatchRange (the LDS counters), one pass
+// over the rows' selection per range; below that many blocks, one pass.
+__global__ __launch_bounds__(256) void scatter_kernel(DispatchArgs a) {
+  extern __shared__ int32_t lcnt[];  // [min(n, kDispatchRange)]
+  const int tid = threadIdx.x;
+  const int64_t w = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int64_t n = a.n;
+  const int g = a.g;
+  const int64_t pic = w * a.gate_t + tid / g;
+  const int h = hk * g + tid % g;
+  const bool valid = tid < a.gate_t * g && pic < a.cnt;
+  const int64_t t = a.t0 + (valid ? pic : 0);
+  const int64_t j = t / a.block;
+  const int32_t* row = a.sel + (int64_t)h * a.sel_stride_h + (t - a.sel_pos_base) * a.topk;
+  const int32_t* wstart = a.hist + (int64_t)hk * n * a.gate_wg + w;  // list i: wstart[i * gate_wg]
+  const int64_t local_row = pic * a.hq + h;
+  for (int64_t r0 = 0; r0 < n; r0 += kDispatchRange) {
+    const int64_t len = n - r0 < kDispatchRange ? n - r0 : kDispatchRange;
+    for (int64_t i = tid; i < len; i += 256) lcnt[i] = 0;
+    __syncthreads();
+    if (valid)
+      for_each_past_entry(a, row, j, [&](int32_t i, int slot) {
+        if (i < r0 || i >= r0 + len) return;
+        const int32_t r = atomicAdd(&lcnt[i - r0], 1);
+        const int64_t L = (int64_t)hk * n + i;
+        a.entries[a.listoff[L] + wstart[(int64_t)i * a.gate_wg] + r] = (int32_t)(local_row * a.kp + slot);
+      });
+    __syncthreads();  // the next range clears the counters
   }
 }
 
 // Counts per (list, gate work-group) from the selection alone: the same rows
 // per work-group as the gate and the scatter, written contiguous per list.
 __global__ __launch_bounds__(256) void hist_kernel(DispatchArgs a) {
-  extern __shared__ int32_t lcnt[];  // [n]
+  extern __shared__ int32_t lcnt[];  // [min(n, kDispatchRange)]
   const int tid = threadIdx.x;
   const int64_t w = blockIdx.x;
   const int hk = blockIdx.y;
   const int64_t n = a.n;
-  for (int64_t i = tid; i < n; i += 256) lcnt[i] = 0;
-  __syncthreads();
   const int g = a.g;
   const int64_t pic = w * a.gate_t + tid / g;
   const int h = hk * g + tid % g;
   const bool valid = tid < a.gate_t * g && pic < a.cnt;
-  if (valid) {
-    const int64_t t = a.t0 + pic;
-    const int64_t j = t / a.block;
-    const int32_t* row = a.sel + (int64_t)h * a.sel_stride_h + (t - a.sel_pos_base) * a.topk;
-    int slot = 0;
-    for (int c = 0; c < a.topk && slot < a.kp; ++c) {
-      const int32_t i = row[c];
-      if (i < 0) break;
-      if (i >= n || (a.causal && i > j)) continue;  // never a valid choice (as in scatter_kernel)
-      if (a.causal && i == j) continue;
-      atomicAdd(&lcnt[i], 1);
-      ++slot;
-    }
-  }
-  __syncthreads();
+  const int64_t t = a.t0 + (valid ? pic : 0);
+  const int64_t j = t / a.block;
+  const int32_t* row = a.sel + (int64_t)h * a.sel_stride_h + (t - a.sel_pos_base) * a.topk;
   int32_t* dst = a.hist + (int64_t)hk * n * a.gate_wg + w;
-  for (int64_t i = tid; i < n; i += 256) dst[i * a.gate_wg] = lcnt[i];
+  for (int64_t r0 = 0; r0 < n; r0 += kDispatchRange) {
+    const int64_t len = n - r0 < kDispatchRange ? n - r0 : kDispatchRange;
+    for (int64_t i = tid; i < len; i += 256) lcnt[i] = 0;
+    __syncthreads();
+    if (valid)
+      for_each_past_entry(a, row, j, [&](int32_t i, int) {
+        if (i >= r0 && i < r0 + len) atomicAdd(&lcnt[i - r0], 1);
+      });
+    __syncthreads();
+    for (int64_t i = tid; i < len; i += 256) dst[(r0 + i) * a.gate_wg] = lcnt[i];
+    __syncthreads();  // the next range clears the counters
+  }
+}
+
+static size_t range_lds(const DispatchArgs& a) {
+  return (size_t)(a.n < kDispatchRange ? a.n : kDispatchRange) * sizeof(int32_t);
 }
 
 int launch_dispatch_from_sel(const DispatchArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)a.gate_wg, (unsigned)a.hkv), dim3(256), (size_t)a.n * sizeof(int32_t),
-                     st, a);
+  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)a.gate_wg, (unsigned)a.hkv), dim3(256), range_lds(a), st, a);
   if (hipGetLastError() != hipSuccess) return -1;
   return launch_dispatch(a, st);
 }
@@ -165,8 +183,8 @@ int launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(list_scan_kernel, dim3((unsigned)lists), dim3(1024), 0, st, a.hist, a.count, a.gate_wg);
   hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, st, a.count, a.listoff, a.tiles, lists,
                      a.tile_rows);
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)a.gate_wg, (unsigned)a.hkv), dim3(256),
-                     (size_t)a.n * sizeof(int32_t), st, a);
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)a.gate_wg, (unsigned)a.hkv), dim3(256), range_lds(a), st,
+                     a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

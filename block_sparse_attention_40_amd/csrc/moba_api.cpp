@@ -290,10 +290,13 @@ int fwd_impl(const void* q, const void* k, const void* v, int64_t batch, int64_t
         sel_pos_base = t0;
       }
       const bool need_lists = bf16 && p.kp > 0;
+      // the gate counts rows per block in LDS up to kDispatchRange blocks;
+      // beyond, the dispatch counts them from the selection
+      const bool gate_counts = need_lists && p.n <= kDispatchRange;
 
       GateArgs ga{};
       ga.q = q; ga.mu = mu; ga.lohi = lohi; ga.minmax = minmax ? 1 : 0; ga.mu3 = mu3; ga.sel = sel_base; ga.sel_stride_h = sel_stride_h; ga.sel_pos_base = sel_pos_base;
-      ga.hist = need_lists ? hist : nullptr;
+      ga.hist = gate_counts ? hist : nullptr;
       ga.seqlen = seqlen; ga.n = p.n; ga.t0 = t0; ga.cnt = cnt; ga.gate_wg = gate_wg;
       ga.hq = num_q_heads; ga.hkv = num_kv_heads; ga.block = block_size; ga.topk = topk; ga.kp = p.kp;
       ga.causal = causal ? 1 : 0; ga.g = p.g; ga.gate_t = p.gate_t; ga.bb = (int32_t)bb;
@@ -328,7 +331,7 @@ int fwd_impl(const void* q, const void* k, const void* v, int64_t batch, int64_t
         da.causal = causal ? 1 : 0; da.g = p.g; da.gate_t = p.gate_t; da.tile_rows = p.tile_rows;
         {
           StageScope sc(MOBA_STAGE_DISPATCH, s, (double)cnt * num_q_heads * topk * 4.0 + past_rows * 4.0);
-          if (launch_dispatch(da, s)) return MOBA_ERR_HIP;
+          if ((gate_counts ? launch_dispatch(da, s) : launch_dispatch_from_sel(da, s)) != 0) return MOBA_ERR_HIP;
         }
 
         PastArgs pa{};

@@ -25,8 +25,8 @@ int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks, bool allow_imag
   Plan q{};
   q.s = s;
   q.n = s.seqlen / s.block;
-  // per-block counters live in LDS (32 KiB at most); grid z carries the batch
-  if (q.n > 8192 || s.batch > 65535) return MOBA_ERR_SHAPE;
+  // grid z carries the batch
+  if (s.batch > 65535) return MOBA_ERR_SHAPE;
   q.keff = (int32_t)std::min<int64_t>(s.topk, q.n);
   q.kp = s.causal ? q.keff - 1 : q.keff;
   q.g = s.hq / s.hkv;
@@ -50,6 +50,14 @@ int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks, bool allow_imag
   } else {
     q.chunk_blocks = (int64_t)std::max<uint64_t>(1, kPartialCapBytes / per_block_partial);
     q.chunk_blocks = std::min<int64_t>(q.chunk_blocks, q.n);
+  }
+  {
+    // the count table: KV heads x blocks x ceil(chunk positions / gate_t)
+    // int32 entries, kept within kHistCapBytes (one block per chunk at least)
+    const uint64_t per_wg = (uint64_t)s.hkv * (uint64_t)q.n * sizeof(int32_t);
+    const uint64_t max_wg = kHistCapBytes / per_wg;
+    const int64_t cb = (int64_t)(max_wg * (uint64_t)q.gate_t / (uint64_t)s.block);
+    q.chunk_blocks = std::max<int64_t>(1, std::min<int64_t>(q.chunk_blocks, cb));
   }
   if (max_chunk_blocks < 0) return MOBA_ERR_SHAPE;
   if (max_chunk_blocks > 0) q.chunk_blocks = std::min<int64_t>(q.chunk_blocks, max_chunk_blocks);

@@ -30,6 +30,14 @@ constexpr int64_t kOwnImageMinBlock = 1024;
 constexpr int kSliceKeys = 64;
 // Upper bound on the partial-result buffer of one query chunk (bf16 o + fp32 lse).
 constexpr uint64_t kPartialCapBytes = 8ull << 30;
+// Per-block row counters that one dispatch pass keeps in LDS (32 KiB); with
+// more blocks the gate leaves the counting to the dispatch, which makes one
+// pass over the selection per range of this many blocks.
+constexpr int64_t kDispatchRange = 8192;
+// Upper bound on the per-(list, gate work-group) count table of one chunk
+// (KV heads x blocks x gate work-groups, int32): it grows with the chunk times
+// the number of blocks, so many-block shapes take shorter chunks.
+constexpr uint64_t kHistCapBytes = 2ull << 30;
 
 struct Shape {
   int64_t batch, seqlen;

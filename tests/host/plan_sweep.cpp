@@ -54,6 +54,11 @@ static void check_plan(const Shape& s, const Plan& p, const char* d) {
         d);
   CHECK(p.max_tiles % 8 == 0 && p.max_tiles >= (p.max_pairs + p.tile_rows - 1) / p.tile_rows, "%s max_tiles", d);
   CHECK(p.gate_wg >= 1, "%s gate_wg", d);
+  // the per-(list, gate work-group) count table fits its region and its cap
+  const uint64_t table = (uint64_t)s.hkv * (uint64_t)p.gate_wg * (uint64_t)p.n * 4;
+  CHECK(p.off_count - p.off_hist >= table, "%s count table region", d);
+  CHECK(table <= kHistCapBytes || p.chunk_blocks == 1, "%s count table %llu above the cap", d,
+        (unsigned long long)table);
   check_offsets({p.off_mu, p.off_sel, p.off_hist, p.off_count, p.off_listoff, p.off_tiles, p.off_entries,
                  p.off_part_o, p.off_part_lse, p.off_kimg, p.off_vimg, p.off_mu3, p.off_lohi},
                 p.total, "fwd", d);

@@ -61,7 +61,8 @@ def ws(b=1, S=1024, Hq=4, Hkv=2, D=128, dt=BF16, B=128, k=3, causal=1):
     (dict(b=0), SHAPE),
     (dict(S=0), SHAPE),
     (dict(B=0), SHAPE),
-    (dict(S=1 << 20, B=64), SHAPE),  # 16384 blocks: more than the gate's LDS counters
+    (dict(S=1 << 20, B=64), OK),  # 16384 blocks: the dispatch counts them in two ranges
+    (dict(S=1 << 20, B=1), OK),  # a block per key
     (dict(S=8192, B=64, k=40), OK),  # 127 past candidates, 39 to choose: the gate ranks in rounds
     (dict(S=8192, B=64, k=33), OK),
     (dict(S=8192, B=64, k=127), OK),  # 126 of 127 past candidates
@@ -216,6 +217,30 @@ def plan_of(wsb, b=1, S=1 << 20, Hq=32, Hkv=8, D=128, dt=BF16, B=4096, k=12, cau
 def chunk_for(wsb, **kw):
     st, cb, _, _ = plan_of(wsb, **kw)
     return st, cb
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,B,k", [
+    (1 << 20, 32, 8, 16, 3),      # 65536 blocks, short partials: the count table sets the chunk
+    (1 << 20, 32, 32, 4, 12),     # 262144 blocks
+    (1 << 20, 32, 8, 4096, 12),   # the 1M workload: unchanged, 22 blocks per chunk
+    (131072, 2, 2, 16, 4),        # 8192 blocks, one chunk
+])
+def test_many_blocks_cut_chunks_to_the_count_table_cap(S, Hq, Hkv, B, k):
+    """The per-(list, gate work-group) count table (KV heads x blocks x gate
+    work-groups of the chunk, int32) stays within 2 GiB: with many blocks the
+    chunk is shortened for it, and shapes that fit keep their chunk."""
+    st, wsb = ws(S=S, Hq=Hq, Hkv=Hkv, B=B, k=k)
+    assert st == OK
+    st, cb, _, _ = plan_of(wsb, S=S, Hq=Hq, Hkv=Hkv, B=B, k=k)
+    assert st == OK and cb >= 1
+    n = S // B
+    gate_t = max(1, 256 // (Hq // Hkv))
+    table = Hkv * n * (-(-cb * B // gate_t)) * 4
+    assert table <= 2 << 30 or cb == 1
+    per_block_partial = B * Hq * (k - 1) * 260
+    cb_partials = min(n, max(1, (8 << 30) // per_block_partial))
+    if Hkv * n * (-(-cb_partials * B // gate_t)) * 4 <= (2 << 30) - Hkv * n * 4:
+        assert cb == cb_partials
 
 
 def test_query_chunks_follow_the_workspace():

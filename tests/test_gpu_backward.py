@@ -205,3 +205,43 @@ def test_backward_workload_128k_sampled_dq():
     check("dq (sampled rows)", got, rq)
     assert float(np.abs(gl - rl).max()) < 2.5e-3
     assert torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all()
+
+
+def test_backward_many_blocks_sampled():
+    """The backward beyond 8192 blocks (8320 blocks of 64 keys, 532K
+    positions, 2/1 heads, top-3): the dispatch counts its row lists per range
+    of 8192 blocks.  dq of sampled rows (the oracle's own selection, near ties
+    skipped) and dk, dv of sampled keys (the last eight of blocks 100 and 8300,
+    the GPU's selection, the attending rows' statistics from the oracle)."""
+    from parity_utils import RowSource
+    w = small("bwd_n8320", 1, 8320 * 64, 2, 1, 64, 3, seed=87)
+    say(f"[case] backward many blocks {w}")
+    q, k, v, _ = W.make_inputs(w, device=DEV)
+    do = dout_for(w, DEV)
+    out, sel, lse = M.moba_attn_fwd_train(q, k, v, w.block_size, w.topk, w.causal)
+    dq, dk, dv = M.moba_attn_bwd(q, k, v, out, do, lse, sel, w.block_size, w.topk, w.causal)
+    torch.cuda.synchronize()
+    B, g = w.block_size, w.num_q_heads // w.num_kv_heads
+    qh, kh, vh, doh = RowSource(q.cpu()), RowSource(k.cpu()), RowSource(v.cpu()), RowSource(do.cpu())
+    selh = sel.cpu().numpy()
+    rng = np.random.default_rng(88)
+    pos = [0, B, 8192 * B - 1, 8192 * B, w.seqlen - 1] + [int(t) for t in rng.integers(0, w.seqlen, 11)]
+    rows = [(0, t, h) for t in pos for h in range(w.num_q_heads)]
+    res = O.moba_rows(qh, kh, vh, B, w.topk, w.causal, rows, keep_scores=True)
+    ties = O.near_tie_rows(res)
+    keep = []
+    for r, (bb, t, h) in enumerate(rows):
+        if np.array_equal(selh[bb, h, t], res.sel[r]):
+            keep.append(r)
+        else:
+            assert ties[r], f"row {rows[r]}: selection differs and is not a near tie"
+    kr = [rows[r] for r in keep]
+    rq, _ = O.backward_dq_rows(qh, kh, vh, doh, B, w.causal, kr, [res.sel[r] for r in keep])
+    check("dq (sampled rows)", np.stack([to_np32(dq[bb, t, h]) for (bb, t, h) in kr]).astype(np.float64), rq)
+    keys = [(0, i * B + B - 8 + x, 0) for i in (100, 8300) for x in range(8)]
+    arows = sorted({r for (bb, s_, hk) in keys for r in O.attending_rows(selh, B, w.causal, bb, s_, hk, g)})
+    say(f"[bwd many blocks] {len(kr)} dq rows, {len(keys)} keys, {len(arows)} attending rows")
+    row_stats = O.backward_row_stats(qh, kh, vh, doh, B, w.causal, arows, [selh[r[0], r[2], r[1]] for r in arows])
+    rk, rv = O.backward_dkdv_keys(qh, kh, vh, doh, B, w.causal, keys, selh, row_stats=row_stats)
+    check("dk (sampled keys)", np.stack([to_np32(dk[bb, s_, hk]) for (bb, s_, hk) in keys]), rk)
+    check("dv (sampled keys)", np.stack([to_np32(dv[bb, s_, hk]) for (bb, s_, hk) in keys]), rv)

@@ -487,11 +487,35 @@ def test_forward_granularity_extremes_32k_sampled(n):
 
 
 def test_forward_max_blocks_sampled():
-    """The largest block count the plan accepts (8192 blocks of 16 keys,
-    128K positions): the gate's per-block counters fill 32 KiB of LDS and the
-    top list ranks up to 8191 candidates."""
+    """The largest block count whose rows the gate counts itself (8192
+    blocks of 16 keys, 128K positions): the per-block counters fill 32 KiB of
+    LDS and the top list ranks up to 8191 candidates."""
     w = small("n8192", "bf16", 1, 131072, 2, 2, 128, 16, 4, seed=77)
     rng = np.random.default_rng(3)
     rows = [(0, int(t), h) for h in range(2) for t in rng.integers(0, 131072, 24)] + \
            [(0, t, 1) for t in (0, 15, 16, 131071)]
     run(w, rows=rows, device_inputs=True)
+
+
+MANY_BLOCKS = [
+    (small("n16384_b4", "bf16", 1, 65536, 2, 1, 128, 4, 8, seed=81), "mean"),
+    # 20010 blocks: a ragged last dispatch range and a ragged last score tile
+    (small("n20010_b4_gqa", "bf16", 1, 80040, 4, 2, 128, 4, 6, seed=82), "mean"),
+    (small("n16384_minmax", "bf16", 1, 65536, 2, 1, 128, 4, 5, seed=83), "minmax"),
+    (small("n16384_noncausal", "bf16", 1, 65536, 2, 2, 128, 4, 5, causal=False, seed=84), "mean"),
+    (small("n16384_f32", "f32", 1, 65536, 2, 1, 64, 4, 5, seed=85), "mean"),
+]
+
+
+@pytest.mark.parametrize("w,gate", MANY_BLOCKS, ids=[w.name for w, _ in MANY_BLOCKS])
+def test_forward_many_blocks_sampled(w, gate):
+    """More blocks than one pass of LDS counters holds (16384 and 20010
+    blocks of 4 keys): the gate leaves the counting to the dispatch, which
+    counts and ranks the rows per range of 8192 blocks; sampled rows across
+    the sequence, the range boundary (block 8192) included."""
+    rng = np.random.default_rng(w.seed)
+    B = w.block_size
+    edges = (0, B - 1, B, 8191 * B, 8192 * B - 1, 8192 * B, 8193 * B + 1, w.seqlen - 1)
+    rows = [(0, int(t), h) for h in range(w.num_q_heads) for t in rng.integers(0, w.seqlen, 48)] + \
+           [(0, t, h) for h in range(w.num_q_heads) for t in edges]
+    run(w, rows=rows, device_inputs=True, gate=gate)
