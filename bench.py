@@ -319,6 +319,12 @@ VALU_COUNTERS = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_B
 VALU_CMD = ("rocprofv3 --pmc " + VALU_COUNTERS + " --output-format csv -d gpurun_out/pmc_valu -o run -- "
             "python3 -u bench.py --steps 1 --warmup 0 --secondary '' --no-cpu-baseline --no-gemm-reference "
             "> gpurun_out/pmc_valu.json")
+# the backward on its benchmark configuration (a training step: the forward
+# with lse, then the backward)
+BWD_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_bwd -o run -- "
+                 "python3 -u bench.py --backward gqa32x8_128k --steps 3 --warmup 1 > gpurun_out/trace_bwd.json")
+BWD_PMC_CMD = ("rocprofv3 --pmc {counters} --output-format csv -d gpurun_out/pmcbwd_{tag} -o run -- "
+               "python3 -u bench.py --backward gqa32x8_128k --steps 1 --warmup 0 > gpurun_out/pmcbwd_{tag}.json")
 PROFILE_CMDS = {
     "gqa32x8_1m": {"title": "gqa32x8_1m workload (1M tokens, 32/8 heads, D 128, block 4096, top-12)",
                    "fetch": PMC_CMD.format(counter="FETCH_SIZE"), "write": PMC_CMD.format(counter="WRITE_SIZE"),
@@ -329,11 +335,21 @@ PROFILE_CMDS = {
                          "mfma": PMC32_CMD.format(counters="SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
                                                   tag="mfma"),
                          "valu": PMC32_CMD.format(counters=VALU_COUNTERS, tag="valu")},
+    "bwd_gqa32x8_128k": {"title": "gqa32x8_128k workload (128K tokens, 32/8 heads, D 128, block 4096, top-12)",
+                         "pass": "training step (forward with lse, then backward)",
+                         "calls": "forward-with-lse and backward calls",
+                         "mfma": BWD_PMC_CMD.format(counters="SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+                                                    tag="mfma"),
+                         "valu": BWD_PMC_CMD.format(counters=VALU_COUNTERS, tag="valu")},
 }
 
 
 def _workload_of(bench_json):
-    return json.loads(open(bench_json).read().strip().splitlines()[-1])["config"]["workload"]
+    """The profile key of a bench.py run: its workload, prefixed with bwd_ for
+    a --backward run."""
+    line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    wl = line["config"]["workload"]
+    return "bwd_" + wl if "backward" in line["metric"] else wl
 
 
 def _counter_rows(d):
@@ -381,9 +397,10 @@ def summarize_mfma(pmc_dir, bench_json):
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         d["disp"].add(r["Dispatch_Id"])
         d["t"][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
-    out = [f"# MFMA busy: MoBA forward, {cmds['title']}",
+    out = [f"# MFMA busy: MoBA {cmds.get('pass', 'forward')}, {cmds['title']}",
            "", "Command (run from the repository root on one MI355X):", "", "```", cmds["mfma"], "```", "",
-           f"Counters summed over the dispatches of the run's forward calls; {simds} SIMDs, {xcc} XCDs. "
+           f"Counters summed over the dispatches of the run's {cmds.get('calls', 'forward calls')}; {simds} SIMDs, "
+           f"{xcc} XCDs. "
            "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs); clock = "
            "(GRBM_GUI_ACTIVE / XCDs) / kernel time.", "",
            "| Kernel | Dispatches | Kernel ms (sum) | MFMA busy | Clock GHz |", "|---|---|---|---|---|"]
@@ -422,9 +439,10 @@ def summarize_valu(pmc_dir, bench_json):
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         d["disp"].add(r["Dispatch_Id"])
         d["t"][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
-    out = [f"# VALU and MFMA issue: MoBA forward, {cmds['title']}",
+    out = [f"# VALU and MFMA issue: MoBA {cmds.get('pass', 'forward')}, {cmds['title']}",
            "", "Command (run from the repository root on one MI355X):", "", "```", cmds["valu"], "```", "",
-           f"Counters summed over the dispatches of the run's forward calls; {simds} SIMDs, {xcc} XCDs; SIMD cycles "
+           f"Counters summed over the dispatches of the run's {cmds.get('calls', 'forward calls')}; {simds} SIMDs, "
+           f"{xcc} XCDs; SIMD cycles "
            "= GRBM_GUI_ACTIVE / XCDs x SIMDs.  VALU issue = SQ_INSTS_VALU x 4 / SIMD cycles (a wave64 VALU "
            "instruction issues over 4 cycles); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMD cycles; co-issue = "
            "SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES; VALU per MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) "
@@ -582,6 +600,39 @@ def summarize_trace(trace_dir, bench_json, out_path):
                 f"average {rf['avg_launch_ms']:.2f} ms per launch (rocprofv3: {float(past['AverageNs']) / 1e6:.2f} ms); "
                 f"{rf['achieved']:.1f} TFLOP/s = {100 * rf['frac']:.1f}% of the {rf['peak']:.0f} TFLOP/s bf16 peak.",
             f"Step: {line['ms_per_step']:.1f} ms, {line['value']:.1f} useful TFLOP/s."]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+
+
+def summarize_bwd_trace(trace_dir, bench_json, out_path):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of
+    bench.py --backward, with bench.py's own HIP-event averages for the two
+    gradient kernels."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = list(csv.DictReader(open(f)))
+    line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    cmds = PROFILE_CMDS[_workload_of(bench_json)]
+    out = [f"# Kernel trace: MoBA {cmds['pass']}, {cmds['title']}",
+           "", "Command (run from the repository root on one MI355X):", "", "```", BWD_TRACE_CMD, "```", "",
+           f"One untimed forward-with-lse and {line['warmup']} untimed backward calls, then {line['steps']} timed "
+           f"forward-with-lse and {line['steps']} timed backward calls.", "",
+           "| Kernel | Calls | Total ns | Average ns | % | Min ns | Max ns |", "|---|---|---|---|---|---|---|"]
+    for r in rows[:14]:
+        name = r["Name"] if len(r["Name"]) < 72 else r["Name"][:69] + "..."
+        out.append(f"| {name} | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.0f} | "
+                   f"{float(r['Percentage']):.2f} | {r['MinNs']} | {r['MaxNs']} |")
+    out.append("")
+    for stage, tag, per_key in (("bwd_dkdv", "bwd_dkdv_kernel", 8), ("bwd_dq", "bwd_dq_kernel", 6)):
+        st = line["stages"][stage]
+        prof = [r for r in rows if tag in r["Name"]][0]
+        out.append(f"bench.py in the same run, HIP events around each {tag} launch: average "
+                   f"{st['ms'] / st['launches']:.2f} ms per launch (rocprofv3: {float(prof['AverageNs']) / 1e6:.2f} "
+                   f"ms); {st['tflops']:.0f} TFLOP/s ({per_key}·D FLOP per attended key) = "
+                   f"{100 * st['tflops'] / PEAK_BF16_TFLOPS:.1f}% of the {PEAK_BF16_TFLOPS:.0f} TFLOP/s bf16 peak.")
+    out.append(f"Backward: {line['ms_per_step']:.1f} ms, {line['value']:.0f} useful TFLOP/s (10·D per attended key); "
+               f"training step (forward with lse + backward): {line['train_step_ms']:.1f} ms.")
     with open(out_path, "w") as fh:
         fh.write("\n".join(out) + "\n")
 
@@ -950,6 +1001,8 @@ def main():
                     help="write the MFMA-busy summary from a rocprofv3 --pmc run, then exit")
     ap.add_argument("--summarize-valu", nargs=2, metavar=("PMC_DIR", "BENCH_JSON"),
                     help="write profiles/valu_<workload>.md from a VALU counter run")
+    ap.add_argument("--summarize-bwd-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="write profiles/kernel_trace_bwd_gqa32x8_128k.md from a kernel-trace run of --backward")
     ap.add_argument("--summarize-hbm", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
                     help="write the per-kernel HBM summary from the two traffic runs, then exit")
     args = ap.parse_args()
@@ -969,6 +1022,10 @@ def main():
     if args.summarize_decode_trace:
         summarize_decode_trace(*args.summarize_decode_trace,
                                os.path.join(ROOT, "profiles", "kernel_trace_decode_gqa32x8_1m_b8.md"))
+        return
+    if args.summarize_bwd_trace:
+        summarize_bwd_trace(*args.summarize_bwd_trace,
+                            os.path.join(ROOT, "profiles", "kernel_trace_bwd_gqa32x8_128k.md"))
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, os.path.join(ROOT, "profiles", "kernel_trace_gqa32x8_1m.md"))
