@@ -624,11 +624,17 @@ def summarize_bwd_trace(trace_dir, bench_json, out_path):
         out.append(f"| {name} | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.0f} | "
                    f"{float(r['Percentage']):.2f} | {r['MinNs']} | {r['MaxNs']} |")
     out.append("")
-    for stage, tag, per_key in (("bwd_dkdv", "bwd_dkdv_kernel", 8), ("bwd_dq", "bwd_dq_kernel", 6)):
+    # the stages bench.py times and the kernels each one launches (the dq
+    # stage of a query chunk: its past-block and own-block tiles, then the
+    # merge of a row's contributions)
+    stages = (("bwd_dkdv", ("bwd_dkdv_kernel",), 8),
+              ("bwd_dq", ("bwd_dq_kernel<false>", "bwd_dq_kernel<true>", "bwd_dq_merge_kernel"), 6))
+    for stage, tags, per_key in stages:
         st = line["stages"][stage]
-        prof = [r for r in rows if tag in r["Name"]][0]
-        out.append(f"bench.py in the same run, HIP events around each {tag} launch: average "
-                   f"{st['ms'] / st['launches']:.2f} ms per launch (rocprofv3: {float(prof['AverageNs']) / 1e6:.2f} "
+        prof = [r for r in rows if any(t in r["Name"] for t in tags)]
+        per_launch = sum(float(r["TotalDurationNs"]) for r in prof) / int(prof[0]["Calls"]) / 1e6
+        out.append(f"bench.py in the same run, HIP events around each {stage} stage ({', '.join(tags)}): average "
+                   f"{st['ms'] / st['launches']:.2f} ms per launch (rocprofv3, the same kernels: {per_launch:.2f} "
                    f"ms); {st['tflops']:.0f} TFLOP/s ({per_key}·D FLOP per attended key) = "
                    f"{100 * st['tflops'] / PEAK_BF16_TFLOPS:.1f}% of the {PEAK_BF16_TFLOPS:.0f} TFLOP/s bf16 peak.")
     out.append(f"Backward: {line['ms_per_step']:.1f} ms, {line['value']:.0f} useful TFLOP/s (10·D per attended key); "
