@@ -294,6 +294,16 @@ constexpr int kKvThreads = 2 * 64 * kKvGroups;  // two waves per key group
 // conflicts.
 __device__ __forceinline__ int unit_pos(int r, int u) { return (u + 4 * (r & 3) + ((r >> 2) & 3)) & 15; }
 __device__ __forceinline__ int row_off(int r, int u) { return r * RROW + unit_pos(r, u) * 16; }
+
+// Division of a 32-bit x by a divisor d fixed for the whole kernel, as the
+// high half of x * ceil(2^64 / d): with ceil(2^64 / d) = 2^64 / d + e,
+// 0 <= e < 1, the product is x / d + x e / 2^64 and x e / 2^64 < 2^-32 < 1 / d,
+// so the floor is exact for every x < 2^32 and d < 2^32 (d = 1 is x itself).
+// It replaces the VALU division sequence in each step's row decoding.
+__device__ __forceinline__ uint64_t div_magic(uint32_t d) { return d <= 1 ? 0ull : (~0ull / d + 1ull); }
+__device__ __forceinline__ uint32_t div_by(uint32_t x, uint32_t d, uint64_t m) {
+  return d <= 1 ? x : (uint32_t)__umul64hi((uint64_t)x, m);
+}
 }  // namespace
 
 __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
@@ -306,6 +316,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int kg = wave % kKvGroups;   // key group (32 keys)
   const bool pw = wave < kKvGroups;  // P-wave (S, P, dV) or dS-wave (dP, dS, dK)
   const int hk = (int)blockIdx.y;
+  const uint64_t m_kp = div_magic((uint32_t)a.kp), m_hq = div_magic((uint32_t)a.hq), m_g = div_magic((uint32_t)a.g);
   const int spb = (a.block + kKvKeys - 1) / kKvKeys;  // work-groups per block
   const int64_t i = blockIdx.x / spb;
   // (consecutive work-groups, one block's slices, go to different XCDs and
@@ -377,13 +388,15 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
       int64_t grow;
       int32_t pos;
       if (D.past[x]) {
-        const int32_t lr = D.raw[x] / a.kp;  // whole-sequence list: row = position * hq + head
-        pos = lr / a.hq;
+        // whole-sequence list: entry = row * kp + slot, row = position * hq + head
+        const int32_t lr = (int32_t)div_by((uint32_t)D.raw[x], (uint32_t)a.kp, m_kp);
+        pos = (int32_t)div_by((uint32_t)lr, (uint32_t)a.hq, m_hq);
         grow = bS * a.hq + lr;
       } else {
-        const int32_t p = (int32_t)own_pos0 + D.raw[x] / a.g;
+        const int32_t qg = (int32_t)div_by((uint32_t)D.raw[x], (uint32_t)a.g, m_g);
+        const int32_t p = (int32_t)own_pos0 + qg;
         pos = p;
-        grow = (bS + p) * a.hq + hk * a.g + D.raw[x] % a.g;
+        grow = (bS + p) * a.hq + hk * a.g + (D.raw[x] - qg * a.g);
       }
       const int u = tid & 15;
       St.q[x] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16raw*>(a.q) + grow * BD + u * 8);
