@@ -307,11 +307,13 @@ __device__ __forceinline__ uint32_t div_by(uint32_t x, uint32_t d, uint64_t m) {
 }  // namespace
 
 __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char rs[2][2 * RTILE];  // [buffer][Q rows | dO rows]
-  __shared__ __attribute__((aligned(16))) float rl[2][RSTEP];
-  __shared__ __attribute__((aligned(16))) float rd[2][RSTEP];
-  __shared__ __attribute__((aligned(16))) int32_t rt[2][RSTEP];
-  __shared__ __attribute__((aligned(16))) uint32_t pex[kKvGroups][64 * 8];  // P handed from P-wave to dS-wave
+  // three row stages and two P hand-over buffers: one barrier per step (see
+  // the loop below)
+  __shared__ __attribute__((aligned(16))) char rs[3][2 * RTILE];  // [stage][Q rows | dO rows]
+  __shared__ __attribute__((aligned(16))) float rl[3][RSTEP];
+  __shared__ __attribute__((aligned(16))) float rd[3][RSTEP];
+  __shared__ __attribute__((aligned(16))) int32_t rt[3][RSTEP];
+  __shared__ __attribute__((aligned(16))) uint32_t pex[2][kKvGroups][64 * 8];  // P handed from P-wave to dS-wave
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 5;
   const int kg = wave % kKvGroups;   // key group (32 keys)
   const bool pw = wave < kKvGroups;  // P-wave (S, P, dV) or dS-wave (dP, dS, dK)
@@ -426,11 +428,11 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int tr_r = 4 * lg + ((lane & 15) >> 2);
   const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // element offset inside a 32-dim tile
   const int32_t mykey = (int32_t)(wkey + (lane & 31));       // position of this lane's key
-  uint32_t* myex = pex[kg] + lane * 8;
 
   // phase 1: S (P-wave) or dP (dS-wave) = rows x this group's keys; the
   // P-wave turns S into P and hands it over through LDS
-  auto phase1 = [&](int buf, f32x16& x) {
+  auto phase1 = [&](int buf, int pb, f32x16& x) {
+    uint32_t* myex = pex[pb][kg] + lane * 8;
     const char* rowsrc = rs[buf] + (pw ? 0 : RTILE);  // Q rows or dO rows
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = 0.f;
@@ -463,7 +465,8 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
   };
   // phase 2: dV += P^T dO (P-wave) or dK += dS^T Q with dS = P (dP - delta)
   // (dS-wave); M = key, N = dim, K = row, the row operand read transposed
-  auto phase2 = [&](int buf, const f32x16& x) {
+  auto phase2 = [&](int buf, int pb, const f32x16& x) {
+    const uint32_t* myex = pex[pb][kg] + lane * 8;
     uint32_t av[8];
     {
       const u32x4 p0 = *reinterpret_cast<const u32x4*>(myex);
@@ -515,17 +518,21 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
     if (nsteps > 2) desc_of(2, D);
   }
   __syncthreads();
-  // step s: X holds step s + 1, Y is free; D locates step s + 2.  Two
-  // barriers per step: after phase 1 (P handed over) and after phase 2.
+  // Iteration s runs phase 2 of step s - 1 and then phase 1 of step s, and
+  // ends with the one barrier of the step.  Step s's rows sit in stage s % 3
+  // and its P in hand-over buffer s % 2; X holds step s + 1's rows (stored
+  // before the barrier, read from iteration s + 1 on), Y is free, D locates
+  // step s + 2.  A stage or P buffer is rewritten only after a barrier that
+  // follows every read of its previous contents: stage (s + 1) % 3 was last
+  // read by phase 2 of step s - 2 (iteration s - 1), P buffer s % 2 by phase 2
+  // of step s - 2 (iteration s - 1).
+  f32x16 x;  // phase 1's S (P-wave) or dP (dS-wave) of the previous step
   auto iter = [&](int64_t s, Stage& X, Stage& Y) {
-    const int buf = (int)(s & 1);
     if (s + 2 < nsteps) load_stage(D, Y);
     if (s + 3 < nsteps) desc_of(s + 3, D);
-    f32x16 x;
-    if (wact) phase1(buf, x);
-    __syncthreads();
-    if (wact) phase2(buf, x);
-    if (s + 1 < nsteps) store_stage(X, (int)((s + 1) & 1));
+    if (s > 0 && wact) phase2((int)((s - 1) % 3), (int)((s - 1) & 1), x);
+    if (wact) phase1((int)(s % 3), (int)(s & 1), x);
+    if (s + 1 < nsteps) store_stage(X, (int)((s + 1) % 3));
     __syncthreads();
   };
   for (int64_t s = 0; s < nsteps; s += 2) {
@@ -533,6 +540,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
     if (s + 1 >= nsteps) break;
     iter(s + 1, SB, SA);
   }
+  if (nsteps > 0 && wact) phase2((int)((nsteps - 1) % 3), (int)((nsteps - 1) & 1), x);
 
   if (!wact) return;
   // C layout of the accumulator: lane = dim 32 dt + lane % 32, element e = key acc_row(e, lg)
