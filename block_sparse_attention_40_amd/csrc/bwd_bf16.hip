@@ -506,7 +506,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   Desc D;
-  Stage SA, SB;
+  Stage SA, SB, SC;
   if (nsteps > 0) {
     desc_of(0, D);
     load_stage(D, SA);
@@ -515,30 +515,37 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
       desc_of(1, D);
       load_stage(D, SA);  // step 1, stored at the end of step 0
     }
-    if (nsteps > 2) desc_of(2, D);
+    if (nsteps > 2) {
+      desc_of(2, D);
+      load_stage(D, SB);  // step 2, stored at the end of step 1
+    }
+    if (nsteps > 3) desc_of(3, D);
   }
   __syncthreads();
   // Iteration s runs phase 2 of step s - 1 and then phase 1 of step s, and
   // ends with the one barrier of the step.  Step s's rows sit in stage s % 3
   // and its P in hand-over buffer s % 2; X holds step s + 1's rows (stored
-  // before the barrier, read from iteration s + 1 on), Y is free, D locates
-  // step s + 2.  A stage or P buffer is rewritten only after a barrier that
-  // follows every read of its previous contents: stage (s + 1) % 3 was last
-  // read by phase 2 of step s - 2 (iteration s - 1), P buffer s % 2 by phase 2
-  // of step s - 2 (iteration s - 1).
+  // before the barrier, read from iteration s + 1 on), Y step s + 2's, Z is
+  // free and D locates step s + 3: a step's rows are loaded three iterations
+  // before they are read.  A stage or P buffer is rewritten only after a
+  // barrier that follows every read of its previous contents: stage
+  // (s + 1) % 3 was last read by phase 2 of step s - 2 (iteration s - 1), P
+  // buffer s % 2 by phase 2 of step s - 2 (iteration s - 1).
   f32x16 x;  // phase 1's S (P-wave) or dP (dS-wave) of the previous step
-  auto iter = [&](int64_t s, Stage& X, Stage& Y) {
-    if (s + 2 < nsteps) load_stage(D, Y);
-    if (s + 3 < nsteps) desc_of(s + 3, D);
+  auto iter = [&](int64_t s, Stage& X, Stage& Z) {
+    if (s + 3 < nsteps) load_stage(D, Z);
+    if (s + 4 < nsteps) desc_of(s + 4, D);
     if (s > 0 && wact) phase2((int)((s - 1) % 3), (int)((s - 1) & 1), x);
     if (wact) phase1((int)(s % 3), (int)(s & 1), x);
     if (s + 1 < nsteps) store_stage(X, (int)((s + 1) % 3));
     __syncthreads();
   };
-  for (int64_t s = 0; s < nsteps; s += 2) {
-    iter(s, SA, SB);
+  for (int64_t s = 0; s < nsteps; s += 3) {
+    iter(s, SA, SC);
     if (s + 1 >= nsteps) break;
     iter(s + 1, SB, SA);
+    if (s + 2 >= nsteps) break;
+    iter(s + 2, SC, SB);
   }
   if (nsteps > 0 && wact) phase2((int)((nsteps - 1) % 3), (int)((nsteps - 1) & 1), x);
 
