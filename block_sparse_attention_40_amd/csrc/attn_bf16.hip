@@ -132,14 +132,6 @@ struct KVStager {
   }
 };
 
-// Wait until every vector-memory load issued so far has returned
-// (s_waitcnt vmcnt(0)), and keep the scheduler from moving loads across.
-__device__ __forceinline__ void drain_vmem() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt = 0; expcnt, lgkmcnt unconstrained
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Softmax state and accumulators of one wave's 32 query rows.
 struct WaveRows {
   bf16x8 qb[8];   // B operand of S^T: step s holds d = (lane/32)*8 + 16 s .. +7
@@ -678,20 +670,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // each image is 16 chunks of 64 units; wave w loads chunks w % 16 and
   // 15 - w % 16 (with 12 waves chunks 4..11 are loaded twice, same data)
   static_assert(NW == 8 || NW == 12, "two chunks per image and wave");
-  // one 16-byte unit per lane from global memory into LDS at m0 + 16 * lane
-  // (m0 = the wave's base, saved and restored around the load)
-  auto lds_dma16 = [](uint32_t lds_base, const void* gptr) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_base), "v"(gptr)
-        : "memory");
-  };
   auto dma = [&](char* lb, int sl) {
     const uint16_t* ks = kimg + src(sl);
     const uint16_t* vs = vimg + src(sl);

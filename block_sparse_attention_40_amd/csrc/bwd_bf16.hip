@@ -90,7 +90,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16raw* __restrict
 // ---------------------------------------------------------------------------
 template <bool kOwn>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * 3 * BIMG];  // two buffers x three images
+  // three slice buffers of the three images each (144 KiB), loaded straight
+  // from HBM two slices ahead
+  __shared__ __attribute__((aligned(16))) char lbs[3][3 * BIMG];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 5;
   int hk, cnt;
   int64_t blk, own_p0 = 0;
@@ -170,33 +172,32 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   }
   const int64_t img0 = (((int64_t)a.bb * a.hkv + hk) * (a.seqlen / BKT) + blk * nsl_blk) * (BKT * BD);
   const uint16_t* im[3] = {a.kimg + img0, a.vkimg + img0, a.kvimg + img0};
-  // staging: 3 images x 1024 units of 16 bytes = 6 units per thread
-  u32x4 stg[6];
-  auto load = [&](int sl) {
-    const int64_t so = (int64_t)(sl < nsl ? sl : nsl - 1) * (BKT * BD);
-#pragma unroll
-    for (int x = 0; x < 6; ++x) {
-      const int u = tid + 512 * x;  // 0 .. 3071
-      stg[x] = *reinterpret_cast<const u32x4*>(im[u >> 10] + so + (u & 1023) * 8);
-    }
-  };
-  auto store = [&](char* buf) {
-#pragma unroll
-    for (int x = 0; x < 6; ++x) {
-      const int u = tid + 512 * x;
-      *reinterpret_cast<u32x4*>(buf + (u >> 10) * BIMG + (u & 1023) * 16) = stg[x];
-    }
-  };
   const int kofs = lg * 1024 + (lane & 31) * 16;  // K-layout operand base (unit-major images)
   const int vofs = lg * 2048 + (lane & 31) * 16;  // V^T-layout operand base
   const float c = a.scale_log2;
 
-  load(0);
-  store(smem);
-  __syncthreads();
-  for (int sl = 0; sl < nsl; ++sl) {
-    const char* buf = smem + (sl & 1) * 3 * BIMG;
-    if (sl + 1 < nsl) load(sl + 1);
+  // The slices go from HBM straight into LDS (global_load_lds, written as
+  // inline asm so the compiler neither tracks nor waits for them): the three
+  // images, 3 x 1024 units of 16 bytes, are 6 units per thread; the 64 lanes
+  // of a wave load 64 consecutive units of one image, so their LDS
+  // destinations are one contiguous kilobyte at a wave-uniform base (m0).
+  // The loads of slice s + 2 go out at the start of slice s; the wait before
+  // each barrier leaves only the youngest slice's 6 loads in flight.  Past the
+  // last slice the loads repeat it, so every iteration issues the same loads.
+  auto dma = [&](char* lb, int sl) {
+    const int64_t so = (int64_t)(sl < nsl ? sl : nsl - 1) * (BKT * BD);
+    typedef __attribute__((address_space(3))) char lds_char;
+    const uint32_t lb_addr = (uint32_t)(uintptr_t)((lds_char*)lb);
+#pragma unroll
+    for (int x = 0; x < 6; ++x) {
+      const int u0 = wave * 64 + 512 * x;  // this wave's first unit (0 .. 3071, one image)
+      const int img = u0 >> 10, unit = (u0 & 1023) + lane;
+      const uint32_t wb = __builtin_amdgcn_readfirstlane(lb_addr + (uint32_t)(img * BIMG + (u0 & 1023) * 16));
+      lds_dma16(wb, im[img] + so + unit * 8);
+    }
+  };
+  auto publish = [] { asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory"); };
+  auto slice = [&](const char* buf, int sl) {
     const int64_t key_base = blk * a.block + (int64_t)sl * BKT;  // absolute position of key 0 of the slice
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -233,9 +234,18 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
-    if (sl + 1 < nsl) store(smem + ((sl + 1) & 1) * 3 * BIMG);
-    __syncthreads();
+  };
+
+  drain_vmem();  // the rows' q and dout in before any slice load goes out
+  dma(lbs[0], 0);
+  dma(lbs[1], 1);
+  publish();  // slice 0 in
+  for (int sl = 0, cur = 0; sl < nsl; ++sl, cur = cur == 2 ? 0 : cur + 1) {
+    dma(lbs[cur == 0 ? 2 : cur - 1], sl + 2);  // buffer (sl + 2) % 3; past the end: the last slice again
+    slice(lbs[cur], sl);
+    publish();  // slice sl + 1 in, in every wave
   }
+  drain_vmem();  // every slice load landed before the work-group ends
 
   if (valid) {
     // lane holds d = 32 b + 8 q + 4 lg + i (i = 0..3) of its row

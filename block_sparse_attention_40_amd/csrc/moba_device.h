@@ -52,6 +52,33 @@ __device__ __forceinline__ void load8(const float* p, float* o) {
   for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[4 + i] = b[i]; }
 }
 
+// Wait until every vector-memory load issued so far has returned
+// (s_waitcnt vmcnt(0)), and keep the scheduler from moving loads across.
+__device__ __forceinline__ void drain_vmem() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt = 0; expcnt, lgkmcnt unconstrained
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One 16-byte unit per lane from global memory straight into LDS, at
+// lds_base + 16 * lane (global_load_lds_dwordx4 with m0 = lds_base, a
+// wave-uniform value; m0 is saved and restored around the load).  Written as
+// inline asm, so the compiler neither tracks the load nor waits for it: the
+// caller waits (s_waitcnt vmcnt) before the barrier that publishes the data,
+// and the memory clobber keeps LDS accesses on their side of the load.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* gptr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(gptr)
+      : "memory");
+}
+
 // Order-preserving map of an fp32 score to uint32 (NaN must be removed first).
 __device__ __forceinline__ uint32_t orderable(float s) {
   uint32_t u = __builtin_bit_cast(uint32_t, s);
