@@ -1,18 +1,28 @@
 // MoBA gate (deep-dive report on MoBA, sections 2.2 and 2.3): fp32 scores
 // s_i = <q, mu_i>, exclusion of future blocks, the forced own block, and a
-// hard top-k with ties broken towards the lower block index.
+// hard top-k with ties broken towards the lower block index.  Every form
+// below chooses exactly the same set.
 //
-// One work-group handles `gate_t` consecutive query positions of one KV head
-// and all query heads of its group (one row per thread), so the block means
-// of that KV head are staged once in LDS (in slices of kMuSlice blocks) and
-// read by every row with broadcast loads.  Each thread keeps its running
-// top-m list in registers as 64-bit keys (orderable score << 32 | ~index):
-// a larger key is a larger score, and between equal scores the lower block
-// index, which is exactly the tie rule.
+// gate_kernel (VALU; fp32 inputs and the stand-alone gate): one work-group
+// handles `gate_t` consecutive query positions of one KV head and all query
+// heads of its group (one row per thread), so the block means of that KV
+// head are staged once in LDS (in slices of kMuSlice blocks) and read by
+// every row with broadcast loads.  Each thread keeps its running top-m list
+// in registers as 64-bit keys (orderable score << 32 | ~index): a larger key
+// is a larger score, and between equal scores the lower block index, which
+// is exactly the tie rule.  gate_rounds_kernel takes over when m exceeds
+// one list of 32 (the cut-off score found in rounds, RoundState).
 //
-// Besides sel_idx the kernel writes, per work-group, how many of its rows
+// gate_mfma_kernel (bf16 inputs): the scores on the matrix cores, the choice
+// in one pass for short lists, in two passes (the m-th largest score, then
+// the blocks above it and the lowest-index ties at it) for longer ones, and
+// in rounds beyond 32.
+//
+// Besides sel_idx the kernels write, per work-group, how many of its rows
 // chose each block (used to build the per-block row lists), stored as
-// [KV head, block, work-group] so that each list's counts are contiguous.
+// [KV head, block, work-group] so that each list's counts are contiguous;
+// with more blocks than the dispatch's LDS counters hold the caller passes no
+// count table and the dispatch counts the rows from sel_idx instead.
 #include "moba_device.h"
 #include "moba_kernels.h"
 #include "moba_plan.h"
