@@ -6,8 +6,9 @@
 // served by KV head hk and chose block i as a non-own block.  Three steps,
 // all on the device (no host round trip):
 //   1. list_scan:  per list (one work-group each), exclusive prefix over the
-//                  gate work-groups of their counts for that list (the gate
-//                  writes them contiguous per list);
+//                  gate work-groups of their counts for that list (written
+//                  contiguous per list by the gate, or by hist_kernel from
+//                  the selection: for the backward, and beyond 8192 blocks);
 //   2. tile_plan:  one work-group scans the list sizes into list offsets and
 //                  cuts every list into tiles of tile_rows rows;
 //   3. scatter:    every row writes its (row, slot) entries into its lists at
