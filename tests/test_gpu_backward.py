@@ -81,6 +81,9 @@ CASES = [
     small("noncausal", 1, 512, 2, 2, 128, 3, causal=False),
     small("g8", 1, 1024, 8, 1, 128, 4),
     small("g3", 1, 1024, 6, 2, 128, 4),
+    # more than 32 past slots per row (the forward's gate ranks in rounds)
+    small("topk40_gqa", 1, 4096, 4, 2, 64, 40),
+    small("topk50_noncausal", 1, 4096, 2, 1, 64, 50, causal=False),
 ]
 
 
