@@ -519,3 +519,20 @@ def test_forward_many_blocks_sampled(w, gate):
     rows = [(0, int(t), h) for h in range(w.num_q_heads) for t in rng.integers(0, w.seqlen, 48)] + \
            [(0, t, h) for h in range(w.num_q_heads) for t in edges]
     run(w, rows=rows, device_inputs=True, gate=gate)
+
+
+@pytest.mark.slow
+def test_forward_many_blocks_1m_count_table_chunks_sampled():
+    """1M positions in blocks of 16 keys (65536 blocks, 32/8 heads, top-3):
+    the per-(list, work-group) count table would exceed its cap in one
+    chunk, so the forward runs in chunks of 4096 blocks, each counted by the
+    dispatch in eight ranges of 8192 blocks.  Sampled rows, with the first
+    and last position of every chunk."""
+    w = small("n65536_1m", "bf16", 1, 1 << 20, 32, 8, 128, 16, 3, seed=91)
+    cb, edges = chunk_edges(w)
+    say(f"[chunks] {cb} blocks per chunk, {len(edges) // 2} chunks")
+    assert cb == 4096
+    rng = np.random.default_rng(92)
+    rows = [(0, int(t), int(h)) for t, h in zip(rng.integers(0, w.seqlen, 192), rng.integers(0, 32, 192))] + \
+           [(0, t, int(h)) for t in edges for h in (0, 31)]
+    run(w, rows=rows, device_inputs=True)
