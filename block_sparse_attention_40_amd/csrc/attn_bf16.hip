@@ -16,13 +16,19 @@
 //       own block up to each query, with the row's partials folded into the
 //       same online softmax as further groups of keys (their loads overlap
 //       the slice loop), then the bf16 output.
+//   attn_past_img_kernel: the past-block tiles of 384 rows, K and V read
+//       from per-slice images laid out as LDS wants them (long lists).
+//   attn_past_rows_kernel / attn_own_rows_kernel: 128-row tiles that load K
+//       and V rows as they are straight into LDS in 32-key slices and read
+//       the V^T operand with the transposing LDS load; three work-groups per
+//       CU (short lists, blocks of a few hundred keys).
 //
 // Work split inside a work-group: every wave owns 32 query rows; 4, 8 or 12
 // waves share each K/V slice staged in LDS, and two or three waves per SIMD
 // let one wave's softmax arithmetic overlap another's MFMAs.  Slices are
 // loaded ahead while the current one is computed (into registers, or
-// straight into a third LDS buffer on the slice-image path), and one barrier
-// per slice separates the buffer hand-over.
+// straight into a third LDS buffer on the direct-load paths), and one
+// barrier per slice separates the buffer hand-over.
 //
 // Tile mathematics (per wave, per 64-key slice, D = 128):
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = keys from LDS, B = the
@@ -298,12 +304,12 @@ __device__ __forceinline__ void qk_slice(const bf16raw* buf, const bf16x8* qb, f
 // bf16 pairs (pk[kb][x] holds accumulator elements 2x and 2x+1 of block kb).
 // masked(kc): key kc + 4 * (lane / 32) of the slice is invisible to this
 // lane's query.
-template <bool kMasked, typename Mask>
+template <bool kMasked, typename Mask, int NKB = 2>
 __device__ __forceinline__ void softmax_p(f32x16* s, WaveRows& R, float c, int lane, Mask masked, uint32_t (*pk)[8]) {
   const int lg = lane >> 5;
   float mx = -__builtin_inff();
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       if (kMasked && masked(key_of(kb, e))) s[kb][e] = -__builtin_inff();
@@ -328,7 +334,7 @@ __device__ __forceinline__ void softmax_p(f32x16* s, WaveRows& R, float c, int l
   }
   const float negm = -R.m;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
       const float p0 = fast_exp2(__builtin_fmaf(s[kb][e], c, negm));
@@ -338,10 +344,18 @@ __device__ __forceinline__ void softmax_p(f32x16* s, WaveRows& R, float c, int l
   // the row sum adds the bf16 weights that P V actually uses; two partial
   // sums keep the dependency chains short
   float ps0 = 0.f, ps1 = 0.f;
+  if constexpr (NKB == 2) {
 #pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    ps0 = add_bf16_pair(pk[0][x], ps0);
-    ps1 = add_bf16_pair(pk[1][x], ps1);
+    for (int x = 0; x < 8; ++x) {
+      ps0 = add_bf16_pair(pk[0][x], ps0);
+      ps1 = add_bf16_pair(pk[1][x], ps1);
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < 8; x += 2) {
+      ps0 = add_bf16_pair(pk[0][x], ps0);
+      ps1 = add_bf16_pair(pk[0][x + 1], ps1);
+    }
   }
   R.l += ps0 + ps1;
 }
@@ -385,10 +399,10 @@ __device__ __forceinline__ void attend_slice(const bf16raw* buf, WaveRows& R, co
 }
 
 // Scores of the keys a mask hides become -inf (weight 0 after the softmax).
-template <typename Mask>
+template <typename Mask, int NKB = 2>
 __device__ __forceinline__ void mask_scores(f32x16* s, Mask masked) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       if (masked(key_of(kb, e))) s[kb][e] = -__builtin_inff();
@@ -724,6 +738,235 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row path (block a whole number of 64-key slices, K and V as they are).
+//
+// A slice goes from HBM straight into LDS (global_load_lds) in row form:
+// 64 K rows and 64 V rows of 256 bytes, the sixteen 16-byte units of row r
+// rotated by rot(r) = 4 (r & 3) + ((r >> 2) & 3) (unit u at position
+// (u + rot(r)) & 15).  The rotation keeps two read shapes free of bank
+// conflicts: 16 consecutive rows at one unit (the K operand of S^T = K Q^T,
+// read as it is), and 4 consecutive rows across two adjacent units, 8 bytes
+// each (the V^T operand of P V: eight consecutive keys of one d per lane,
+// which the transposing load ds_read_b64_tr_b16 gathers from the V rows).
+// So no slice images are needed, and nothing passes through registers.
+constexpr int ROW_BYTES = HD * 2;           // one K or V row in LDS
+constexpr int ROWS_BYTES = KT * ROW_BYTES;  // one slice of K (or V) rows, 16 KiB
+__device__ __forceinline__ int row_rot(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+// This lane's LDS byte offsets inside a slice of rows.  k[s]: the K operand
+// of contraction step s (key lane & 31, d 16 s + 8 (lane / 32) .. + 7); the
+// second 32-key block adds 32 rows.  va[b] / vb[b]: the two transposing V
+// reads of d block b (keys 4 (lane / 32) + ((lane & 15) >> 2) and 8 more,
+// d 32 b + 16 ((lane >> 4) & 1) + 4 (lane & 3) .. + 3); the 16-key step
+// (kb, hs) adds 32 kb + 16 hs rows.
+struct RowOffsets {
+  int k[8];
+  int va[4], vb[4];
+  __device__ __forceinline__ void init(int lane) {
+    const int lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) k[s] = lr * ROW_BYTES + (((2 * s + lg + row_rot(lr)) & 15) << 4);
+    const int tr = 4 * lg + ((lane & 15) >> 2);
+    const int tc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int u = 4 * b + (tc >> 3), half = ((tc >> 2) & 1) * 8;
+      va[b] = tr * ROW_BYTES + (((u + row_rot(tr)) & 15) << 4) + half;
+      vb[b] = (tr + 8) * ROW_BYTES + (((u + row_rot(tr + 8)) & 15) << 4) + half;
+    }
+  }
+};
+
+template <int NKB>
+__device__ __forceinline__ void qk_rows(const char* kbuf, const bf16x8* qb, f32x16* s, const RowOffsets& ro) {
+  bf16x8 ka[NKB][8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) ka[kb][st] = *reinterpret_cast<const bf16x8*>(kbuf + ro.k[st] + kb * 32 * ROW_BYTES);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][st], qb[st], s[kb], 0, 0, 0);
+}
+
+// O^T += V^T P^T for one slice of V rows.  The transposing load gives lane l
+// the values of column d = 32 b + (l & 31) on four consecutive rows; the two
+// loads cover keys 4 lg .. 4 lg + 3 and 8 + 4 lg .. 8 + 4 lg + 3 of the
+// 16-key step, the order in which P^T holds them (the score accumulator's
+// row order).
+template <int NKB>
+__device__ __forceinline__ void pv_rows(const char* vbuf, const uint32_t (*pk)[8], WaveRows& R, const RowOffsets& ro) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  bf16x8 va[8 * NKB];
+#pragma unroll
+  for (int x = 0; x < 8 * NKB; ++x) {
+    const int kb = x >> 3, hs = (x >> 2) & 1, b = x & 3;
+    const char* base = vbuf + (32 * kb + 16 * hs) * ROW_BYTES;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + ro.va[b]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + ro.vb[b]));
+    va[x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      const u32x4 pw = {pk[kb][4 * hs], pk[kb][4 * hs + 1], pk[kb][4 * hs + 2], pk[kb][4 * hs + 3]};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        R.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[8 * kb + 4 * hs + b], pb, R.o[b], 0, 0, 0);
+    }
+}
+
+// Past-block tiles of NW * 32 rows over a block that is a whole number of
+// slices, K and V read as rows (no images).  A slice is NKB blocks of 32
+// keys (64 or 32 keys: the shorter slice halves the LDS a work-group needs,
+// so more work-groups share a CU).  NBUF LDS slice buffers: with two, the
+// loads of slice s+1 go out at the start of slice s; with three, those of
+// slice s+2.  K (or V) rows of a slice are 8 NKB loads of 1 KiB (four whole
+// rows each); wave w issues loads w, w + NW, ...
+template <int NW, int NBUF, int NKB>
+struct RowsCfg {
+  static constexpr int SK = 32 * NKB;                  // keys per slice
+  static constexpr int TBYTES = SK * ROW_BYTES;        // K (or V) rows of one slice
+  static constexpr int BUF = 2 * TBYTES;               // one slice buffer
+  static constexpr int PER = 8 * NKB / NW;             // loads per tensor, wave and slice
+  static constexpr int WGS = (160 * 1024) / (NBUF * BUF);  // work-groups per CU by LDS
+  static constexpr int WPS0 = WGS * NW / 4;            // waves per SIMD by LDS
+  static constexpr int WPS = WPS0 < 1 ? 1 : (WPS0 > 3 ? 3 : WPS0);  // at most three (168 registers)
+};
+
+template <int NW, int NBUF, int NKB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RowsCfg<NW, NBUF, NKB>::WPS,
+                                                                         RowsCfg<NW, NBUF, NKB>::WPS))) void
+attn_past_rows_kernel(PastArgs a) {
+  using C = RowsCfg<NW, NBUF, NKB>;
+  static_assert((8 * NKB) % NW == 0 && (NBUF == 2 || NBUF == 3), "whole loads per wave; two or three buffers");
+  __shared__ __attribute__((aligned(16))) char lb[NBUF][C::BUF];
+  constexpr int ROWS = NW * 32;
+  constexpr int PER = C::PER;
+  const int32_t total = a.tiles[0];
+  const int32_t per_xcd = (total + 7) >> 3;
+  const int32_t loc = blockIdx.x >> 3;
+  if (loc >= per_xcd) return;
+  const int32_t tile = (int32_t)(blockIdx.x & 7) * per_xcd + loc;
+  if (tile >= total) return;
+  const int32_t L = a.tiles[8 + 2 * tile];
+  const int32_t start = a.tiles[9 + 2 * tile];
+  const int32_t end = a.listoff[L] + a.count[L];
+  const int32_t cnt = (end - start) < ROWS ? (end - start) : ROWS;
+  const int hk = (int)(L / a.n);
+  const int64_t blk = L % a.n;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  WaveRows R;
+  const int r = wave * 32 + (lane & 31);
+  const bool valid = r < cnt;
+  const int32_t entry = a.entries[start + (valid ? r : 0)];
+  {
+    const int64_t local_row = entry / a.kp;
+    const int64_t pic = local_row / a.hq;
+    const int h = (int)(local_row % a.hq);
+    const int64_t t = a.t0 + pic;
+    load_q(reinterpret_cast<const bf16raw*>(a.q) + ((a.bb * a.seqlen + t) * a.hq + h) * HD, lane, R.qb);
+  }
+  rows_init(R);
+  RowOffsets ro;
+  ro.init(lane);
+
+  const int nsl = a.block / C::SK;
+  const int64_t rs = (int64_t)a.hkv * HD;
+  const int64_t base = ((int64_t)a.bb * a.seqlen + blk * a.block) * rs + hk * HD;
+  const bf16raw* kblk = reinterpret_cast<const bf16raw*>(a.k) + base;
+  const bf16raw* vblk = reinterpret_cast<const bf16raw*>(a.v) + base;
+  // load j of a tensor: rows 4 j + lane / 16, LDS position lane & 15 of its
+  // row, so the lane fetches the unit that the row's rotation puts there
+  int goff[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = wave + NW * i;
+    const int row = 4 * j + (lane >> 4);
+    goff[i] = row * (int)rs + (((lane & 15) - row_rot(row)) & 15) * 8;
+  }
+  // past the last slice the loads repeat it, so every iteration issues the same loads
+  auto dma = [&](char* buf, int sl) {
+    const int64_t so = (int64_t)(sl < nsl ? sl : nsl - 1) * C::SK * rs;
+    typedef __attribute__((address_space(3))) char lds_char;
+    const uint32_t lb_addr = (uint32_t)(uintptr_t)((lds_char*)buf);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t wb = __builtin_amdgcn_readfirstlane(lb_addr + (uint32_t)((wave + NW * i) * 1024));
+      lds_dma16(wb, kblk + so + goff[i]);
+      lds_dma16(wb + C::TBYTES, vblk + so + goff[i]);
+    }
+  };
+  const float c = a.scale_log2;
+  auto slice = [&](const char* buf) {
+    f32x16 sc[NKB];
+    uint32_t pk[NKB][8];
+    qk_rows<NKB>(buf, R.qb, sc, ro);
+    softmax_p<false, NoMask, NKB>(sc, R, c, lane, NoMask{}, pk);
+    pv_rows<NKB>(buf + C::TBYTES, pk, R, ro);
+  };
+
+  // The loads into LDS are inline asm, so the compiler neither tracks them
+  // nor waits for them: each barrier that publishes a slice first waits
+  // (vmcnt) until only the younger slices' loads are in flight, and the asm
+  // memory clobber keeps the LDS reads on their side of it.  A buffer is
+  // loaded again only after the barrier that ends the slice that read it.
+  drain_vmem();  // the query rows in before any slice load goes out
+  if constexpr (NBUF == 2) {
+    auto publish = [] { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
+    dma(lb[0], 0);
+    publish();
+    for (int sl = 0; sl < nsl; ++sl) {
+      if (sl + 1 < nsl) dma(lb[(sl + 1) & 1], sl + 1);
+      slice(lb[sl & 1]);
+      publish();
+    }
+  } else {
+    static_assert(NBUF == 2 || 2 * PER == 8 || 2 * PER == 4, "vmcnt of one slice");
+    auto publish = [] {
+      if constexpr (2 * PER == 8)
+        asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    };
+    dma(lb[0], 0);
+    dma(lb[1], 1);
+    publish();
+    auto step = [&](int sl, char* cur, char* nx2) {
+      dma(nx2, sl + 2);  // past the end: the last slice again
+      slice(cur);
+      publish();  // slice sl + 1 in, in every wave
+    };
+    for (int sl = 0; sl < nsl; sl += 3) {
+      step(sl, lb[0], lb[2]);
+      if (sl + 1 >= nsl) break;
+      step(sl + 1, lb[1], lb[0]);
+      if (sl + 2 >= nsl) break;
+      step(sl + 2, lb[2], lb[1]);
+    }
+    drain_vmem();
+  }
+
+  const int lg = lane >> 5;
+  const float ltot = pair_sum(R.l);
+  if (valid) {
+    const int64_t local_row = entry / a.kp, slot = entry - local_row * a.kp;
+    const int64_t orow = partial_row(local_row / a.hq, (int)(local_row % a.hq), a.block, a.hkv, a.g);
+    store_partial(a.part_o, a.part_rows, orow, slot, R.o, 1.f / ltot, lg);
+    if (lg == 0) a.part_lse[slot * a.part_rows + orow] = R.m + fast_log2(ltot);
+  }
+}
+
 constexpr int OWN_NW = 8;  // own-block tiles: 8 waves x 32 rows
 
 // Own block of each query (causal up to the query itself) plus the merge
@@ -901,6 +1144,152 @@ __global__ __launch_bounds__(OWN_NW * 64) void attn_own_kernel(OwnArgs a) {
   }
 }
 
+// The own block from K and V rows (block a whole number of NKB * 32-key
+// slices), loaded straight into LDS as in attn_past_rows_kernel, in tiles of
+// NW * 32 rows; the row's partials are folded after the slice loop.
+template <int NW, int NBUF, int NKB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RowsCfg<NW, NBUF, NKB>::WPS,
+                                                                         RowsCfg<NW, NBUF, NKB>::WPS))) void
+attn_own_rows_kernel(OwnArgs a) {
+  using C = RowsCfg<NW, NBUF, NKB>;
+  static_assert((8 * NKB) % NW == 0 && (NBUF == 2 || NBUF == 3), "whole loads per wave; two or three buffers");
+  __shared__ __attribute__((aligned(16))) char lb[NBUF][C::BUF];
+  constexpr int PER = C::PER;
+  // tile order as in attn_own_kernel
+  const int64_t tiles_per_block = (a.block + a.own_t - 1) / a.own_t;
+  const int64_t units = (a.cnt / a.block) * a.hkv;
+  const int64_t total = units * tiles_per_block;
+  const int64_t lt = units >= 64 ? (int64_t)(blockIdx.x & 7) * ((total + 7) >> 3) + (blockIdx.x >> 3) : (int64_t)blockIdx.x;
+  if (lt >= total) return;
+  const int64_t jl = lt / tiles_per_block / a.hkv;
+  const int hk = (int)(lt / tiles_per_block % a.hkv);
+  const int64_t p0 = (tiles_per_block - 1 - lt % tiles_per_block) * a.own_t;
+  const int64_t j = a.t0 / a.block + jl;
+  const int G = a.g;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lg = lane >> 5;
+  WaveRows R;
+  const int rr = wave * 32 + (lane & 31);
+  const int64_t pp = p0 + rr / G;
+  const bool valid = rr < a.own_t * G && pp < a.block;
+  const int64_t pos = valid ? pp : p0;
+  const int h = valid ? hk * G + rr % G : hk * G;
+  {
+    const int64_t t = j * a.block + pos;
+    load_q(reinterpret_cast<const bf16raw*>(a.q) + ((a.bb * a.seqlen + t) * a.hq + h) * HD, lane, R.qb);
+  }
+  rows_init(R);
+
+  const int64_t nslot = a.causal ? (j < a.kp ? j : a.kp) : a.kp;
+  const int64_t orow = partial_row(j * a.block + pos - a.t0, h, a.block, a.hkv, G);
+  const bf16raw* po = reinterpret_cast<const bf16raw*>(a.part_o);
+  const int64_t rows = a.part_rows;
+
+  if (a.causal) {
+    const int64_t last = (p0 + a.own_t < a.block ? p0 + a.own_t : a.block);  // keys [0, last) of the block
+    const int nsl = (int)((last + C::SK - 1) / C::SK);
+    int64_t wmax = p0 + (wave * 32 + 31) / G;
+    if (wmax > a.block - 1) wmax = a.block - 1;
+    const int nfree = (int)(p0 / C::SK);
+    const float c = a.scale_log2;
+    RowOffsets ro;
+    ro.init(lane);
+    const int64_t rs = (int64_t)a.hkv * HD;
+    const int64_t base = ((int64_t)a.bb * a.seqlen + j * a.block) * rs + hk * HD;
+    const bf16raw* kblk = reinterpret_cast<const bf16raw*>(a.k) + base;
+    const bf16raw* vblk = reinterpret_cast<const bf16raw*>(a.v) + base;
+    int goff[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int jj = wave + NW * i;
+      const int row = 4 * jj + (lane >> 4);
+      goff[i] = row * (int)rs + (((lane & 15) - row_rot(row)) & 15) * 8;
+    }
+    // keys past `last` in the last slice exist (the block is whole slices)
+    // and are masked like every key after the query; past the last slice the
+    // loads repeat it
+    auto dma = [&](char* buf, int sl) {
+      const int64_t so = (int64_t)(sl < nsl ? sl : nsl - 1) * C::SK * rs;
+      typedef __attribute__((address_space(3))) char lds_char;
+      const uint32_t lb_addr = (uint32_t)(uintptr_t)((lds_char*)buf);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const uint32_t wb = __builtin_amdgcn_readfirstlane(lb_addr + (uint32_t)((wave + NW * i) * 1024));
+        lds_dma16(wb, kblk + so + goff[i]);
+        lds_dma16(wb + C::TBYTES, vblk + so + goff[i]);
+      }
+    };
+    auto slice = [&](int sl, const char* buf) {
+      const int64_t k0 = (int64_t)sl * C::SK;
+      if (k0 <= wmax) {
+        f32x16 sc[NKB];
+        uint32_t pk[NKB][8];
+        qk_rows<NKB>(buf, R.qb, sc, ro);
+        if (sl >= nfree) mask_scores<CausalMask, NKB>(sc, CausalMask((int)(pos - k0), lane));
+        softmax_p<false, NoMask, NKB>(sc, R, c, lane, NoMask{}, pk);
+        pv_rows<NKB>(buf + C::TBYTES, pk, R, ro);
+      }
+    };
+    drain_vmem();  // the query rows in before any slice load goes out
+    if constexpr (NBUF == 2) {
+      auto publish = [] { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
+      dma(lb[0], 0);
+      publish();
+      for (int sl = 0; sl < nsl; ++sl) {
+        if (sl + 1 < nsl) dma(lb[(sl + 1) & 1], sl + 1);
+        slice(sl, lb[sl & 1]);
+        publish();
+      }
+    } else {
+      static_assert(NBUF == 2 || 2 * PER == 8 || 2 * PER == 4, "vmcnt of one slice");
+      auto publish = [] {
+        if constexpr (2 * PER == 8)
+          asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+      };
+      dma(lb[0], 0);
+      dma(lb[1], 1);
+      publish();
+      auto step = [&](int sl, char* cur, char* nx2) {
+        dma(nx2, sl + 2);
+        slice(sl, cur);
+        publish();
+      };
+      for (int sl = 0; sl < nsl; sl += 3) {
+        step(sl, lb[0], lb[2]);
+        if (sl + 1 >= nsl) break;
+        step(sl + 1, lb[1], lb[0]);
+        if (sl + 2 >= nsl) break;
+        step(sl + 2, lb[2], lb[1]);
+      }
+      drain_vmem();
+    }
+  }
+
+  for (int64_t s = 0; s < nslot; ++s) {
+    u32x4 pv[8];
+    load_partial(po, rows, orow, s, lg, pv);
+    fold_partial(R, pv, a.part_lse[s * rows + orow], lg);
+  }
+  const float Lsum = pair_sum(R.l);
+  if (valid) {
+    const float inv = 1.f / Lsum;
+    const int64_t t = j * a.block + pos;
+    if (a.lse && lg == 0) a.lse[((int64_t)a.bb * a.hq + h) * a.seqlen + t] = (R.m + fast_log2(Lsum)) * 0.6931471805599453f;
+    bf16raw* dst = reinterpret_cast<bf16raw*>(a.out) + ((a.bb * a.seqlen + t) * a.hq + h) * HD;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x2 w2 = {pack_bf16x2(R.o[b][4 * q4] * inv, R.o[b][4 * q4 + 1] * inv),
+                          pack_bf16x2(R.o[b][4 * q4 + 2] * inv, R.o[b][4 * q4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(dst + b * 32 + 8 * q4 + lg * 4) = w2;
+      }
+  }
+}
+
 int launch_attn_past(const PastArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.max_tiles);
   // the 384-row tiles read K and V only from the slice images
@@ -913,8 +1302,12 @@ int launch_attn_past(const PastArgs& a, hipStream_t st) {
     // 12 waves (three per SIMD) over the slice images
     hipLaunchKernelGGL((attn_past_img_kernel<12>), grid, dim3(768), 0, st, a);
   } else {
-    // 4 waves, two independent work-groups per CU
-    hipLaunchKernelGGL((attn_past_kernel<4>), grid, dim3(256), 0, st, a);
+    // 4 waves: from K and V rows in 32-key slices (block a multiple of 32),
+    // three work-groups per CU; otherwise two, with register staging
+    if (a.block % 32 == 0)
+      hipLaunchKernelGGL((attn_past_rows_kernel<4, 3, 1>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_past_kernel<4>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -931,10 +1324,17 @@ int launch_attn_own(const OwnArgs& a, hipStream_t st) {
   const int64_t nblk = a.cnt / a.block;
   const int64_t per_xcd = (nblk * tiles_per_block * a.hkv + 7) / 8;  // see attn_own_kernel
   const dim3 grid((unsigned)(8 * per_xcd));
-  if (a.kimg && a.block % KT == 0)
+  if (a.kimg && a.block % KT == 0) {
+    if (a.own_t * a.g > OWN_NW * 32) return -1;
     hipLaunchKernelGGL(attn_own_kernel<true>, grid, dim3(OWN_NW * 64), 0, st, a);
-  else
+  } else if (a.block % 32 == 0) {
+    // 128-row tiles from K and V rows, 32-key slices: three work-groups per CU
+    if (a.own_t * a.g > 128) return -1;
+    hipLaunchKernelGGL((attn_own_rows_kernel<4, 3, 1>), grid, dim3(256), 0, st, a);
+  } else {
+    if (a.own_t * a.g > OWN_NW * 32) return -1;
     hipLaunchKernelGGL(attn_own_kernel<false>, grid, dim3(OWN_NW * 64), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -40,7 +40,6 @@ int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks, bool allow_imag
   if (s.seqlen > (int64_t(1) << 31) / s.hq) return MOBA_ERR_SHAPE;
 
   q.gate_t = std::max(1, kGateRows / q.g);
-  q.own_t = std::max(1, kOwnRows / q.g);
 
   // per (row, past block) pair: the normalised partial o in bf16 plus its lse in fp32
   const uint64_t per_block_partial =
@@ -91,6 +90,8 @@ int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks, bool allow_imag
   // blocks are long, e.g. block_size = seqlen: dense causal attention)
   q.kv_image = allow_image && s.dtype == MOBA_DTYPE_BF16 && s.block % kSliceKeys == 0 &&
                (q.kp > 0 ? q.tile_rows == kTileRowsImage : s.block >= kOwnImageMinBlock);
+  const bool own_rows = s.dtype == MOBA_DTYPE_BF16 && !q.kv_image && s.block % kRowSliceKeys == 0;
+  q.own_t = std::max(1, (own_rows ? kOwnRowsSmall : kOwnRows) / q.g);
   const size_t img = q.kv_image ? (size_t)s.batch * s.hkv * s.seqlen * s.d * sizeof(uint16_t) : 0;
   q.off_kimg = take(img);
   q.off_vimg = take(img);

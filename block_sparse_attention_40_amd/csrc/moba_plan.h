@@ -17,8 +17,13 @@ constexpr int kTileRowsLarge = 256;
 constexpr int kTileRowsImage = 384;
 // Mean list length from which the large tile is used.
 constexpr int64_t kLargeTileMinRows = 2048;
-// Query rows of one own-block attention tile (8 waves x 32 rows).
+// Query rows of one own-block attention tile: 8 waves x 32 rows, or 4 waves
+// x 32 rows when the tile reads K and V rows in 32-key slices (bf16, no
+// slice images, block a multiple of 32), three work-groups per CU.
 constexpr int kOwnRows = 256;
+constexpr int kOwnRowsSmall = 128;
+// Keys per LDS slice of the kernels that read K and V rows directly.
+constexpr int kRowSliceKeys = 32;
 // Largest query-head group (num_q_heads / num_kv_heads) the tiles support.
 constexpr int kMaxGroup = 128;
 // Blocks per tile of the bf16 gate's score MFMAs.

@@ -141,6 +141,10 @@ SMALL = [
     small("gate_n64_k16", "bf16", 1, 4096, 4, 1, 128, 64, 16),
     small("gate_n64_k20", "bf16", 1, 4096, 2, 2, 128, 64, 20),
     small("gate_noncausal_n40", "bf16", 1, 2560, 2, 1, 128, 64, 6, causal=False),
+    # blocks of five 32-key slices (not whole 64-key slices) and g = 3: the
+    # direct-load row kernels' three-buffer pipeline over an odd slice count,
+    # 42-position own tiles with a masked last slice
+    small("rows_b160_g3", "bf16", 1, 1920, 6, 2, 128, 160, 4),
     small("f32_d128_gqa", "f32", 1, 1024, 4, 2, 128, 128, 3),
     small("f32_noncausal", "f32", 1, 512, 2, 1, 64, 64, 3, causal=False),
     # more than 32 past blocks to rank (the gate's rounds): 2 and 4 rounds on
