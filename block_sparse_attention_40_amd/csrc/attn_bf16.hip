@@ -1324,13 +1324,14 @@ int launch_attn_own(const OwnArgs& a, hipStream_t st) {
   const int64_t nblk = a.cnt / a.block;
   const int64_t per_xcd = (nblk * tiles_per_block * a.hkv + 7) / 8;  // see attn_own_kernel
   const dim3 grid((unsigned)(8 * per_xcd));
-  if (a.kimg && a.block % KT == 0) {
-    if (a.own_t * a.g > OWN_NW * 32) return -1;
-    hipLaunchKernelGGL(attn_own_kernel<true>, grid, dim3(OWN_NW * 64), 0, st, a);
-  } else if (a.block % 32 == 0) {
+  if (a.rows) {
     // 128-row tiles from K and V rows, 32-key slices: three work-groups per CU
     if (a.own_t * a.g > 128) return -1;
+    if (a.block % 32 != 0) return -1;
     hipLaunchKernelGGL((attn_own_rows_kernel<4, 3, 1>), grid, dim3(256), 0, st, a);
+  } else if (a.kimg && a.block % KT == 0) {
+    if (a.own_t * a.g > OWN_NW * 32) return -1;
+    hipLaunchKernelGGL(attn_own_kernel<true>, grid, dim3(OWN_NW * 64), 0, st, a);
   } else {
     if (a.own_t * a.g > OWN_NW * 32) return -1;
     hipLaunchKernelGGL(attn_own_kernel<false>, grid, dim3(OWN_NW * 64), 0, st, a);

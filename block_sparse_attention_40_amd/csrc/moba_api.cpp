@@ -351,7 +351,7 @@ int fwd_impl(const void* q, const void* k, const void* v, int64_t batch, int64_t
       oa.q = q; oa.k = k; oa.v = v; oa.out = out; oa.part_o = part_o; oa.part_lse = part_lse;
       oa.part_rows = part_rows;
       oa.seqlen = seqlen; oa.n = p.n; oa.t0 = t0; oa.cnt = cnt; oa.hq = num_q_heads; oa.hkv = num_kv_heads;
-      oa.block = block_size; oa.kp = p.kp; oa.g = p.g; oa.own_t = p.own_t; oa.bb = (int32_t)bb;
+      oa.block = block_size; oa.kp = p.kp; oa.g = p.g; oa.own_t = p.own_t; oa.rows = p.own_rows ? 1 : 0; oa.bb = (int32_t)bb;
       oa.causal = causal ? 1 : 0; oa.scale_log2 = sl2; oa.kimg = kimg; oa.vimg = vimg; oa.lse = lse;
       {
         StageScope sc(MOBA_STAGE_OWN, s, 4.0 * D * own_keys);

@@ -71,6 +71,7 @@ struct OwnArgs {
   float* lse;              // [batch, hq, seqlen] row log-sum-exp (natural log), or null
   int64_t seqlen, n, t0, cnt;
   int32_t hq, hkv, block, kp, g, own_t, bb, causal;
+  int32_t rows;            // 128-row tiles read from K and V rows (block a multiple of 32)
   float scale_log2;
 };
 

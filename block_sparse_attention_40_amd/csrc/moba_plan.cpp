@@ -90,8 +90,10 @@ int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks, bool allow_imag
   // blocks are long, e.g. block_size = seqlen: dense causal attention)
   q.kv_image = allow_image && s.dtype == MOBA_DTYPE_BF16 && s.block % kSliceKeys == 0 &&
                (q.kp > 0 ? q.tile_rows == kTileRowsImage : s.block >= kOwnImageMinBlock);
-  const bool own_rows = s.dtype == MOBA_DTYPE_BF16 && !q.kv_image && s.block % kRowSliceKeys == 0;
-  q.own_t = std::max(1, (own_rows ? kOwnRowsSmall : kOwnRows) / q.g);
+  // own-block tiles: from the images when they exist (256 rows), else from
+  // K and V rows in 32-key slices (128 rows) when the block allows it
+  q.own_rows = s.dtype == MOBA_DTYPE_BF16 && !q.kv_image && s.block % kRowSliceKeys == 0;
+  q.own_t = std::max(1, (q.own_rows ? kOwnRowsSmall : kOwnRows) / q.g);
   const size_t img = q.kv_image ? (size_t)s.batch * s.hkv * s.seqlen * s.d * sizeof(uint16_t) : 0;
   q.off_kimg = take(img);
   q.off_vimg = take(img);

@@ -57,6 +57,7 @@ struct Plan {
   int32_t g;            // query heads per KV head
   int32_t gate_t;       // query positions per gate work-group
   int32_t own_t;        // query positions per own-block tile
+  bool own_rows;        // own-block tiles of 128 rows from K and V rows (else 256, images or register staging)
   int32_t tile_rows;    // rows per past-block attention tile
   int64_t chunk_blocks; // query blocks processed per chunk
   int64_t gate_wg;      // gate work-groups per KV head per chunk
