@@ -139,7 +139,24 @@ def measure(M, W, w, steps, warmup, log, gate="mean", graph=False, max_chunk_blo
     return res, inputs, stages
 
 
-def roofline(stages, steps):
+def past_kernel_name(M, w):
+    """The past-block kernel the forward launches on workload w, from its
+    plan: 384-row tiles over the slice images, 256-row tiles through
+    registers, or 128-row tiles (straight from K and V rows when the block is
+    a multiple of 32 keys)."""
+    dt = M.DTYPE_BF16 if w.dtype == "bf16" else M.DTYPE_F32
+    nbytes = M.workspace_bytes(w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, dt, w.block_size,
+                               w.topk, w.causal)
+    plan = M.plan_info(w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, dt, w.block_size, w.topk,
+                       w.causal, nbytes)
+    if plan["tile_rows"] == 384:
+        return PAST_KERNEL
+    if plan["tile_rows"] == 256:
+        return "moba::attn_past_kernel<8>"
+    return "moba::attn_past_rows_kernel<4, 3, 1>" if w.block_size % 32 == 0 else "moba::attn_past_kernel<4>"
+
+
+def roofline(stages, steps, kernel=PAST_KERNEL, workload="gqa32x8_1m"):
     past = stages["attn_past"]
     if not past["launches"]:
         return None
@@ -150,9 +167,10 @@ def roofline(stages, steps):
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
         src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if rec.get("kernel_source_sha256") == src_hash:
+        if (rec.get("kernel_source_sha256") == src_hash and rec.get("kernel") == kernel
+                and rec.get("workload") == workload):
             traffic = rec.get("hbm_bytes_per_launch")
-    return {"kernel": PAST_KERNEL, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+    return {"kernel": kernel, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
             "avg_launch_ms": avg_ms, "launches_per_step": past["launches"] / steps,
             "flops_per_launch": flops_per_launch}
@@ -1111,7 +1129,7 @@ def main():
         "attention_tflops": res["attention_tflops"],
         "mfma_util_attention": res["mfma_util_attention"],
         "stages": res["stages"],
-        "roofline": roofline(stages, args.steps),
+        "roofline": roofline(stages, args.steps, past_kernel_name(M, w), w.name),
     }
     if args.secondary:
         w2 = W.WORKLOADS[args.secondary]
