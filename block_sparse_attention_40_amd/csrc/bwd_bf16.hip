@@ -131,18 +131,17 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   const int r = wave * 32 + (lane & 31);
   const bool valid = r < cnt;
   const int rr = valid ? r : 0;
-  int64_t t, pidx;
+  int64_t t;
   int h;
+  int32_t entry = 0;
   if constexpr (!kOwn) {
-    const int32_t entry = a.entries[start + rr];
+    entry = a.entries[start + rr];
     const int64_t local_row = entry / a.kp;
     t = a.t0 + local_row / a.hq;
     h = (int)(local_row % a.hq);
-    pidx = local_row * a.kps + entry % a.kp;
   } else {
     h = hk * a.g + rr % a.g;
     t = blk * a.block + own_p0 + rr / a.g;
-    pidx = ((t - a.t0) * a.hq + h) * a.kps + a.kp;  // the own slot
   }
   const int64_t grow = ((int64_t)a.bb * a.seqlen + t) * a.hq + h;
   bf16x8 qb[8], db[8];
@@ -198,7 +197,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   };
   auto publish = [] { asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory"); };
   auto slice = [&](const char* buf, int sl) {
-    const int64_t key_base = blk * a.block + (int64_t)sl * BKT;  // absolute position of key 0 of the slice
+    // own block: key kc of the slice (slice-relative, accumulator row
+    // kc + 4 lg) is visible iff kc <= lim, one int32 limit per slice
+    int lim = 0;
+    if constexpr (kOwn) lim = (int)own_p0 + rr / a.g - sl * BKT - 4 * lg;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s, dp;
@@ -210,6 +212,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(buf + BIMG + kofs + st * 2048 + kb * 512);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[st], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, db[st], dp, 0, 0, 0);
+        // own block: operands read four steps at a time (the mask's registers
+        // would otherwise push the kernel past 256)
+        if constexpr (kOwn)
+          if (st == 3) __builtin_amdgcn_sched_barrier(0);
       }
       // dS^T, packed as the B operand of dQ^T (same order as the forward's P^T)
       uint32_t pk[8];
@@ -218,9 +224,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
         float p0 = fast_exp2(__builtin_fmaf(s[e], c, -lse2));
         float p1 = fast_exp2(__builtin_fmaf(s[e + 1], c, -lse2));
         if constexpr (kOwn) {
-          const int64_t k0 = key_base + kb * 32 + acc_row(e, lg);
-          if (k0 > t) p0 = 0.f;
-          if (k0 + 1 > t) p1 = 0.f;
+          const int kc = kb * 32 + 8 * (e >> 2) + (e & 3);
+          if (kc > lim) p0 = 0.f;
+          if (kc + 1 > lim) p1 = 0.f;
         }
         pk[e >> 1] = pack_bf16x2(p0 * (dp[e] - dl), p1 * (dp[e + 1] - dl));
       }
@@ -248,6 +254,14 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   drain_vmem();  // every slice load landed before the work-group ends
 
   if (valid) {
+    // the row's contribution slot: its past slot, or the own slot kp
+    int64_t pidx;
+    if constexpr (!kOwn) {
+      const int64_t local_row = entry / a.kp;
+      pidx = local_row * a.kps + entry % a.kp;
+    } else {
+      pidx = ((blk * a.block + own_p0 + rr / a.g - a.t0) * a.hq + h) * a.kps + a.kp;
+    }
     // lane holds d = 32 b + 8 q + 4 lg + i (i = 0..3) of its row
     float* dst = a.dq_part + pidx * BD;
 #pragma unroll
