@@ -681,21 +681,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // barrier publish a slice to every wave, and the asm memory clobbers keep
   // the LDS reads on their side of it.  A buffer is loaded again only after
   // the barrier that ends the slice that read it.
-  // each image is 16 chunks of 64 units; wave w loads chunks w % 16 and
-  // 15 - w % 16 (with 12 waves chunks 4..11 are loaded twice, same data)
-  static_assert(NW == 8 || NW == 12, "two chunks per image and wave");
+  // the two images are 32 chunks of 64 units (chunk c < 16: K image chunk
+  // c, else V^T image chunk c - 16); wave w loads chunks w, w + NW, ...
+  // (with 12 waves, waves 0..7 three chunks and waves 8..11 two)
+  static_assert(NW == 8 || NW == 12, "8 or 12 waves");
+  constexpr int kMaxPer = (32 + NW - 1) / NW;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto dma = [&](char* lb, int sl) {
     const uint16_t* ks = kimg + src(sl);
     const uint16_t* vs = vimg + src(sl);
     typedef __attribute__((address_space(3))) char lds_char;
     const uint32_t lb_addr = (uint32_t)(uintptr_t)((lds_char*)lb);
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int chunk = NW == 8 ? wave + 8 * x : (x == 0 ? wave : 15 - wave);
-      const int u = chunk * 64 + lane;
-      const uint32_t wb = __builtin_amdgcn_readfirstlane(lb_addr + (uint32_t)(chunk * 64 * 16));
-      lds_dma16(wb, ks + u * 8);
-      lds_dma16(wb + IMG_BYTES, vs + u * 8);
+    for (int x = 0; x < kMaxPer; ++x) {
+      const int c = wv + NW * x;
+      if (c < 32) {
+        const int chunk = c & 15;
+        const int u = chunk * 64 + lane;
+        const uint32_t wb = __builtin_amdgcn_readfirstlane(lb_addr + (uint32_t)((c >> 4) * IMG_BYTES + chunk * 64 * 16));
+        lds_dma16(wb, (c < 16 ? ks : vs) + u * 8);
+      }
     }
   };
   auto slice = [&](const char* buf) {
@@ -706,11 +711,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     pv_img(buf + IMG_BYTES + vofs, pk, R);
   };
 
-  // wait until at most one slice's loads (this thread's 4) are in flight,
-  // then the barrier; no fence, so the younger slice's loads stay in flight
-  // (a fence would wait for every load into LDS); the memory clobber keeps
-  // the compiler from moving LDS accesses across
-  auto publish = [] { asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory"); };
+  // wait until at most one slice's loads (this wave's 4, 3 or 2) are in
+  // flight, then the barrier; no fence, so the younger slice's loads stay
+  // in flight (a fence would wait for every load into LDS); the memory
+  // clobber keeps the compiler from moving LDS accesses across
+  auto publish = [&] {
+    if (NW == 8)
+      asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    else if (wv < 8)
+      asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+  };
   drain_vmem();  // the query rows in before any slice load goes out
   dma(lb0, 0);
   dma(lb1, 1);
