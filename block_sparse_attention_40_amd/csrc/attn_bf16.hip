@@ -21,7 +21,7 @@
 //   attn_past_rows_kernel / attn_own_rows_kernel: 128-row tiles that load K
 //       and V rows as they are straight into LDS in 32-key slices and read
 //       the V^T operand with the transposing LDS load; three work-groups per
-//       CU (short lists, blocks of a few hundred keys).
+//       CU (the past blocks of short lists; the own block of most shapes).
 //
 // Work split inside a work-group: every wave owns 32 query rows; 4, 8 or 12
 // waves share each K/V slice staged in LDS, and two or three waves per SIMD

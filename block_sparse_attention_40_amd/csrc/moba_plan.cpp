@@ -90,9 +90,13 @@ int make_plan(const Shape& s, Plan* p, int64_t max_chunk_blocks, bool allow_imag
   // blocks are long, e.g. block_size = seqlen: dense causal attention)
   q.kv_image = allow_image && s.dtype == MOBA_DTYPE_BF16 && s.block % kSliceKeys == 0 &&
                (q.kp > 0 ? q.tile_rows == kTileRowsImage : s.block >= kOwnImageMinBlock);
-  // own-block tiles: from the images when they exist (256 rows), else from
-  // K and V rows in 32-key slices (128 rows) when the block allows it
-  q.own_rows = s.dtype == MOBA_DTYPE_BF16 && !q.kv_image && s.block % kRowSliceKeys == 0;
+  // own-block tiles: 128 rows from K and V rows in 32-key slices (three
+  // work-groups per CU) when the block allows it; where the slice images
+  // exist, only with past blocks and blocks of at least kOwnRowsMinBlock
+  // keys (dense attention and short blocks run faster in 256-row tiles from
+  // the images)
+  q.own_rows = s.dtype == MOBA_DTYPE_BF16 && s.block % kRowSliceKeys == 0 &&
+               (!q.kv_image || (q.kp > 0 && s.block >= kOwnRowsMinBlock));
   q.own_t = std::max(1, (q.own_rows ? kOwnRowsSmall : kOwnRows) / q.g);
   const size_t img = q.kv_image ? (size_t)s.batch * s.hkv * s.seqlen * s.d * sizeof(uint16_t) : 0;
   q.off_kimg = take(img);
