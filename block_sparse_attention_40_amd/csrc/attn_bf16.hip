@@ -855,6 +855,90 @@ struct RowsCfg {
   static constexpr int WPS = WPS0 < 1 ? 1 : (WPS0 > 3 ? 3 : WPS0);  // at most three (168 registers)
 };
 
+// The loads of one slice of K and V rows straight into an LDS buffer.  Load
+// j of a tensor covers rows 4 j .. 4 j + 3 (lane / 16 picks the row, and the
+// lane fetches the unit that the row's rotation puts at LDS position
+// lane & 15); wave w issues loads w, w + NW, ...  kbase / vbase: row 0 of
+// the block in K / V, rs: the row stride in elements.
+template <int NW, int NBUF, int NKB>
+struct RowSliceLoader {
+  using C = RowsCfg<NW, NBUF, NKB>;
+  const bf16raw* kbase;
+  const bf16raw* vbase;
+  int64_t rs;
+  int nsl, wave;
+  int goff[C::PER];
+  __device__ __forceinline__ RowSliceLoader(const bf16raw* k, const bf16raw* v, int64_t rs_, int nsl_, int wave_,
+                                            int lane)
+      : kbase(k), vbase(v), rs(rs_), nsl(nsl_), wave(wave_) {
+#pragma unroll
+    for (int i = 0; i < C::PER; ++i) {
+      const int row = 4 * (wave + NW * i) + (lane >> 4);
+      goff[i] = row * (int)rs + (((lane & 15) - row_rot(row)) & 15) * 8;
+    }
+  }
+  // slice sl into buf; past the last slice the loads repeat it, so every
+  // pipeline step issues the same number of loads
+  __device__ __forceinline__ void operator()(char* buf, int sl) const {
+    const int64_t so = (int64_t)(sl < nsl ? sl : nsl - 1) * C::SK * rs;
+    typedef __attribute__((address_space(3))) char lds_char;
+    const uint32_t lb_addr = (uint32_t)(uintptr_t)((lds_char*)buf);
+#pragma unroll
+    for (int i = 0; i < C::PER; ++i) {
+      const uint32_t wb = __builtin_amdgcn_readfirstlane(lb_addr + (uint32_t)((wave + NW * i) * 1024));
+      lds_dma16(wb, kbase + so + goff[i]);
+      lds_dma16(wb + C::TBYTES, vbase + so + goff[i]);
+    }
+  }
+};
+
+// Slices 0 .. nsl - 1 through the NBUF buffers lb: load(buf, sl) issues a
+// slice's loads into LDS, body(sl, buf) computes it.  The loads are inline
+// asm, so the compiler neither tracks them nor waits for them: each barrier
+// that publishes a slice first waits (vmcnt) until only the younger slices'
+// loads (2 PER per wave and slice) are in flight, and the asm memory clobber
+// keeps the LDS reads on their side of it.  A buffer is loaded again only
+// after the barrier that ends the slice that read it.  With two buffers the
+// loads of slice s+1 go out at the start of slice s; with three, those of
+// slice s+2.  The caller's own loads must have landed (drain_vmem) before.
+template <int NBUF, int PER, int BUF, typename Load, typename Body>
+__device__ __forceinline__ void run_row_slices(char (*lb)[BUF], int nsl, const Load& load, Body&& body) {
+  static_assert(NBUF == 2 || (NBUF == 3 && (2 * PER == 4 || 2 * PER == 8)), "two buffers, or three (vmcnt 4 or 8)");
+  if constexpr (NBUF == 2) {
+    auto publish = [] { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
+    load(lb[0], 0);
+    publish();
+    for (int sl = 0; sl < nsl; ++sl) {
+      if (sl + 1 < nsl) load(lb[(sl + 1) & 1], sl + 1);
+      body(sl, lb[sl & 1]);
+      publish();
+    }
+  } else {
+    auto publish = [] {
+      if constexpr (2 * PER == 8)
+        asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    };
+    load(lb[0], 0);
+    load(lb[1], 1);
+    publish();
+    auto step = [&](int sl, char* cur, char* nx2) {
+      load(nx2, sl + 2);  // past the end: the last slice again
+      body(sl, cur);
+      publish();  // slice sl + 1 in, in every wave
+    };
+    for (int sl = 0; sl < nsl; sl += 3) {
+      step(sl, lb[0], lb[2]);
+      if (sl + 1 >= nsl) break;
+      step(sl + 1, lb[1], lb[0]);
+      if (sl + 2 >= nsl) break;
+      step(sl + 2, lb[2], lb[1]);
+    }
+    drain_vmem();
+  }
+}
+
 template <int NW, int NBUF, int NKB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RowsCfg<NW, NBUF, NKB>::WPS,
                                                                          RowsCfg<NW, NBUF, NKB>::WPS))) void
@@ -896,78 +980,17 @@ attn_past_rows_kernel(PastArgs a) {
   const int nsl = a.block / C::SK;
   const int64_t rs = (int64_t)a.hkv * HD;
   const int64_t base = ((int64_t)a.bb * a.seqlen + blk * a.block) * rs + hk * HD;
-  const bf16raw* kblk = reinterpret_cast<const bf16raw*>(a.k) + base;
-  const bf16raw* vblk = reinterpret_cast<const bf16raw*>(a.v) + base;
-  // load j of a tensor: rows 4 j + lane / 16, LDS position lane & 15 of its
-  // row, so the lane fetches the unit that the row's rotation puts there
-  int goff[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int j = wave + NW * i;
-    const int row = 4 * j + (lane >> 4);
-    goff[i] = row * (int)rs + (((lane & 15) - row_rot(row)) & 15) * 8;
-  }
-  // past the last slice the loads repeat it, so every iteration issues the same loads
-  auto dma = [&](char* buf, int sl) {
-    const int64_t so = (int64_t)(sl < nsl ? sl : nsl - 1) * C::SK * rs;
-    typedef __attribute__((address_space(3))) char lds_char;
-    const uint32_t lb_addr = (uint32_t)(uintptr_t)((lds_char*)buf);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint32_t wb = __builtin_amdgcn_readfirstlane(lb_addr + (uint32_t)((wave + NW * i) * 1024));
-      lds_dma16(wb, kblk + so + goff[i]);
-      lds_dma16(wb + C::TBYTES, vblk + so + goff[i]);
-    }
-  };
+  const RowSliceLoader<NW, NBUF, NKB> load(reinterpret_cast<const bf16raw*>(a.k) + base,
+                                           reinterpret_cast<const bf16raw*>(a.v) + base, rs, nsl, wave, lane);
   const float c = a.scale_log2;
-  auto slice = [&](const char* buf) {
+  drain_vmem();  // the query rows in before any slice load goes out
+  run_row_slices<NBUF, PER>(lb, nsl, load, [&](int, const char* buf) {
     f32x16 sc[NKB];
     uint32_t pk[NKB][8];
     qk_rows<NKB>(buf, R.qb, sc, ro);
     softmax_p<false, NoMask, NKB>(sc, R, c, lane, NoMask{}, pk);
     pv_rows<NKB>(buf + C::TBYTES, pk, R, ro);
-  };
-
-  // The loads into LDS are inline asm, so the compiler neither tracks them
-  // nor waits for them: each barrier that publishes a slice first waits
-  // (vmcnt) until only the younger slices' loads are in flight, and the asm
-  // memory clobber keeps the LDS reads on their side of it.  A buffer is
-  // loaded again only after the barrier that ends the slice that read it.
-  drain_vmem();  // the query rows in before any slice load goes out
-  if constexpr (NBUF == 2) {
-    auto publish = [] { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
-    dma(lb[0], 0);
-    publish();
-    for (int sl = 0; sl < nsl; ++sl) {
-      if (sl + 1 < nsl) dma(lb[(sl + 1) & 1], sl + 1);
-      slice(lb[sl & 1]);
-      publish();
-    }
-  } else {
-    static_assert(NBUF == 2 || 2 * PER == 8 || 2 * PER == 4, "vmcnt of one slice");
-    auto publish = [] {
-      if constexpr (2 * PER == 8)
-        asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-    };
-    dma(lb[0], 0);
-    dma(lb[1], 1);
-    publish();
-    auto step = [&](int sl, char* cur, char* nx2) {
-      dma(nx2, sl + 2);  // past the end: the last slice again
-      slice(cur);
-      publish();  // slice sl + 1 in, in every wave
-    };
-    for (int sl = 0; sl < nsl; sl += 3) {
-      step(sl, lb[0], lb[2]);
-      if (sl + 1 >= nsl) break;
-      step(sl + 1, lb[1], lb[0]);
-      if (sl + 2 >= nsl) break;
-      step(sl + 2, lb[2], lb[1]);
-    }
-    drain_vmem();
-  }
+  });
 
   const int lg = lane >> 5;
   const float ltot = pair_sum(R.l);
@@ -1209,30 +1232,12 @@ attn_own_rows_kernel(OwnArgs a) {
     ro.init(lane);
     const int64_t rs = (int64_t)a.hkv * HD;
     const int64_t base = ((int64_t)a.bb * a.seqlen + j * a.block) * rs + hk * HD;
-    const bf16raw* kblk = reinterpret_cast<const bf16raw*>(a.k) + base;
-    const bf16raw* vblk = reinterpret_cast<const bf16raw*>(a.v) + base;
-    int goff[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int jj = wave + NW * i;
-      const int row = 4 * jj + (lane >> 4);
-      goff[i] = row * (int)rs + (((lane & 15) - row_rot(row)) & 15) * 8;
-    }
     // keys past `last` in the last slice exist (the block is whole slices)
-    // and are masked like every key after the query; past the last slice the
-    // loads repeat it
-    auto dma = [&](char* buf, int sl) {
-      const int64_t so = (int64_t)(sl < nsl ? sl : nsl - 1) * C::SK * rs;
-      typedef __attribute__((address_space(3))) char lds_char;
-      const uint32_t lb_addr = (uint32_t)(uintptr_t)((lds_char*)buf);
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const uint32_t wb = __builtin_amdgcn_readfirstlane(lb_addr + (uint32_t)((wave + NW * i) * 1024));
-        lds_dma16(wb, kblk + so + goff[i]);
-        lds_dma16(wb + C::TBYTES, vblk + so + goff[i]);
-      }
-    };
-    auto slice = [&](int sl, const char* buf) {
+    // and are masked like every key after the query
+    const RowSliceLoader<NW, NBUF, NKB> load(reinterpret_cast<const bf16raw*>(a.k) + base,
+                                             reinterpret_cast<const bf16raw*>(a.v) + base, rs, nsl, wave, lane);
+    drain_vmem();  // the query rows in before any slice load goes out
+    run_row_slices<NBUF, PER>(lb, nsl, load, [&](int sl, const char* buf) {
       const int64_t k0 = (int64_t)sl * C::SK;
       if (k0 <= wmax) {
         f32x16 sc[NKB];
@@ -1242,42 +1247,7 @@ attn_own_rows_kernel(OwnArgs a) {
         softmax_p<false, NoMask, NKB>(sc, R, c, lane, NoMask{}, pk);
         pv_rows<NKB>(buf + C::TBYTES, pk, R, ro);
       }
-    };
-    drain_vmem();  // the query rows in before any slice load goes out
-    if constexpr (NBUF == 2) {
-      auto publish = [] { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
-      dma(lb[0], 0);
-      publish();
-      for (int sl = 0; sl < nsl; ++sl) {
-        if (sl + 1 < nsl) dma(lb[(sl + 1) & 1], sl + 1);
-        slice(sl, lb[sl & 1]);
-        publish();
-      }
-    } else {
-      static_assert(NBUF == 2 || 2 * PER == 8 || 2 * PER == 4, "vmcnt of one slice");
-      auto publish = [] {
-        if constexpr (2 * PER == 8)
-          asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-      };
-      dma(lb[0], 0);
-      dma(lb[1], 1);
-      publish();
-      auto step = [&](int sl, char* cur, char* nx2) {
-        dma(nx2, sl + 2);
-        slice(sl, cur);
-        publish();
-      };
-      for (int sl = 0; sl < nsl; sl += 3) {
-        step(sl, lb[0], lb[2]);
-        if (sl + 1 >= nsl) break;
-        step(sl + 1, lb[1], lb[0]);
-        if (sl + 2 >= nsl) break;
-        step(sl + 2, lb[2], lb[1]);
-      }
-      drain_vmem();
-    }
+    });
   }
 
   for (int64_t s = 0; s < nslot; ++s) {
