@@ -350,13 +350,20 @@ def moba_decode_means(k_cache: torch.Tensor, cache_lens: torch.Tensor, block_siz
     """Mean key of every complete block of every cached sequence:
     mu_cache [b, Hkv, max_len / block_size, D] fp32 (entries of incomplete or
     unused blocks are left as they are; a new tensor starts at zero)."""
-    _check_dev(k_cache, cache_lens)
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [batch, max_len, Hkv, D]")
     b, Lmax, Hkv, D = k_cache.shape
-    if cache_lens.dtype != torch.int32 or cache_lens.numel() != b:
-        raise ValueError("cache_lens must be int32 [batch]")
+    dt = _dtype_code(k_cache)
+    shape = (b, Hkv, Lmax // max(block_size, 1), D)
+    _check_shape(cache_lens, "cache_lens", (b,), torch.int32)
+    if mu_cache is not None:
+        _check_shape(mu_cache, "mu_cache", shape, torch.float32)
+    _check_dev(k_cache)
+    _check_on(cache_lens, "cache_lens", k_cache.device)
     if mu_cache is None:
-        mu_cache = torch.zeros((b, Hkv, Lmax // max(block_size, 1), D), dtype=torch.float32, device=k_cache.device)
-    st = lib.moba_decode_means(k_cache.data_ptr(), cache_lens.data_ptr(), b, Lmax, Hkv, D, _dtype_code(k_cache),
+        mu_cache = torch.zeros(shape, dtype=torch.float32, device=k_cache.device)
+    _check_on(mu_cache, "mu_cache", k_cache.device)
+    st = lib.moba_decode_means(k_cache.data_ptr(), cache_lens.data_ptr(), b, Lmax, Hkv, D, dt,
                                block_size, mu_cache.data_ptr(), _stream_ptr(k_cache.device))
     if st != MOBA_OK:
         raise MobaError(st, "moba_decode_means")
@@ -371,18 +378,21 @@ def moba_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     Hkv, D]; mu_cache fp32 [b, Hkv, max_len / block_size, D] (moba_decode_means,
     kept current by this call); cache_lens int32 [b] (the new token included).
     Returns (out [b, Hq, D], sel_idx [b, Hq, topk] int32 or None)."""
-    _check_dev(q, k_cache, v_cache, mu_cache, cache_lens)
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [batch, Hq, D] and k_cache [batch, max_len, Hkv, D]")
     b, Hq, D = q.shape
-    _, Lmax, Hkv, _ = k_cache.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"num_q_heads {Hq} must be a multiple of num_kv_heads {Hkv}")
     dt = _dtype_code(q)
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or k_cache.shape != v_cache.shape:
-        raise ValueError("q and the caches must share dtype; k_cache and v_cache must share shape")
-    if cache_lens.dtype != torch.int32 or cache_lens.numel() != b:
-        raise ValueError("cache_lens must be int32 [batch]")
-    if mu_cache.dtype != torch.float32 or tuple(mu_cache.shape) != (b, Hkv, Lmax // max(block_size, 1), D):
-        raise ValueError("mu_cache must be fp32 [batch, Hkv, max_len / block_size, D]")
-    if k_cache.dim() != 4 or k_cache.shape[0] != b or k_cache.shape[3] != D or Hq % max(Hkv, 1) != 0:
-        raise ValueError("k_cache / v_cache must be [batch, max_len, Hkv, D] matching q [batch, Hq, D]")
+    # every extent the C ABI uses comes from q and k_cache: check the rest
+    _check_shape(k_cache, "k_cache", (b, Lmax, Hkv, D), q.dtype)
+    _check_shape(v_cache, "v_cache", (b, Lmax, Hkv, D), q.dtype)
+    _check_shape(mu_cache, "mu_cache", (b, Hkv, Lmax // max(block_size, 1), D), torch.float32)
+    _check_shape(cache_lens, "cache_lens", (b,), torch.int32)
+    _check_dev(q)
+    for t_, name in ((k_cache, "k_cache"), (v_cache, "v_cache"), (mu_cache, "mu_cache"), (cache_lens, "cache_lens")):
+        _check_on(t_, name, q.device)
     if out is None:
         out = torch.empty_like(q)
     _check_like(out, "out", q.shape, q.dtype, q.device)

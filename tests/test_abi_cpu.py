@@ -324,6 +324,42 @@ def test_binding_checks_shapes_before_calling():
                          torch.device("cpu"))
 
 
+def test_decode_binding_checks_shapes_before_calling():
+    """The decode wrappers check every tensor against q and k_cache (the
+    extents the C ABI uses) before anything reaches the library, a
+    caller's mu_cache included (moba_decode_means writes into it)."""
+    b, L, Hq, Hkv, D, B = 2, 1024, 4, 2, 128, 128
+    q = torch.zeros(b, Hq, D, dtype=torch.bfloat16)
+    kc = torch.zeros(b, L, Hkv, D, dtype=torch.bfloat16)
+    mu = torch.zeros(b, Hkv, L // B, D)
+    lens = torch.zeros(b, dtype=torch.int32)
+    with pytest.raises(ValueError, match="mu_cache must have shape"):
+        M.moba_decode_means(kc, lens, B, mu_cache=torch.zeros(b, Hkv, L // B - 1, D))
+    with pytest.raises(ValueError, match="mu_cache must be"):
+        M.moba_decode_means(kc, lens, B, mu_cache=mu.double())
+    with pytest.raises(ValueError, match="cache_lens must have shape"):
+        M.moba_decode_means(kc, torch.zeros(b + 1, dtype=torch.int32), B)
+    with pytest.raises(ValueError, match="cache_lens must be"):
+        M.moba_decode_means(kc, lens.long(), B)
+    with pytest.raises(ValueError, match="v_cache must have shape"):
+        M.moba_decode_fwd(q, kc, kc[:, : L // 2].contiguous(), mu, lens, B, 3)
+    with pytest.raises(ValueError, match="k_cache must be"):
+        M.moba_decode_fwd(q, kc.float(), kc, mu, lens, B, 3)
+    with pytest.raises(ValueError, match="k_cache must have shape"):
+        M.moba_decode_fwd(q, torch.zeros(b, L, Hkv, 64, dtype=torch.bfloat16), kc, mu, lens, B, 3)
+    with pytest.raises(ValueError, match="mu_cache must have shape"):
+        M.moba_decode_fwd(q, kc, kc, torch.zeros(b, Hkv, L // B, 64), lens, B, 3)
+    with pytest.raises(ValueError, match="cache_lens must have shape"):
+        M.moba_decode_fwd(q, kc, kc, mu, lens[:1], B, 3)
+    with pytest.raises(ValueError, match="multiple of num_kv_heads"):
+        M.moba_decode_fwd(torch.zeros(b, 3, D, dtype=torch.bfloat16), kc, kc, mu, lens, B, 3)
+    with pytest.raises(ValueError, match="must be \\[batch, Hq, D\\]"):
+        M.moba_decode_fwd(q[0], kc, kc, mu, lens, B, 3)
+    # shapes right, CPU tensors: refused by the device check
+    with pytest.raises(ValueError, match="live on the GPU"):
+        M.moba_decode_fwd(q, kc, kc, mu, lens, B, 3)
+
+
 def test_noalloc_entry_point_checks_on_the_host():
     """The fixed-scratch forward validates like moba_attn_fwd and refuses
     shapes whose smallest workspace exceeds its scratch, all before it looks
