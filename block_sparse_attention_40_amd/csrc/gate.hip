@@ -827,7 +827,13 @@ static void launch_gate_valu(const GateArgs& a, int kcap, hipStream_t st, dim3 g
 
 template <bool kMinMax>
 static void launch_gate_mfma(const GateArgs& a, int kc, size_t sh, hipStream_t st, dim3 grid) {
-  if (kc <= 4)
+  // the list as short as the kept blocks allow: each entry a score may pass
+  // costs a 64-bit compare-and-swap in the one-pass form
+  if (kc <= 1)
+    hipLaunchKernelGGL((gate_mfma_kernel<1, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);
+  else if (kc <= 2)
+    hipLaunchKernelGGL((gate_mfma_kernel<2, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);
+  else if (kc <= 4)
     hipLaunchKernelGGL((gate_mfma_kernel<4, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);
   else if (kc <= 8)
     hipLaunchKernelGGL((gate_mfma_kernel<8, kMinMax>), grid, dim3(512), sh, st, a, a.mu3);

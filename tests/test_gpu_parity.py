@@ -234,7 +234,7 @@ def test_forward_minmax_small(w):
     run(w, gate="minmax")
 
 
-TIE_CASES = [(dtype, topk, gate) for dtype in ("bf16", "f32") for topk in (3, 9, 13, 20, 50)
+TIE_CASES = [(dtype, topk, gate) for dtype in ("bf16", "f32") for topk in (2, 3, 5, 9, 13, 20, 50)
              for gate in ("mean", "minmax")]
 
 
@@ -246,8 +246,9 @@ def test_forward_exact_ties_go_to_lower_index(dtype, topk, gate):
     sides, and the report's tie rule (section 2.3: the lower block index
     wins) fixes the selection.  Every row whose oracle gap is exactly 0 must
     match the oracle's selection; only rows with a non-zero gap below the
-    near-tie threshold may differ.  Covers each gate list capacity (one pass,
-    two passes, rounds) on 128 blocks (four 32-block score tiles)."""
+    near-tie threshold may differ.  Covers each gate list capacity on 128
+    blocks (four 32-block score tiles): one pass with lists of 1, 2 and 4
+    entries (top-2, top-3, top-5), two passes (8, 12, 32 entries), rounds."""
     D = 128 if dtype == "bf16" else 64
     w = small(f"ties_{dtype}_k{topk}", dtype, 1, 4096, 2, 1, D, 32, topk, seed=43)
     say(f"[case] exact ties {w} gate={gate}")
