@@ -577,6 +577,14 @@ __device__ __forceinline__ void pv_img(const char* vb, const uint32_t (*pk)[8], 
       for (int b = 0; b < 4; ++b)
         R.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[8 * kb + 4 * hs + b], pb, R.o[b], 0, 0, 0);
     }
+  // operand reads four MFMAs ahead, as in qk_img
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int x = 0; x < 12; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 // S^T = K Q^T for one slice from a K image; kb = this lane's base
@@ -595,6 +603,15 @@ __device__ __forceinline__ void qk_img(const char* kb, const bf16x8* qb, f32x16*
     s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qb[st], s[0], 0, 0, 0);
     s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[st], qb[st], s[1], 0, 0, 0);
   }
+  // operand reads two steps ahead of the MFMAs: four reads, then one MFMA
+  // per read, then the last four MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int x = 0; x < 12; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 // Registers that carry one slice of the K and V^T images from HBM to LDS:
@@ -805,6 +822,14 @@ __device__ __forceinline__ void qk_rows(const char* kbuf, const bf16x8* qb, f32x
   for (int st = 0; st < 8; ++st)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][st], qb[st], s[kb], 0, 0, 0);
+  // operand reads two MFMAs ahead
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int x = 0; x < 8 * NKB - 2; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 }
 
 // O^T += V^T P^T for one slice of V rows.  The transposing load gives lane l
@@ -835,6 +860,14 @@ __device__ __forceinline__ void pv_rows(const char* vbuf, const uint32_t (*pk)[8
       for (int b = 0; b < 4; ++b)
         R.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[8 * kb + 4 * hs + b], pb, R.o[b], 0, 0, 0);
     }
+  // operand reads (two transposing loads per operand) two MFMAs ahead
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int x = 0; x < 8 * NKB - 2; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 }
 
 // Past-block tiles of NW * 32 rows over a block that is a whole number of
