@@ -458,6 +458,10 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
   auto phase1 = [&](int buf, int pb, f32x16& x) {
     uint32_t* myex = pex[pb][kg] + lane * 8;
     const char* rowsrc = rs[buf] + (pw ? 0 : RTILE);  // Q rows or dO rows
+    // the row-operand reads four MFMAs ahead of their MFMAs (left alone the
+    // compiler read each operand just before its MFMA); the fence keeps
+    // phase 2's reads out of this pattern
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = 0.f;
     const int ar = lane & 31;
@@ -466,6 +470,13 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
       const bf16x8 ra = *reinterpret_cast<const bf16x8*>(rowsrc + row_off(ar, lg + 2 * st));
       x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra, kv[st], x, 0, 0, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     if (pw) {
       uint32_t pk[8];
 #pragma unroll
