@@ -522,6 +522,8 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     const char* tsrc = rs[buf] + (pw ? RTILE : 0);  // dO rows (for dV) or Q rows (for dK)
+    // the transposed row operands two MFMAs ahead (fenced from the reads above)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const bf16x8 A = __builtin_bit_cast(bf16x8, u32x4{av[4 * st], av[4 * st + 1], av[4 * st + 2], av[4 * st + 3]});
@@ -538,6 +540,13 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BwdArgs a) {
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[dt], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int x = 0; x < 6; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
 
   Desc D;
